@@ -1,0 +1,376 @@
+"""Pins for the fp64 CPU oracle: worked examples and closed forms from the pages,
+textbook special cases, invariants, an independent library (torch CPU float64),
+and pure-Python brute force.  None of these re-types the oracle's own formula:
+each checks it against something that fixes the answer independently.
+"""
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from softmax_cross_entropy_fwd_amd import inputs
+
+RNG = np.random.default_rng(20261202)
+
+
+def f32(a):
+    return np.asarray(a, dtype=np.float32)
+
+
+# ------------------------------------------------------------------ golden
+
+def test_worked_example_matches_page(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "worked_example.json")))
+    x = f32([g["logits"]])
+    t = np.array([g["target"]])
+    loss, lse = oracle.loss_rows(x, t, with_lse=True)
+    # the page prints its values cut (not rounded) to three decimals
+    step = 10.0 ** -g["printed_decimals"]
+    assert 0 <= float(loss[0]) - g["printed"]["loss"] < step
+    assert 0 <= float(lse[0]) - g["printed"]["lse"] < step
+    # the shifted sum the page traces: sum_j exp(x_j - max) = exp(lse - max)
+    assert 0 <= math.exp(float(lse[0]) - 3.0) - g["printed"]["sum_exp_shifted"] < step
+    # 50-digit evaluation of the direct formula the page checks against
+    getcontext().prec = 50
+    e = [Decimal(v).exp() for v in g["logits"]]
+    exact = (e[0] + e[1] + e[2]).ln() - Decimal(g["logits"][g["target"]])
+    assert abs(float(loss[0]) - float(exact)) <= 2e-16 * float(exact)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_uniform_rows_give_log_v(golden_dir, dtype):
+    g = json.load(open(os.path.join(golden_dir, "uniform_rows.json")))
+    for case in g["cases"]:
+        V = case["V"]
+        assert case["loss"] == pytest.approx(math.log(V), rel=1e-15)
+        for L in [0.0, -3.5, 11.0] + ([-60000.0] if dtype == "f16" else [-1e30]):
+            row = np.full((2, V), L, dtype=np.float32)
+            x = row if dtype == "f32" else _to_bits(row, dtype)
+            t = np.array([0, V - 1])
+            loss = oracle.loss_rows(x, t, dtype=dtype)
+            np.testing.assert_allclose(loss, case["loss"], rtol=2e-15)
+
+
+# ------------------------------------------------------- textbook special cases
+
+def test_single_class_loss_and_grad_are_zero():
+    x = f32(RNG.normal(size=(5, 1)) * 10)
+    t = np.zeros(5, dtype=np.int64)
+    assert np.all(oracle.loss_rows(x, t) == 0.0)
+    _, g64 = oracle.grad_rows(x, t, c=0.2, want64=True)
+    assert np.all(g64 == 0.0)
+
+
+def test_two_classes_is_softplus():
+    x = f32(RNG.normal(size=(64, 2)) * 6)
+    t = RNG.integers(0, 2, size=64)
+    loss = oracle.loss_rows(x, t)
+    for i in range(64):
+        other = float(x[i, 1 - t[i]]) - float(x[i, t[i]])
+        # softplus(d) = log(1 + e^d), written stably for both signs
+        sp = max(other, 0.0) + math.log1p(math.exp(-abs(other)))
+        assert loss[i] == pytest.approx(sp, rel=1e-14, abs=1e-300)
+    # the value quoted for [0, 1], t = 0
+    assert oracle.loss_rows(f32([[0.0, 1.0]]), np.array([0]))[0] == pytest.approx(
+        1.3132616875182228, rel=1e-15)
+
+
+# ------------------------------------------------------------------ invariants
+
+def _grid_values(shape, scale=8.0):
+    """fp32 values on a 2^-10 grid with |x| < scale, so adding 1024 is exact."""
+    return f32(np.round(RNG.uniform(-scale, scale, size=shape) * 1024) / 1024)
+
+
+def test_shift_invariance():
+    x = _grid_values((16, 300))
+    t = RNG.integers(0, 300, size=16)
+    a = oracle.loss_rows(x, t)
+    b = oracle.loss_rows(x + f32(1024.0), t)
+    assert np.all(x + f32(1024.0) - f32(1024.0) == x)      # the shift is exact
+    np.testing.assert_allclose(a, b, rtol=1e-13)
+
+
+def test_column_permutation_with_target():
+    x = f32(RNG.normal(size=(8, 257)) * 3)
+    t = RNG.integers(0, 257, size=8)
+    a = oracle.loss_rows(x, t)
+    for _ in range(3):
+        p = RNG.permutation(257)
+        inv = np.argsort(p)
+        b = oracle.loss_rows(np.ascontiguousarray(x[:, p]), inv[t])
+        np.testing.assert_allclose(a, b, rtol=1e-14)
+
+
+def test_removing_minus_inf_column_changes_nothing():
+    x = f32(RNG.normal(size=(6, 50)))
+    t = RNG.integers(1, 50, size=6)
+    y = np.concatenate([np.full((6, 1), -np.inf, dtype=np.float32), x], axis=1)
+    a = oracle.loss_rows(x, t - 1)
+    b = oracle.loss_rows(y, t)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_dominant_target_bound():
+    V = 50257
+    x = f32(RNG.normal(size=(4, V)) * 8)
+    t = RNG.integers(0, V, size=4)
+    for i in range(4):
+        others = np.delete(x[i], t[i])
+        x[i, t[i]] = others.max() + f32(30.0)
+    loss = oracle.loss_rows(x, t)
+    bound = math.log1p((V - 1) * math.exp(-30.0))
+    assert bound == pytest.approx(4.70e-9, rel=2e-3)
+    assert np.all(loss >= 0) and np.all(loss <= bound)
+    assert np.all(loss > 0)
+
+
+def test_grad_rows_sum_to_zero_and_target_negative():
+    x = f32(RNG.normal(size=(10, 333)) * 4)
+    t = RNG.integers(0, 333, size=10)
+    c = 1.0 / 10
+    _, g = oracle.grad_rows(x, t, c=c, want64=True)
+    assert np.all(np.abs(g.sum(axis=1)) <= 1e-15 * c * 10)
+    assert np.all(g[np.arange(10), t] < 0)
+    g2 = g.copy()
+    g2[np.arange(10), t] = 0
+    assert np.all(g2 >= 0)
+
+
+def test_grad_matches_central_differences():
+    # inputs on a 2^-6 grid, perturbation 2^-12: x +/- h stays exact in fp32
+    V = 7
+    x = f32(np.round(RNG.uniform(-3, 3, size=(3, V)) * 64) / 64)
+    t = RNG.integers(0, V, size=3)
+    h = 2.0 ** -12
+    _, g = oracle.grad_rows(x, t, c=1.0, want64=True)
+    for i in range(3):
+        for j in range(V):
+            xp = x[i:i + 1].copy()
+            xm = x[i:i + 1].copy()
+            xp[0, j] += h
+            xm[0, j] -= h
+            fd = (oracle.loss_rows(xp, t[i:i + 1])[0] - oracle.loss_rows(xm, t[i:i + 1])[0]) / (2 * h)
+            assert fd == pytest.approx(g[i, j], abs=2e-7)
+
+
+def test_out_of_range_target_gives_nan_and_no_onehot():
+    x = f32(RNG.normal(size=(3, 20)))
+    t = np.array([-1, 20, 5])
+    loss = oracle.loss_rows(x, t)
+    assert np.isnan(loss[0]) and np.isnan(loss[1]) and np.isfinite(loss[2])
+    _, g = oracle.grad_rows(x, t, c=0.5, want64=True)
+    np.testing.assert_allclose(g[:2].sum(axis=1), 0.5, rtol=1e-14)
+    assert abs(g[2].sum()) < 1e-15
+
+
+def test_all_minus_inf_row_and_minus_inf_target():
+    x = f32([[-np.inf, -np.inf, -np.inf], [0.0, -np.inf, 1.0]])
+    loss = oracle.loss_rows(x, np.array([0, 1]))
+    assert np.isnan(loss[0])
+    assert loss[1] == np.inf
+
+
+def test_reductions_agree_with_per_row():
+    x, t = inputs.make("f32", 97, 301, 2.0, seed=7)
+    xb = inputs.host_bits(x)
+    per = oracle.fwd(xb, t.numpy(), reduction="none")
+    assert oracle.fwd(xb, t.numpy(), reduction="mean") == pytest.approx(math.fsum(per) / 97, rel=1e-15)
+    assert oracle.fwd(xb, t.numpy(), reduction="sum") == pytest.approx(math.fsum(per), rel=1e-15)
+
+
+def test_empty_batch_reductions():
+    x = np.zeros((0, 5), dtype=np.float32)
+    t = np.zeros(0, dtype=np.int64)
+    assert oracle.fwd(x, t, reduction="sum") == 0.0
+    assert math.isnan(oracle.fwd(x, t, reduction="mean"))
+    assert oracle.fwd(x, t, reduction="none").size == 0
+
+
+# ----------------------------------------------- independent library: torch fp64
+
+def _torch_ref(xb, t, dtype, reduction):
+    w = torch.from_numpy(_widen_all(xb, dtype)).requires_grad_(True)
+    loss = F.cross_entropy(w, torch.from_numpy(np.asarray(t)), reduction=reduction)
+    (loss.sum() if reduction == "none" else loss).backward()
+    return loss.detach().numpy(), w.grad.numpy()
+
+
+def _widen_all(xb, dtype):
+    if dtype == "f32":
+        return xb.astype(np.float64)
+    if dtype == "f16":
+        return xb.view(np.float16).astype(np.float64)
+    return torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+@pytest.mark.parametrize("name,rows", [("tiny", None), ("classifier", 24), ("lmhead", 3),
+                                       ("stress", 64), ("skinny", 500)])
+def test_against_torch_float64(name, rows):
+    c = inputs.CONFIGS[name]
+    M = c["M"] if rows is None else rows
+    x, t = inputs.make(c["dtype"], M, c["V"], c["sigma"], c["seed"], c["structure"])
+    xb, tn = inputs.host_bits(x), t.numpy()
+    dt = c["dtype"]
+    for red in ("none", "mean", "sum"):
+        ref, gref = _torch_ref(xb, tn, dt, red)
+        if red == "none":
+            got = oracle.fwd(xb, tn, dtype=dt, reduction="none")
+            np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+            cscale = 1.0
+        else:
+            got = oracle.fwd(xb, tn, dtype=dt, reduction=red)
+            assert got == pytest.approx(float(ref), rel=1e-12)
+            cscale = 1.0 / M if red == "mean" else 1.0
+        _, g64 = oracle.grad_rows(xb, tn, dtype=dt, c=cscale, want64=True)
+        np.testing.assert_allclose(g64, gref, rtol=1e-10, atol=1e-15 * cscale)
+
+
+# ------------------------------------------------------ pure-Python brute force
+
+def _brute_lse(row):
+    """log sum exp in 60-digit decimal arithmetic (-inf entries contribute 0)."""
+    getcontext().prec = 60
+    m = Decimal(max(row))
+    s = sum((Decimal(v) - m).exp() for v in row if v != -math.inf)
+    return m + s.ln()
+
+
+def _brute_loss(row, t):
+    return float(_brute_lse(row) - Decimal(row[t]))
+
+
+@pytest.mark.parametrize("V", [1, 2, 3, 5, 8])
+def test_brute_force_small(V):
+    specials = [0.0, -0.0, 1.0, -1.0, 80.0, -80.0, 1e4, -1e4, -np.inf, 3.0]
+    for trial in range(60):
+        if trial % 3 == 0:
+            row = list(RNG.choice(specials, size=V))
+        else:
+            row = list(RNG.normal(size=V) * RNG.choice([1e-3, 1.0, 30.0]))
+        row = [float(np.float32(v)) for v in row]
+        if all(v == -math.inf for v in row):
+            row[0] = 0.0
+        finite = [j for j in range(V) if row[j] != -math.inf]
+        for t in finite:
+            x = f32([row])
+            got = oracle.loss_rows(x, np.array([t]))[0]
+            want = _brute_loss(row, t)
+            assert got == pytest.approx(want, rel=1e-13, abs=1e-13), (row, t)
+            _, g = oracle.grad_rows(x, np.array([t]), c=1.0, want64=True)
+            lse = _brute_lse(row)
+            p = [(Decimal(v) - lse).exp() if v != -math.inf else Decimal(0) for v in row]
+            for j in range(V):
+                gw = float(p[j] - (1 if j == t else 0))
+                assert g[0, j] == pytest.approx(gw, rel=1e-12, abs=1e-15), (row, t, j)
+
+
+# -------------------------------------------- storage decode / RNE rounding
+
+def _to_bits(a, dtype):
+    a = np.asarray(a, dtype=np.float32)
+    if dtype == "f16":
+        return a.astype(np.float16).view(np.uint16)
+    return torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_widen_f16_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.widen(bits, "f16")
+    want = bits.view(np.float16).astype(np.float64)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    np.testing.assert_array_equal(got[ok], want[ok])
+    np.testing.assert_array_equal(np.signbit(got[ok]), np.signbit(want[ok]))
+
+
+def test_widen_bf16_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.widen(bits, "bf16")
+    want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    np.testing.assert_array_equal(got[ok], want[ok])
+    np.testing.assert_array_equal(np.signbit(got[ok]), np.signbit(want[ok]))
+
+
+def _rounding_probes(table):
+    """Doubles near every kind of boundary: exact values, midpoints (ties),
+    just above/below midpoints, subnormals, overflow thresholds."""
+    fin = np.sort(np.unique(table[np.isfinite(table) & (table >= 0)]))
+    mids = (fin[:-1] + fin[1:]) / 2
+    v = np.concatenate([fin, mids, np.nextafter(mids, np.inf), np.nextafter(mids, -np.inf),
+                        RNG.uniform(0, fin[-1] * 1.01, size=2000),
+                        np.exp(RNG.uniform(-120, 12, size=2000)),
+                        [fin[-1] * 1.0001, fin[-1] + (fin[-1] - fin[-2]) / 2, np.inf]])
+    v = np.concatenate([v, -v, [0.0, -0.0, np.nan]])
+    return v
+
+
+def test_round_f16_matches_numpy_direct_conversion():
+    table = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float64)
+    v = _rounding_probes(table)
+    sel = RNG.choice(v.size, size=min(v.size, 40000), replace=False)
+    v = v[sel]
+    got = oracle.round_to(v, "f16")
+    want = v.astype(np.float16).view(np.uint16)   # numpy rounds double -> half in one step
+    nan = np.isnan(v)
+    np.testing.assert_array_equal(got[~nan], want[~nan])
+    assert np.all(np.isnan(got[nan].view(np.float16)))
+
+
+def test_round_bf16_is_nearest_even():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    table = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    pos = bits[np.isfinite(table) & (table >= 0) & ~np.signbit(table)]
+    vals = table[pos]
+    order = np.argsort(vals)
+    pos, vals = pos[order], vals[order]
+    v = _rounding_probes(table)
+    v = v[RNG.choice(v.size, size=6000, replace=False)]
+    got = oracle.round_to(v, "bf16")
+    for x, g in zip(v, got):
+        if np.isnan(x):
+            assert (g & 0x7f80) == 0x7f80 and (g & 0x7f) != 0
+            continue
+        a = abs(float(x))
+        sign = 0x8000 if np.signbit(x) else 0
+        k = np.searchsorted(vals, a)
+        if k >= len(vals):
+            # beyond the largest finite: RNE overflows iff a >= max + half spacing
+            top, prev = Fraction(float(vals[-1])), Fraction(float(vals[-2]))
+            want = 0x7f80 if Fraction(a) >= top + (top - prev) / 2 else int(pos[-1])
+        else:
+            lo = max(k - 1, 0)
+            cands = [(abs(Fraction(a) - Fraction(float(vals[j]))), int(pos[j]) & 1, int(pos[j]))
+                     for j in (lo, k) if j < len(vals)]
+            cands.sort()
+            best = cands[0]
+            if len(cands) > 1 and cands[0][0] == cands[1][0]:
+                best = min(cands, key=lambda c: c[1])      # tie -> even fraction
+            want = best[2]
+        assert int(g) == (sign | want), (x, hex(g), hex(sign | want))
+
+
+def test_round_f32_matches_numpy():
+    v = np.concatenate([RNG.normal(size=500) * 1e3, np.exp(RNG.uniform(-100, 80, size=500))])
+    got = oracle.round_to(v, "f32")
+    np.testing.assert_array_equal(got, v.astype(np.float32))
+
+
+def test_grad_rounding_fp16_subnormals():
+    # c = 1/8192 pushes most gradients below the fp16 normal range
+    x, t = inputs.make("f16", 4, 50257, 8.0, seed=3)
+    xb, tn = inputs.host_bits(x), t.numpy()
+    g16, g64 = oracle.grad_rows(xb, tn, dtype="f16", c=1.0 / 8192, want64=True)
+    want = g64.astype(np.float16).view(np.uint16)
+    np.testing.assert_array_equal(g16, want)
+    sub = (g16 & 0x7c00) == 0
+    assert sub.mean() > 0.5
