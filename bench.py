@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Throughput of row-wise softmax cross-entropy on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--op fwd|fwd_bwd]
+                    [--reduction mean|none|sum] [--no-extra] [--no-cpu]
+
+A step is one pass of the whole path (one call of the C-ABI entry point) over
+one batch of synthetic logits already resident in HBM.  The headline line is
+the classifier workload (fp32 [32768, 4096], forward, mean): algorithmic HBM
+GB/s = bytes the method must move / kernel time.  The same line carries:
+
+  roofline      the kernel's achieved GB/s (algorithmic bytes per launch over
+                the average launch duration, from HIP events on the launch
+                stream) against MI355X's 8 TB/s, and the HBM traffic counted by
+                rocprofv3 (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy)
+                when a summary taken on the current kernel source is committed
+                under profiles/;
+  cpu_baseline  the fp64 oracle timed on the host cores over the whole workload;
+  also          the LM-head workload (bf16 [16384, 131072]) forward and fused
+                forward + in-place backward, timed the same way.
+
+Inputs rotate over enough buffers (>= 1 GiB in total) that no launch finds its
+rows in the 256 MB last-level cache; the in-place backward restores its logits
+from a pristine copy between steps, outside the timed launch.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+ELEM = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def alg_bytes(M, V, dtype, op, reduction):
+    """Bytes the method must move: logits read (and gradient written), int64
+    targets read, the output written."""
+    s = ELEM[dtype]
+    out = 4 * M if reduction == "none" else 4
+    if op == "fwd":
+        return M * V * s + 8 * M + out
+    return 2 * M * V * s + 8 * M + out
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "softmax_cross_entropy_fwd_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "ce.h"), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, op, reduction):
+    """Counter-based HBM bytes per launch from a committed rocprofv3 summary,
+    or None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s_%s.json" % (workload, op, reduction))
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def time_workload(ce, workload, op, reduction, steps, warmup, log):
+    import torch
+    from softmax_cross_entropy_fwd_amd import inputs
+    c = inputs.CONFIGS[workload]
+    M, V, dtype = c["M"], c["V"], c["dtype"]
+    dev = torch.device("cuda:0")
+    x0, t = inputs.make_config(workload, device=dev)
+    nbytes = x0.numel() * x0.element_size()
+    nbuf = max(1, -(-(1 << 30) // nbytes)) if op == "fwd" else 1
+    xs = [x0] + [x0.clone() for _ in range(nbuf - 1)]
+    pristine = x0.clone() if op == "fwd_bwd" else None
+    fn = ce.ce_fwd if op == "fwd" else ce.ce_fwd_bwd_inplace
+    out = torch.empty((M,) if reduction == "none" else (), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    plan = ce.ce_plan_describe(M, V, {"f32": 0, "f16": 1, "bf16": 2}[dtype], reduction,
+                               op == "fwd_bwd")
+    log("workload %s op %s reduction %s plan %s buffers %d" % (workload, op, reduction, plan, nbuf))
+    for i in range(warmup):
+        if pristine is not None:
+            xs[0].copy_(pristine)
+        fn(xs[i % nbuf], t, reduction, out=out)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(steps):
+        if pristine is not None:
+            xs[0].copy_(pristine)
+        starts[i].record(stream)
+        fn(xs[i % nbuf], t, reduction, out=out)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_ms = sum(ms) / len(ms)
+    ab = alg_bytes(M, V, dtype, op, reduction)
+    res = {
+        "workload": workload, "op": op, "reduction": reduction, "M": M, "V": V,
+        "storage": dtype, "plan": plan,
+        "kernel_ms_avg": avg_ms, "kernel_ms_min": min(ms),
+        "wall_ms_per_step": 1e3 * wall / steps,
+        "alg_bytes_per_launch": ab,
+        "alg_GBps": ab / (avg_ms * 1e-3) / 1e9,
+        "rows_per_s": M / (avg_ms * 1e-3),
+        "loss": float(out.float().mean().item()) if reduction != "none" else None,
+    }
+    res["frac_of_peak"] = res["alg_GBps"] / PEAK_GBS
+    log("  %.4f ms/launch (min %.4f), %.1f GB/s = %.1f%% of 8 TB/s, %.3g rows/s" % (
+        avg_ms, min(ms), res["alg_GBps"], 100 * res["frac_of_peak"], res["rows_per_s"]))
+    del xs, pristine, x0
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(workload, op, reduction, log, budget_s=20.0):
+    """The fp64 oracle over the whole workload, repeated until ~3 s have passed
+    (each pass is bounded by the budget), on every host core OpenMP gives it."""
+    import numpy as np
+    import torch
+    import oracle
+    from softmax_cross_entropy_fwd_amd import inputs
+    c = inputs.CONFIGS[workload]
+    M, V, dtype = c["M"], c["V"], c["dtype"]
+    x, t = inputs.make_config(workload, device="cpu")
+    xb, tn = inputs.host_bits(x), t.numpy()
+    del x
+    reps, t0 = 0, time.perf_counter()
+    rows = M
+    while True:
+        if op == "fwd":
+            oracle.fwd(xb[:rows], tn[:rows], dtype=dtype, reduction=reduction)
+        else:
+            oracle.grad_rows(xb[:rows], tn[:rows], dtype=dtype, c=1.0 / rows)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= 3.0 or el > budget_s:
+            break
+        if reps == 1 and el > budget_s / 4:
+            break
+    ab = alg_bytes(rows, V, dtype, op, reduction)
+    val = ab * reps / el / 1e9
+    log("cpu oracle: %d pass(es) over %d rows in %.2f s = %.3f GB/s on %d threads" % (
+        reps, rows, el, val, oracle.num_threads()))
+    return {"value": val, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "the whole %s workload (%d x %d %s, %s %s), %d pass(es), %.1f s; %.3g rows/s"
+                      % (workload, rows, V, dtype, op, reduction, reps, el, rows * reps / el)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="classifier")
+    ap.add_argument("--op", default=None, choices=[None, "fwd", "fwd_bwd"])
+    ap.add_argument("--reduction", default=None, choices=[None, "mean", "none", "sum"])
+    ap.add_argument("--no-extra", action="store_true", help="skip the LM-head lines")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--quiet", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    def log(msg):
+        if not args.quiet:
+            print(msg, file=sys.stderr, flush=True)
+
+    import torch
+    import softmax_cross_entropy_fwd_amd as ce
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    ce.load_library()
+    from softmax_cross_entropy_fwd_amd import inputs
+    c = inputs.CONFIGS[args.workload]
+    op = args.op or c["ops"][0]
+    red = args.reduction or c["reductions"][0]
+    log("device: %s, torch %s, hip %s" % (torch.cuda.get_device_name(0), torch.__version__,
+                                          torch.version.hip))
+
+    head = time_workload(ce, args.workload, op, red, args.steps, args.warmup, log)
+    also = []
+    if not args.no_extra and args.workload == "classifier":
+        for eop in ("fwd", "fwd_bwd"):
+            also.append(time_workload(ce, "lmhead", eop, "mean", max(20, args.steps // 5),
+                                      max(3, args.warmup // 5), log))
+    traffic = load_traffic(args.workload, op, red)
+    cpu = None if args.no_cpu else cpu_baseline(args.workload, op, red, log)
+
+    line = {
+        "metric": "CE %s HBM GB/s (algorithmic bytes / kernel time), %s %dx%d %s"
+                  % ("fwd" if op == "fwd" else "fused fwd+bwd", args.workload, c["M"], c["V"],
+                     c["dtype"]),
+        "value": round(head["alg_GBps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["kernel_ms_avg"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0, sigma) logits, uniform int64 targets)",
+        "config": {"workload": args.workload, "M": c["M"], "V": c["V"], "storage": c["dtype"],
+                   "op": op, "reduction": red, "plan": head["plan"]},
+        "rows_per_s": round(head["rows_per_s"], 1),
+        "wall_ms_per_step": round(head["wall_ms_per_step"], 5),
+        "roofline": {"bound": "hbm", "achieved": round(head["alg_GBps"], 2), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(head["frac_of_peak"], 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "also": [{k: (round(v, 5) if isinstance(v, float) else v) for k, v in a.items()}
+                 for a in also],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

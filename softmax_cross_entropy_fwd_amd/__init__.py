@@ -1,1 +1,155 @@
-"""Row-wise softmax cross-entropy on MI355X (gfx950)."""
+"""Row-wise softmax cross-entropy on MI355X (gfx950).
+
+A thin ctypes binding over the C ABI in ``include/ce.h`` (``libce.so``, built
+from ``csrc/`` by ``python -m softmax_cross_entropy_fwd_amd.build``).  The
+functions keep the C names; they only marshal torch tensors into pointers and
+sizes and pass torch's current HIP stream.  Every step of the computation runs
+in the library's HIP kernels; if the library is missing, every call raises.
+
+    loss = ce_fwd(logits, targets, reduction="mean")
+    loss = ce_fwd_bwd_inplace(logits, targets, reduction="mean")   # logits <- grad
+"""
+import ctypes
+import os
+import threading
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libce.so")
+
+CE_F32, CE_F16, CE_BF16 = 0, 1, 2
+CE_NONE, CE_MEAN, CE_SUM = 0, 1, 2
+CE_OK = 0
+CE_ERR_NULL, CE_ERR_SHAPE, CE_ERR_DTYPE, CE_ERR_REDUCTION = -1, -2, -3, -4
+CE_ERR_WORKSPACE, CE_ERR_HIP, CE_ERR_ALIGNMENT, CE_ERR_ALIAS = -5, -6, -7, -8
+REDUCTIONS = {"none": CE_NONE, "mean": CE_MEAN, "sum": CE_SUM}
+
+_lib = None
+_lock = threading.Lock()
+_workspaces = {}
+
+
+class CEError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, ce_status_string(status), status))
+
+
+def load_library(path=None):
+    """Load libce.so (after torch, so the library binds to torch's HIP runtime)."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        import torch  # noqa: F401  -- loads the HIP runtime libce.so must share
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError("%s is not built; run `python -m softmax_cross_entropy_fwd_amd.build`" % p)
+        lib = ctypes.CDLL(p)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        lib.ce_workspace_bytes.argtypes = [i64, i64, i32, i32]
+        lib.ce_workspace_bytes.restype = sz
+        lib.ce_fwd.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, sz, vp]
+        lib.ce_fwd.restype = i32
+        lib.ce_fwd_bwd_inplace.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, sz, vp]
+        lib.ce_fwd_bwd_inplace.restype = i32
+        lib.ce_status_string.argtypes = [i32]
+        lib.ce_status_string.restype = ctypes.c_char_p
+        lib.ce_plan_describe.argtypes = [i64, i64, i32, i32, i32, ctypes.c_char_p, sz]
+        lib.ce_plan_describe.restype = i32
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def _dtype_code(t):
+    import torch
+    codes = {torch.float32: CE_F32, torch.float16: CE_F16, torch.bfloat16: CE_BF16}
+    if t.dtype not in codes:
+        raise TypeError("logits must be float32, float16 or bfloat16, got %s" % t.dtype)
+    return codes[t.dtype]
+
+
+def ce_status_string(status):
+    return load_library().ce_status_string(int(status)).decode()
+
+
+def ce_workspace_bytes(M, V, dtype, reduction):
+    """Workspace bytes a call needs (dtype: CE_* code, reduction: name or code)."""
+    red = REDUCTIONS.get(reduction, reduction)
+    return int(load_library().ce_workspace_bytes(int(M), int(V), int(dtype), int(red)))
+
+
+def ce_plan_describe(M, V, dtype, reduction="mean", fwd_bwd=False):
+    """The launch plan the library picks on the current device."""
+    red = REDUCTIONS.get(reduction, reduction)
+    buf = ctypes.create_string_buffer(256)
+    rc = load_library().ce_plan_describe(int(M), int(V), int(dtype), int(red), int(bool(fwd_bwd)),
+                                         buf, 256)
+    if rc:
+        raise CEError(rc, "ce_plan_describe")
+    return buf.value.decode()
+
+
+def workspace_for(device, stream, nbytes):
+    """A zero-filled workspace cached per (device, stream); calls leave it zeroed."""
+    import torch
+    key = (device.index, int(stream.cuda_stream))
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        with torch.cuda.stream(stream):
+            ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _check(logits, targets):
+    import torch
+    if not logits.is_cuda:
+        raise ValueError("logits must be a device tensor")
+    if logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous [M, V] tensor")
+    if targets.dtype != torch.int64 or targets.dim() != 1 or not targets.is_contiguous():
+        raise ValueError("targets must be a contiguous int64 [M] tensor")
+    if targets.device != logits.device or targets.numel() != logits.shape[0]:
+        raise ValueError("targets must be on the logits' device with M entries")
+
+
+def _call(fn_name, logits, targets, reduction, out, workspace):
+    import torch
+    lib = load_library()
+    _check(logits, targets)
+    red = REDUCTIONS[reduction]
+    M, V = logits.shape
+    dev = logits.device
+    if out is None:
+        out = torch.empty((M,) if red == CE_NONE else (), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    nbytes = int(lib.ce_workspace_bytes(M, V, _dtype_code(logits), red))
+    if nbytes and workspace is None:
+        workspace = workspace_for(dev, stream, nbytes)
+    ws_ptr = workspace.data_ptr() if nbytes else None
+    ws_len = workspace.numel() * workspace.element_size() if nbytes else 0
+    with torch.cuda.device(dev):
+        rc = getattr(lib, fn_name)(logits.data_ptr(), targets.data_ptr(), M, V, _dtype_code(logits),
+                                   red, out.data_ptr() if out.numel() else None, ws_ptr, ws_len,
+                                   stream.cuda_stream)
+    if rc:
+        raise CEError(rc, fn_name)
+    return out
+
+
+def ce_fwd(logits, targets, reduction="mean", out=None, workspace=None):
+    """Cross-entropy of each row of logits [M, V] against targets [M].
+
+    Returns a 0-d fp32 tensor (mean, sum) or the [M] fp32 row losses (none).
+    """
+    return _call("ce_fwd", logits, targets, reduction, out, workspace)
+
+
+def ce_fwd_bwd_inplace(logits, targets, reduction="mean", out=None, workspace=None):
+    """Loss as ce_fwd, and logits overwritten with d(loss)/d(logits)."""
+    return _call("ce_fwd_bwd_inplace", logits, targets, reduction, out, workspace)
+
+
+__all__ = ["ce_fwd", "ce_fwd_bwd_inplace", "ce_workspace_bytes", "ce_status_string",
+           "ce_plan_describe", "load_library", "CEError", "LIB_PATH"]

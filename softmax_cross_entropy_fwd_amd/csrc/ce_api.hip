@@ -1,0 +1,365 @@
+// ce_api.hip -- the C ABI: argument checks, launch plan, launch.
+//
+// Every argument check happens before the first HIP call, so a bad call
+// returns its status without touching the device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <unordered_map>
+
+#include "ce.h"
+#include "ce_device.h"
+#include "ce_internal.h"
+
+namespace {
+
+using cek::KernelRef;
+
+constexpr size_t kTicketBytes = 256;
+constexpr size_t kWorkspaceBytes = kTicketBytes + sizeof(double) * cek::kMaxPartials;
+
+size_t elem_size(int dtype) { return dtype == CE_F32 ? 4 : 2; }
+
+struct Plan {
+    int kind = 0, a = 0, b = 0;
+    KernelRef k{nullptr, 0};
+    int64_t grid = 0;
+    int occupancy = 0;
+    int cus = 0;
+};
+
+KernelRef lookup(int dtype, int kind, int a, int b, bool bwd)
+{
+    switch (dtype) {
+    case CE_F32: return cek::get_kernel_f32(kind, a, b, bwd);
+    case CE_F16: return cek::get_kernel_f16(kind, a, b, bwd);
+    default: return cek::get_kernel_bf16(kind, a, b, bwd);
+    }
+}
+
+int pow2ceil(int64_t n)
+{
+    int p = 1;
+    while (p < n)
+        p <<= 1;
+    return p;
+}
+
+// Mapping and tile for a row of nvec 16-byte vectors (worst case over rows).
+void choose_shape(int64_t nvec, int *kind, int *a, int *b)
+{
+    if (nvec <= 4) {
+        *kind = cek::KIND_ROWS;
+        *a = 1;
+        *b = nvec <= 1 ? 1 : nvec <= 2 ? 2 : 4;
+    } else if (nvec <= 256) {
+        *kind = cek::KIND_ROWS;
+        *a = pow2ceil((nvec + 3) / 4);
+        *b = 4;
+    } else if (nvec <= 512) {
+        *kind = cek::KIND_ROWS;
+        *a = 64;
+        *b = 8;
+    } else if (nvec <= 1024) {
+        *kind = cek::KIND_ROWS;
+        *a = 64;
+        *b = 16;
+    } else if (nvec <= 16384) {
+        static const int cand[][2] = {{4, 8}, {8, 8}, {8, 12}, {8, 16}, {16, 12}, {16, 16}};
+        *kind = cek::KIND_WG;
+        for (const auto &c : cand) {
+            if ((int64_t)c[0] * 64 * c[1] >= nvec) {
+                *a = c[0];
+                *b = c[1];
+                break;
+            }
+        }
+    } else {
+        *kind = cek::KIND_STREAM;
+        *a = 8;
+        *b = 8;
+    }
+}
+
+// CE_FORCE_PLAN=rows:G:K | wg:W:K | stream:W:K overrides the mapping (tuning).
+bool forced_shape(int *kind, int *a, int *b)
+{
+    const char *s = std::getenv("CE_FORCE_PLAN");
+    if (!s || !*s)
+        return false;
+    char name[16] = {0};
+    int x = 0, y = 0;
+    if (std::sscanf(s, "%15[a-z]:%d:%d", name, &x, &y) != 3)
+        return false;
+    if (!std::strcmp(name, "rows"))
+        *kind = cek::KIND_ROWS;
+    else if (!std::strcmp(name, "wg"))
+        *kind = cek::KIND_WG;
+    else if (!std::strcmp(name, "stream"))
+        *kind = cek::KIND_STREAM;
+    else
+        return false;
+    *a = x;
+    *b = y;
+    return true;
+}
+
+std::mutex g_mu;
+std::unordered_map<int, int> g_cus;                       // device -> CU count
+std::unordered_map<uint64_t, int> g_occ;                  // (device, fn) -> blocks per CU
+
+int device_cus(int dev, int *cus)
+{
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_cus.find(dev);
+    if (it != g_cus.end()) {
+        *cus = it->second;
+        return CE_OK;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return CE_ERR_HIP;
+    g_cus[dev] = n;
+    *cus = n;
+    return CE_OK;
+}
+
+int blocks_per_cu(int dev, const KernelRef &k, int *occ)
+{
+    uint64_t key = ((uint64_t)(uint32_t)dev << 48) ^ (uint64_t)(uintptr_t)k.fn;
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_occ.find(key);
+    if (it != g_occ.end()) {
+        *occ = it->second;
+        return CE_OK;
+    }
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k.fn, k.block, 0) != hipSuccess)
+        return CE_ERR_HIP;
+    if (n < 1)
+        n = 1;
+    g_occ[key] = n;
+    *occ = n;
+    return CE_OK;
+}
+
+// Worst-case 16-byte vectors a row window spans.
+int64_t window_vectors(int64_t V, int E, bool aligned)
+{
+    return aligned ? V / E : (V + 2 * E - 2) / E;
+}
+
+int make_plan(int64_t M, int64_t V, int dtype, bool bwd, bool aligned, Plan *plan)
+{
+    const int E = 16 / (int)elem_size(dtype);
+    const int64_t nvec = window_vectors(V, E, aligned);
+    int kind = 0, a = 0, b = 0;
+    choose_shape(nvec, &kind, &a, &b);
+    int fk, fa, fb;
+    if (forced_shape(&fk, &fa, &fb)) {
+        KernelRef f = lookup(dtype, fk, fa, fb, bwd);
+        bool fits = fk == cek::KIND_STREAM ||
+                    (fk == cek::KIND_ROWS ? (int64_t)fa * fb >= nvec : (int64_t)fa * 64 * fb >= nvec);
+        if (f.fn && fits) {
+            kind = fk;
+            a = fa;
+            b = fb;
+        }
+    }
+    plan->kind = kind;
+    plan->a = a;
+    plan->b = b;
+    plan->k = lookup(dtype, kind, a, b, bwd);
+    if (!plan->k.fn)
+        return CE_ERR_HIP;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return CE_ERR_HIP;
+    int rc = device_cus(dev, &plan->cus);
+    if (rc)
+        return rc;
+    rc = blocks_per_cu(dev, plan->k, &plan->occupancy);
+    if (rc)
+        return rc;
+    int64_t rows_per_wg = kind == cek::KIND_ROWS ? (plan->k.block / 64) * (64 / a) : 1;
+    int64_t needed = (M + rows_per_wg - 1) / rows_per_wg;
+    int64_t cap = (int64_t)plan->cus * plan->occupancy;
+    const char *g = std::getenv("CE_FORCE_GRID");
+    if (g && *g && std::atoll(g) > 0)
+        cap = std::atoll(g);
+    if (cap > cek::kMaxPartials)
+        cap = cek::kMaxPartials;
+    plan->grid = needed < cap ? needed : cap;
+    if (plan->grid < 1)
+        plan->grid = 1;
+    return CE_OK;
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb)
+{
+    if (!a || !b || !na || !nb)
+        return false;
+    uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int check_args(const void *logits, const int64_t *targets, int64_t M, int64_t V, int dtype,
+               int reduction, const float *out, const void *ws, size_t ws_bytes, bool bwd)
+{
+    if (dtype != CE_F32 && dtype != CE_F16 && dtype != CE_BF16)
+        return CE_ERR_DTYPE;
+    if (reduction != CE_NONE && reduction != CE_MEAN && reduction != CE_SUM)
+        return CE_ERR_REDUCTION;
+    if (M < 0 || V < 1 || V > CE_MAX_V)
+        return CE_ERR_SHAPE;
+    const size_t s = elem_size(dtype);
+    if (M > 0 && (uint64_t)M > (uint64_t)INT64_MAX / (uint64_t)V / s)
+        return CE_ERR_SHAPE;
+    if (M == 0) {
+        if (reduction != CE_NONE && !out)
+            return CE_ERR_NULL;
+        return CE_OK;
+    }
+    if (!logits || !targets || !out)
+        return CE_ERR_NULL;
+    if ((uintptr_t)logits % s)
+        return CE_ERR_ALIGNMENT;
+    if (reduction != CE_NONE) {
+        if (!ws || ws_bytes < kWorkspaceBytes || (uintptr_t)ws % 8)
+            return CE_ERR_WORKSPACE;
+    }
+    if (bwd) {
+        const size_t xb = (size_t)M * (size_t)V * s;
+        const size_t ob = reduction == CE_NONE ? (size_t)M * 4 : 4;
+        if (overlaps(logits, xb, targets, (size_t)M * 8) || overlaps(logits, xb, out, ob) ||
+            (reduction != CE_NONE && overlaps(logits, xb, ws, kWorkspaceBytes)))
+            return CE_ERR_ALIAS;
+    }
+    return CE_OK;
+}
+
+int run(const void *logits, const int64_t *targets, int64_t M, int64_t V, int dtype,
+        int reduction, float *out, void *ws, size_t ws_bytes, void *stream, bool bwd)
+{
+    int rc = check_args(logits, targets, M, V, dtype, reduction, out, ws, ws_bytes, bwd);
+    if (rc)
+        return rc;
+    hipStream_t st = (hipStream_t)stream;
+    if (M == 0) {
+        if (reduction == CE_NONE)
+            return CE_OK;
+        float value = reduction == CE_MEAN ? __builtin_nanf("") : 0.0f;
+        void *args[] = {&out, &value};
+        if (hipLaunchKernel(cek::empty_reduce_fn(), dim3(1), dim3(64), args, 0, st) != hipSuccess)
+            return CE_ERR_HIP;
+        return CE_OK;
+    }
+    const size_t s = elem_size(dtype);
+    const int E = 16 / (int)s;
+    const uintptr_t base = (uintptr_t)logits;
+    const int head0 = (int)((base % 16) / s);
+    const bool aligned = head0 == 0 && V % E == 0;
+    Plan plan;
+    rc = make_plan(M, V, dtype, bwd, aligned, &plan);
+    if (rc)
+        return rc;
+
+    cek::Params p;
+    p.x = (cek::Vec *)(base - (uintptr_t)head0 * s);
+    p.targets = targets;
+    p.out = out;
+    p.ticket = reduction == CE_NONE ? nullptr : (unsigned int *)ws;
+    p.partials = reduction == CE_NONE ? nullptr : (double *)((char *)ws + kTicketBytes);
+    p.M = M;
+    p.V = V;
+    p.head0 = head0;
+    p.aligned = aligned ? 1 : 0;
+    p.reduction = reduction;
+    const double c = reduction == CE_MEAN ? 1.0 / (double)M : 1.0;
+    p.c = (float)c;
+    p.log2c = (float)std::log2(c);
+    p.out_scale = c;
+    void *args[] = {&p};
+    if (hipLaunchKernel(plan.k.fn, dim3((unsigned)plan.grid), dim3(plan.k.block), args, 0, st) !=
+        hipSuccess)
+        return CE_ERR_HIP;
+    return CE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ce_workspace_bytes(int64_t M, int64_t V, ce_dtype_t dtype, ce_reduction_t reduction)
+{
+    if (dtype != CE_F32 && dtype != CE_F16 && dtype != CE_BF16)
+        return 0;
+    if (reduction != CE_MEAN && reduction != CE_SUM)
+        return 0;
+    if (M <= 0 || V < 1 || V > CE_MAX_V)
+        return 0;
+    return kWorkspaceBytes;
+}
+
+int ce_fwd(const void *logits, const int64_t *targets, int64_t M, int64_t V, ce_dtype_t dtype,
+           ce_reduction_t reduction, float *out, void *workspace, size_t workspace_bytes,
+           void *stream)
+{
+    return run(logits, targets, M, V, (int)dtype, (int)reduction, out, workspace,
+               workspace_bytes, stream, false);
+}
+
+int ce_fwd_bwd_inplace(void *logits, const int64_t *targets, int64_t M, int64_t V,
+                       ce_dtype_t dtype, ce_reduction_t reduction, float *loss_out,
+                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    return run(logits, targets, M, V, (int)dtype, (int)reduction, loss_out, workspace,
+               workspace_bytes, stream, true);
+}
+
+const char *ce_status_string(int status)
+{
+    switch (status) {
+    case CE_OK: return "ok";
+    case CE_ERR_NULL: return "a required pointer is NULL";
+    case CE_ERR_SHAPE: return "bad shape (M < 0, V < 1, V too large, or size overflow)";
+    case CE_ERR_DTYPE: return "unknown dtype";
+    case CE_ERR_REDUCTION: return "unknown reduction";
+    case CE_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case CE_ERR_HIP: return "HIP runtime error or launch failure";
+    case CE_ERR_ALIGNMENT: return "logits not aligned to its element size";
+    case CE_ERR_ALIAS: return "in-place logits overlap targets, output or workspace";
+    default: return "unknown status";
+    }
+}
+
+int ce_plan_describe(int64_t M, int64_t V, ce_dtype_t dtype, ce_reduction_t reduction,
+                     int fwd_bwd, char *buf, size_t buf_len)
+{
+    if (!buf || !buf_len)
+        return CE_ERR_NULL;
+    if (dtype != CE_F32 && dtype != CE_F16 && dtype != CE_BF16)
+        return CE_ERR_DTYPE;
+    if (reduction != CE_NONE && reduction != CE_MEAN && reduction != CE_SUM)
+        return CE_ERR_REDUCTION;
+    if (M < 1 || V < 1 || V > CE_MAX_V)
+        return CE_ERR_SHAPE;
+    const int E = 16 / (int)elem_size(dtype);
+    const bool aligned = V % E == 0;   // for a 16-byte aligned base
+    Plan plan;
+    int rc = make_plan(M, V, (int)dtype, fwd_bwd != 0, aligned, &plan);
+    if (rc)
+        return rc;
+    static const char *names[] = {"rows", "wg", "stream"};
+    std::snprintf(buf, buf_len, "%s:%d:%d block=%d grid=%lld occupancy=%d cus=%d",
+                  names[plan.kind], plan.a, plan.b, plan.k.block, (long long)plan.grid,
+                  plan.occupancy, plan.cus);
+    return CE_OK;
+}
+
+}  // extern "C"

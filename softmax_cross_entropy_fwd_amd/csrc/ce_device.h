@@ -1,0 +1,849 @@
+// ce_device.h -- device code for row-wise softmax cross-entropy on gfx950.
+//
+// Internal to the library.  Three row mappings share the per-row arithmetic:
+//
+//   rows_kernel<G, K>   G lanes per row (64/G rows per wavefront), the whole
+//                       row held in registers (K 16-byte vectors per lane).
+//   wg_kernel<W, K>     one row per workgroup of W wavefronts, the whole row
+//                       held in registers across the workgroup; cross-wave
+//                       combine through LDS.
+//   stream_kernel<W, K> one row per workgroup, streamed in chunks of
+//                       W*64*K vectors with an online (max, sum) rescale; the
+//                       backward re-reads the row.  Any row length.
+//
+// Per row (the cross-entropy of the POPCORNBENCH "Kimi-K2.6 l1_p95" trace and
+// of loss_kernel in the Triton issue "Cross Entropy Loss performance issue"):
+//   m   = max_j x_j
+//   s   = sum_j 2^(x_j*log2e - m*log2e)          (fp32, exp2 on the VALU)
+//   loss = (m - x_t) + ln 2 * log2(s)
+// and, for the fused backward ("9 Triton kernels in 9 weeks", week 7),
+//   g_j = 2^(x_j*log2e - m*log2e - log2(s)) * c,  g_t = (p_t - 1) * c,
+// written over the row.  The two-phase form (row max first, then the sum
+// against that max) replaces the pages' per-element online update wherever the
+// row sits in registers; the chunked stream applies the pages' blockwise
+// rescale once per chunk, in base 2 so it cannot overflow.
+//
+// When the target holds more than half of the probability mass (p_t > 1/2),
+// 1 - p_t and the loss are recomputed from the sum of the other terms, so the
+// target's gradient and a small loss keep their relative accuracy.
+//
+// Rows are read in aligned 16-byte vectors.  A row that does not start or end
+// on a 16-byte boundary is covered by the aligned window around it; elements
+// of the window outside the row are treated as -inf and never written.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cek {
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+enum : int { RED_NONE = 0, RED_MEAN = 1, RED_SUM = 2 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr int kMaxPartials = 4096;
+
+struct alignas(16) Vec {
+    uint32_t w[4];
+};
+
+struct Params {
+    Vec *x;                  // 16-byte aligned address at or before logits[0]
+    const int64_t *targets;  // [M]
+    float *out;              // [M] (none) or [1]
+    double *partials;        // [gridDim.x] per-workgroup loss sums
+    unsigned int *ticket;    // zero between calls
+    int64_t M;
+    int64_t V;
+    int head0;               // elements between x and logits[0]
+    int aligned;             // every row starts and ends on a 16-byte boundary
+    int reduction;
+    float c;                 // gradient scale
+    float log2c;             // log2(c)
+    double out_scale;        // 1/M (mean) or 1 (sum)
+};
+
+// ------------------------------------------------------------ storage types
+
+template <int DT> struct Traits;
+template <> struct Traits<DT_F32> {
+    static constexpr int E = 4;                  // elements per 16-byte vector
+    static constexpr uint32_t kNegInfWord = 0xff800000u;
+};
+template <> struct Traits<DT_F16> {
+    static constexpr int E = 8;
+    static constexpr uint32_t kNegInfWord = 0xfc00fc00u;
+};
+template <> struct Traits<DT_BF16> {
+    static constexpr int E = 8;
+    static constexpr uint32_t kNegInfWord = 0xff80ff80u;
+};
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+
+// Element j (compile-time after unrolling) of a vector, widened to fp32.
+template <int DT>
+__device__ __forceinline__ float elem(const Vec &v, int j)
+{
+    if constexpr (DT == DT_F32) {
+        return __uint_as_float(v.w[j]);
+    } else if constexpr (DT == DT_BF16) {
+        uint32_t w = v.w[j >> 1];
+        return __uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
+    } else {
+        half2_t h = __builtin_bit_cast(half2_t, v.w[j >> 1]);
+        return (float)((j & 1) ? h.y : h.x);
+    }
+}
+
+// Replace the elements of v outside [lo, hi) with -inf.
+template <int DT>
+__device__ __forceinline__ void mask_outside(Vec &v, int lo, int hi)
+{
+    constexpr int E = Traits<DT>::E;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        if (j < lo || j >= hi) {
+            if constexpr (DT == DT_F32) {
+                v.w[j] = 0xff800000u;
+            } else if constexpr (DT == DT_F16) {
+                v.w[j >> 1] = (j & 1) ? ((v.w[j >> 1] & 0x0000ffffu) | 0xfc000000u)
+                                      : ((v.w[j >> 1] & 0xffff0000u) | 0x0000fc00u);
+            } else {
+                v.w[j >> 1] = (j & 1) ? ((v.w[j >> 1] & 0x0000ffffu) | 0xff800000u)
+                                      : ((v.w[j >> 1] & 0xffff0000u) | 0x0000ff80u);
+            }
+        }
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ Vec neg_inf_vec()
+{
+    Vec v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        v.w[i] = Traits<DT>::kNegInfWord;
+    return v;
+}
+
+// Two fp32 gradients -> one 32-bit word of the storage type (RNE).
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b)
+{
+    if constexpr (DT == DT_BF16) {
+        bf162_t r;
+        r.x = (__bf16)a;
+        r.y = (__bf16)b;
+        return __builtin_bit_cast(uint32_t, r);
+    } else {
+        half2_t r;
+        r.x = (_Float16)a;
+        r.y = (_Float16)b;
+        return __builtin_bit_cast(uint32_t, r);
+    }
+}
+
+// Store elements [lo, hi) of v at p (a vector-aligned address) one by one.
+template <int DT>
+__device__ __forceinline__ void store_partial(Vec *p, const Vec &v, int lo, int hi)
+{
+    constexpr int E = Traits<DT>::E;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        if (j >= lo && j < hi) {
+            if constexpr (DT == DT_F32) {
+                reinterpret_cast<uint32_t *>(p)[j] = v.w[j];
+            } else {
+                uint32_t w = v.w[j >> 1];
+                reinterpret_cast<uint16_t *>(p)[j] = (uint16_t)((j & 1) ? (w >> 16) : w);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ------------------------------------------------------- lane reductions
+// DPP within 16-lane rows, a lane swap for 32, and readlane for 64.  Every
+// lane of a G-lane group ends with the same (bitwise) result.
+
+struct OpMax {
+    __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+    static constexpr float identity() { return -__builtin_inff(); }
+};
+struct OpSum {
+    __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+    static constexpr float identity() { return 0.0f; }
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+template <int G, class Op>
+__device__ __forceinline__ float group_reduce(float v, Op op)
+{
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16 || G == 32 || G == 64, "G");
+    if constexpr (G >= 2) v = op(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) v = op(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) v = op(v, dpp<0x141>(v));  // row_half_mirror
+    if constexpr (G >= 16) v = op(v, dpp<0x140>(v)); // row_mirror
+    if constexpr (G == 32) v = op(v, __shfl_xor(v, 16, 64));
+    if constexpr (G == 64) {
+        float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
+        float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+        float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
+        float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+        v = op(op(a, b), op(c, d));
+    }
+    return v;
+}
+
+// Value of lane `src` of this lane's G-lane group.
+template <int G>
+__device__ __forceinline__ float group_bcast(float v, int src_in_group)
+{
+    if constexpr (G == 1) {
+        return v;
+    } else if constexpr (G == 64) {
+        return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src_in_group));
+    } else {
+        int lane = threadIdx.x & 63;
+        return __shfl(v, (lane & ~(G - 1)) + src_in_group, 64);
+    }
+}
+
+// ------------------------------------------------------ per-row helpers
+
+// Where the target sits in the row's window of vectors (32-bit: a window
+// holds fewer than 2^31 elements).
+struct TargetPos {
+    bool valid;
+    int vt;   // window vector index, -1 when the target is out of range
+    int jt;   // element within the vector
+};
+
+template <int DT>
+__device__ __forceinline__ TargetPos target_pos(int64_t t, int64_t V, int head)
+{
+    constexpr int E = Traits<DT>::E;
+    TargetPos tp;
+    tp.valid = (uint64_t)t < (uint64_t)V;
+    const uint32_t wt = tp.valid ? (uint32_t)t + (uint32_t)head : 0u;
+    tp.vt = tp.valid ? (int)(wt / E) : -1;
+    tp.jt = (int)(wt % E);
+    return tp;
+}
+
+// Keeps the compiler from carrying values derived from the row (widened
+// elements, exponentials) from one pass to the next: each pass recomputes
+// them from the packed registers, which bounds register use to the packed row.
+template <int K>
+__device__ __forceinline__ void opt_barrier(Vec (&raw)[K])
+{
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        asm volatile("" : "+v"(raw[k].w[0]), "+v"(raw[k].w[1]), "+v"(raw[k].w[2]), "+v"(raw[k].w[3]));
+}
+
+// Loads window vectors lidx + STRIDE*k (k < K) of a row whose window has nvec
+// vectors and starts at xrow.  Every load is issued, in one block, before any
+// is used: a lane whose vector lies past the window re-reads the window's last
+// vector (a cache hit), and the caller drops that copy from the sum with
+// vec_valid().  kfull (uniform) is the number of leading k for which every
+// lane's vector lies inside every row's window.  Elements of the window
+// outside the row become -inf; only the first and the last window vector (and
+// copies of the last) can hold such elements.
+template <int DT, int K, int STRIDE>
+__device__ __forceinline__ void load_window(Vec (&raw)[K], const Vec *xrow, int lidx, int nvec,
+                                            int kfull, int head, int64_t V, bool aligned)
+{
+    constexpr int E = Traits<DT>::E;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int v = lidx + STRIDE * k;
+        raw[k] = xrow[v < nvec ? v : nvec - 1];
+    }
+    if (!aligned) {
+        if (lidx == 0 && head > 0)
+            mask_outside<DT>(raw[0], head, E);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            if (k + 1 >= kfull) {
+                const int v = lidx + STRIDE * k;
+                if (v >= nvec - 1)
+                    mask_outside<DT>(raw[k], 0, (int)(head + V - (int64_t)(nvec - 1) * E));
+            }
+        }
+    }
+}
+
+// Whether the lane's k-th vector is a window vector of its own (not a copy).
+template <int STRIDE>
+__device__ __forceinline__ bool vec_valid(int k, int kfull, int lidx, int nvec)
+{
+    return k < kfull || lidx + STRIDE * k < nvec;
+}
+
+// Gradient coefficients for one row: g = 2^(x*log2e - bias) * post.
+// fp16: the scale c is folded into the exponent.  bf16, whose range reaches
+// below fp32's normal range: the exponent is lifted by 64 and the product
+// scaled back by 2^-64, so gradients that round to bf16 subnormals are formed
+// from normal fp32 values.  fp32: g = 2^((x - m)*log2e - log2 s) * c, which
+// keeps the exponent small and the relative error near 1e-6.
+template <int DT>
+struct GradCoef {
+    float m;
+    float bias;
+    float post;
+};
+
+template <int DT>
+__device__ __forceinline__ GradCoef<DT> grad_coef(float m, float mL, float log2s, float c, float log2c)
+{
+    GradCoef<DT> g;
+    g.m = m;
+    if constexpr (DT == DT_F32) {
+        g.bias = log2s;
+        g.post = c;
+    } else if constexpr (DT == DT_F16) {
+        g.bias = mL + log2s - log2c;
+        g.post = 1.0f;
+    } else {
+        g.bias = mL + log2s - log2c - 64.0f;
+        g.post = 5.42101086242752217e-20f;   // 2^-64
+    }
+    return g;
+}
+
+template <int DT>
+__device__ __forceinline__ float grad_elem(float x, const GradCoef<DT> &gc)
+{
+    if constexpr (DT == DT_F32)
+        return fast_exp2(__builtin_fmaf(x - gc.m, kLog2e, -gc.bias)) * gc.post;
+    else if constexpr (DT == DT_F16)
+        return fast_exp2(__builtin_fmaf(x, kLog2e, -gc.bias));
+    else
+        return fast_exp2(__builtin_fmaf(x, kLog2e, -gc.bias)) * gc.post;
+}
+
+// Gradients of one vector, with the target's element replaced by gt when
+// is_target; returns the packed vector.
+template <int DT>
+__device__ __forceinline__ Vec grad_vec(const Vec &in, const GradCoef<DT> &gc, bool is_target,
+                                        int jt, float gt)
+{
+    constexpr int E = Traits<DT>::E;
+    float g[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+        g[j] = grad_elem<DT>(elem<DT>(in, j), gc);
+    if (is_target) {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            if (j == jt)
+                g[j] = gt;
+    }
+    Vec out;
+    if constexpr (DT == DT_F32) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            out.w[j] = __float_as_uint(g[j]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            out.w[j] = pack2<DT>(g[2 * j], g[2 * j + 1]);
+    }
+    return out;
+}
+
+template <int DT>
+__device__ __forceinline__ float vec_max(const Vec &v, float m)
+{
+    constexpr int E = Traits<DT>::E;
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+        m = fmaxf(m, elem<DT>(v, j));
+    return m;
+}
+
+// Sum of 2^(x*log2e - mL) over the vector (two chains for latency).
+template <int DT>
+__device__ __forceinline__ float vec_sumexp(const Vec &v, float mL)
+{
+    constexpr int E = Traits<DT>::E;
+    float a = fast_exp2(__builtin_fmaf(elem<DT>(v, 0), kLog2e, -mL));
+    float b = fast_exp2(__builtin_fmaf(elem<DT>(v, 1), kLog2e, -mL));
+#pragma unroll
+    for (int j = 2; j < E; j += 2) {
+        a += fast_exp2(__builtin_fmaf(elem<DT>(v, j), kLog2e, -mL));
+        b += fast_exp2(__builtin_fmaf(elem<DT>(v, j + 1), kLog2e, -mL));
+    }
+    return a + b;
+}
+
+// The same sum leaving out element jt.
+template <int DT>
+__device__ __forceinline__ float vec_sumexp_skip(const Vec &v, float mL, int jt)
+{
+    constexpr int E = Traits<DT>::E;
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        float e = fast_exp2(__builtin_fmaf(elem<DT>(v, j), kLog2e, -mL));
+        a += (j == jt) ? 0.0f : e;
+    }
+    return a;
+}
+
+template <int DT>
+__device__ __forceinline__ float vec_elem_dyn(const Vec &v, int jt)
+{
+    constexpr int E = Traits<DT>::E;
+    float r = 0.0f;
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+        if (j == jt)
+            r = elem<DT>(v, j);
+    return r;
+}
+
+// Loss and target gradient of a row from its reduced statistics.
+struct RowResult {
+    float loss;
+    float gt;       // gradient of the target element (already times c)
+};
+
+__device__ __forceinline__ RowResult row_result(bool tvalid, float m, float xt, float et, float s,
+                                                float s_excl, bool accurate, float c)
+{
+    RowResult r;
+    if (!tvalid) {
+        r.loss = __builtin_nanf("");
+        r.gt = 0.0f;
+        return r;
+    }
+    if (accurate) {
+        r.loss = log1pf(s_excl / et);
+        r.gt = -(s_excl / s) * c;
+    } else {
+        r.loss = (m - xt) + kLn2 * __log2f(s);
+        r.gt = (et / s - 1.0f) * c;
+    }
+    return r;
+}
+
+// Writes the gradient of window vector v (lane's k-th vector) over the row,
+// leaving elements outside the row untouched.
+template <int DT>
+__device__ __forceinline__ void store_grad(Vec *xrow, int v, const Vec &g, int head, int64_t V,
+                                           bool aligned)
+{
+    constexpr int E = Traits<DT>::E;
+    if (aligned) {
+        xrow[v] = g;
+        return;
+    }
+    const int64_t lo = head - (int64_t)v * E;
+    const int64_t hi = lo + V;
+    if (lo <= 0 && hi >= E)
+        xrow[v] = g;
+    else
+        store_partial<DT>(xrow + v, g, (int)(lo > 0 ? lo : 0), (int)(hi < E ? hi : E));
+}
+
+// ------------------------------------------- reductions across a row's lanes
+
+// G lanes of one wavefront per row.
+template <int G>
+struct GroupRed {
+    float xt_local = 0.0f;
+    int owner = 0;
+    __device__ __forceinline__ void publish_xt(float v, bool is_owner, int owner_idx)
+    {
+        if (is_owner)
+            xt_local = v;
+        owner = owner_idx;
+    }
+    __device__ __forceinline__ float max(float v) { return group_reduce<G>(v, OpMax()); }
+    __device__ __forceinline__ float xt() { return group_bcast<G>(xt_local, owner); }
+    __device__ __forceinline__ float sum(float v) { return group_reduce<G>(v, OpSum()); }
+    __device__ __forceinline__ float sum_excl(float v) { return group_reduce<G>(v, OpSum()); }
+};
+
+// W wavefronts of one workgroup per row: DPP within each wavefront, LDS across
+// them, partials added in wavefront order.  Every call is made by the whole
+// workgroup.  Each LDS slot is read before the next barrier and rewritten only
+// after it, so the slots are safely reused row after row.
+template <int W>
+struct WgRed {
+    float *smax, *ssum, *sexc, *sxt;
+    int wave, lane;
+    __device__ __forceinline__ void publish_xt(float v, bool is_owner, int)
+    {
+        if (is_owner)
+            *sxt = v;
+    }
+    __device__ __forceinline__ float combine(float v, float *slot, bool is_max)
+    {
+        v = is_max ? group_reduce<64>(v, OpMax()) : group_reduce<64>(v, OpSum());
+        if (lane == 0)
+            slot[wave] = v;
+        __syncthreads();
+        float r = slot[0];
+#pragma unroll
+        for (int w = 1; w < W; ++w)
+            r = is_max ? fmaxf(r, slot[w]) : r + slot[w];
+        return r;
+    }
+    __device__ __forceinline__ float max(float v) { return combine(v, smax, true); }
+    __device__ __forceinline__ float xt() { return *sxt; }
+    __device__ __forceinline__ float sum(float v) { return combine(v, ssum, false); }
+    __device__ __forceinline__ float sum_excl(float v) { return combine(v, sexc, false); }
+};
+
+// One row held in registers: K vectors per lane, lane lidx of STRIDE lanes.
+// Returns the row's loss (identical in every lane of the row).  Lanes with
+// write == false take part in the reductions but store nothing.
+template <int DT, int K, int STRIDE, bool BWD, class Red>
+__device__ __forceinline__ float row_in_registers(const Params &p, Red &red, Vec *xrow, int lidx,
+                                                  int nvec, int kfull, int head, int64_t t,
+                                                  bool write)
+{
+    Vec raw[K];
+    load_window<DT, K, STRIDE>(raw, xrow, lidx, nvec, kfull, head, p.V, p.aligned);
+    const TargetPos tp = target_pos<DT>(t, p.V, head);
+    const int kt = tp.valid ? tp.vt / STRIDE : -1;
+    const int owner = tp.valid ? tp.vt % STRIDE : 0;
+    const bool is_owner = tp.valid && lidx == owner;
+
+    float xt_l = 0.0f;
+    float lm = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        lm = vec_max<DT>(raw[k], lm);
+        if (k == kt && is_owner)
+            xt_l = vec_elem_dyn<DT>(raw[k], tp.jt);
+    }
+    red.publish_xt(xt_l, is_owner, owner);
+    const float m = red.max(lm);
+    const float xt = tp.valid ? red.xt() : __builtin_nanf("");
+    const float mL = m * kLog2e;
+
+    opt_barrier<K>(raw);
+    float ls = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const float e = vec_sumexp<DT>(raw[k], mL);
+        ls += vec_valid<STRIDE>(k, kfull, lidx, nvec) ? e : 0.0f;
+    }
+    const float s = red.sum(ls);
+
+    const float et = fast_exp2(__builtin_fmaf(xt, kLog2e, -mL));
+    const bool accurate = tp.valid && et > 0.5f * s;
+    float s_excl = s - et;
+    if (accurate) {
+        opt_barrier<K>(raw);
+        float lx = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const float e = (k == kt && is_owner) ? vec_sumexp_skip<DT>(raw[k], mL, tp.jt)
+                                                  : vec_sumexp<DT>(raw[k], mL);
+            lx += vec_valid<STRIDE>(k, kfull, lidx, nvec) ? e : 0.0f;
+        }
+        s_excl = red.sum_excl(lx);
+    }
+    const RowResult rr = row_result(tp.valid, m, xt, et, s, s_excl, accurate, p.c);
+
+    if constexpr (BWD) {
+        opt_barrier<K>(raw);
+        const GradCoef<DT> gc = grad_coef<DT>(m, mL, __log2f(s), p.c, p.log2c);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int v = lidx + STRIDE * k;
+            if (write && vec_valid<STRIDE>(k, kfull, lidx, nvec)) {
+                const Vec g = grad_vec<DT>(raw[k], gc, k == kt && is_owner, tp.jt, rr.gt);
+                store_grad<DT>(xrow, v, g, head, p.V, p.aligned);
+            }
+        }
+    }
+    return rr.loss;
+}
+
+// --------------------------------------------- end of kernel: mean / sum
+// Each workgroup publishes its fp64 loss sum; the last one to finish (integer
+// ticket) adds all of them in index order and writes the result, then clears
+// the ticket.  The order of every addition is fixed by the launch shape.
+
+__device__ __forceinline__ void finish_reduction(const Params &p, double wg_sum)
+{
+    __shared__ int s_last;
+    __shared__ double s_red[1024];
+    if (threadIdx.x == 0) {
+        __hip_atomic_store(&p.partials[blockIdx.x], wg_sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        unsigned prev = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == gridDim.x - 1);
+    }
+    __syncthreads();
+    if (!s_last)
+        return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    double acc = 0.0;
+    for (unsigned i = threadIdx.x; i < gridDim.x; i += blockDim.x)
+        acc += __hip_atomic_load(&p.partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_red[threadIdx.x] = acc;
+    __syncthreads();
+    for (unsigned w = blockDim.x / 2; w > 0; w >>= 1) {
+        if (threadIdx.x < w)
+            s_red[threadIdx.x] += s_red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        p.out[0] = (float)(s_red[0] * p.out_scale);
+        __hip_atomic_store(p.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Window geometry of one row.
+struct Window {
+    Vec *xrow;
+    int head;
+    int nvec;
+};
+
+template <int DT>
+__device__ __forceinline__ Window row_window(const Params &p, int64_t row)
+{
+    constexpr int E = Traits<DT>::E;
+    const int64_t e0 = row * p.V + p.head0;
+    Window w;
+    w.xrow = p.x + (e0 / E);
+    w.head = (int)(e0 % E);
+    w.nvec = (int)((w.head + p.V + E - 1) / E);
+    return w;
+}
+
+// ================================================================ kernels
+
+// ---- G lanes per row, row in registers ------------------------------------
+template <int DT, int G, int K, bool BWD>
+__global__ void __launch_bounds__(256) rows_kernel(Params p)
+{
+    constexpr int E = Traits<DT>::E;
+    constexpr int GPW = 64 / G;               // rows per wavefront
+    const int lane = threadIdx.x & 63;
+    const int lig = lane & (G - 1);
+    const int wave = threadIdx.x >> 6;
+    const int nwaves = blockDim.x >> 6;
+    const int64_t wave_id = (int64_t)blockIdx.x * nwaves + wave;
+    const int64_t row_step = (int64_t)gridDim.x * nwaves * GPW;
+    const int kfull = (int)((p.V + E - 1) / E) / G;
+    double acc = 0.0;
+
+    for (int64_t rb = wave_id * GPW; rb < p.M; rb += row_step) {
+        const int64_t row = rb + lane / G;
+        const bool active = row < p.M;
+        const int64_t r = active ? row : 0;   // idle groups redo row 0 and discard it
+        const Window w = row_window<DT>(p, r);
+        const int64_t t = active ? p.targets[r] : -1;
+        GroupRed<G> red;
+        const float loss = row_in_registers<DT, K, G, BWD>(p, red, w.xrow, lig, w.nvec, kfull,
+                                                           w.head, t, active);
+        if (active && lig == 0) {
+            if (p.reduction == RED_NONE)
+                p.out[row] = loss;
+            else
+                acc += (double)loss;
+        }
+    }
+
+    if (p.reduction == RED_NONE)
+        return;
+    __shared__ double s_grp[256 / G];
+    if (lig == 0)
+        s_grp[threadIdx.x / G] = acc;
+    __syncthreads();
+    double wg_sum = 0.0;
+    if (threadIdx.x == 0) {
+        for (int i = 0; i < (int)(blockDim.x / G); ++i)
+            wg_sum += s_grp[i];
+    }
+    finish_reduction(p, wg_sum);
+}
+
+// ---- one row per workgroup, row in registers --------------------------------
+template <int DT, int W, int K, bool BWD>
+__global__ void __launch_bounds__(W * 64) wg_kernel(Params p)
+{
+    constexpr int E = Traits<DT>::E;
+    constexpr int NT = W * 64;
+    __shared__ float s_max[W], s_sum[W], s_exc[W], s_xt;
+    WgRed<W> red;
+    red.smax = s_max;
+    red.ssum = s_sum;
+    red.sexc = s_exc;
+    red.sxt = &s_xt;
+    red.wave = threadIdx.x >> 6;
+    red.lane = threadIdx.x & 63;
+    const int kfull = (int)((p.V + E - 1) / E) / NT;
+    double acc = 0.0;
+
+    for (int64_t row = blockIdx.x; row < p.M; row += gridDim.x) {
+        const Window w = row_window<DT>(p, row);
+        const float loss = row_in_registers<DT, K, NT, BWD>(p, red, w.xrow, threadIdx.x, w.nvec,
+                                                            kfull, w.head, p.targets[row], true);
+        if (threadIdx.x == 0) {
+            if (p.reduction == RED_NONE)
+                p.out[row] = loss;
+            else
+                acc += (double)loss;
+        }
+    }
+    if (p.reduction != RED_NONE)
+        finish_reduction(p, acc);
+}
+
+// ---- one row per workgroup, streamed in chunks ---------------------------------
+template <int DT, int W, int K, bool BWD>
+__global__ void __launch_bounds__(W * 64) stream_kernel(Params p)
+{
+    constexpr int E = Traits<DT>::E;
+    constexpr int NT = W * 64;
+    constexpr int CH = NT * K;                  // vectors per chunk
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    __shared__ float s_max[W], s_sum[W], s_exc[W], s_xt;
+    double acc = 0.0;
+
+    for (int64_t row = blockIdx.x; row < p.M; row += gridDim.x) {
+        const Window w = row_window<DT>(p, row);
+        const int64_t t = p.targets[row];
+        const TargetPos tp = target_pos<DT>(t, p.V, w.head);
+
+        // pass 1: online (max, sum) per lane, rescaled once per chunk
+        float m_run = -__builtin_inff();
+        float s_run = 0.0f;
+        for (int cb = 0; cb < w.nvec; cb += CH) {
+            Vec raw[K];
+            const int kfull = (w.nvec - cb) >= CH ? K : (w.nvec - cb) / NT;
+            // the chunk is a window of its own: the row's head lies in chunk 0,
+            // and its end is at element head + V - cb*E of the chunk
+            load_window<DT, K, NT>(raw, w.xrow + cb, tid, w.nvec - cb, kfull,
+                                   cb == 0 ? w.head : 0,
+                                   cb == 0 ? p.V : p.V + w.head - (int64_t)cb * E,
+                                   p.aligned != 0);
+            if (tp.valid && tp.vt >= cb && tp.vt < cb + CH) {
+                const int off = tp.vt - cb;
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+                    if (off == tid + NT * k)
+                        s_xt = vec_elem_dyn<DT>(raw[k], tp.jt);
+            }
+            float cm = m_run;
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                cm = vec_max<DT>(raw[k], cm);
+            if (cm != -__builtin_inff()) {
+                const float cmL = cm * kLog2e;
+                float add = 0.0f;
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    const float e = vec_sumexp<DT>(raw[k], cmL);
+                    add += vec_valid<NT>(k, kfull, tid, w.nvec - cb) ? e : 0.0f;
+                }
+                // the old sum is scaled by 2^(m_old - m_new); m_old = -inf gives 0
+                s_run = s_run * fast_exp2((m_run - cm) * kLog2e) + add;
+                m_run = cm;
+            }
+        }
+        float wm = group_reduce<64>(m_run, OpMax());
+        if (lane == 0)
+            s_max[wave] = wm;
+        __syncthreads();
+        float m = s_max[0];
+#pragma unroll
+        for (int i = 1; i < W; ++i)
+            m = fmaxf(m, s_max[i]);
+        const float mL = m * kLog2e;
+        const float xt = tp.valid ? s_xt : __builtin_nanf("");
+        // every lane's sum, moved to the row max
+        float ls = (m_run == -__builtin_inff()) ? 0.0f : s_run * fast_exp2(m_run * kLog2e - mL);
+        ls = group_reduce<64>(ls, OpSum());
+        if (lane == 0)
+            s_sum[wave] = ls;
+        __syncthreads();
+        float s = s_sum[0];
+#pragma unroll
+        for (int i = 1; i < W; ++i)
+            s += s_sum[i];
+
+        const float et = fast_exp2(__builtin_fmaf(xt, kLog2e, -mL));
+        const bool accurate = tp.valid && et > 0.5f * s;
+        float s_excl = s - et;
+        if (accurate) {
+            // re-read the row and sum every term but the target's
+            float lx = 0.0f;
+            for (int cb = 0; cb < w.nvec; cb += CH) {
+                Vec raw[K];
+                const int kfull = (w.nvec - cb) >= CH ? K : (w.nvec - cb) / NT;
+                load_window<DT, K, NT>(raw, w.xrow + cb, tid, w.nvec - cb, kfull,
+                                       cb == 0 ? w.head : 0,
+                                       cb == 0 ? p.V : p.V + w.head - (int64_t)cb * E,
+                                       p.aligned != 0);
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    const float e = (cb + tid + NT * k == tp.vt) ? vec_sumexp_skip<DT>(raw[k], mL, tp.jt)
+                                                                 : vec_sumexp<DT>(raw[k], mL);
+                    lx += vec_valid<NT>(k, kfull, tid, w.nvec - cb) ? e : 0.0f;
+                }
+            }
+            lx = group_reduce<64>(lx, OpSum());
+            if (lane == 0)
+                s_exc[wave] = lx;
+            __syncthreads();
+            s_excl = s_exc[0];
+#pragma unroll
+            for (int i = 1; i < W; ++i)
+                s_excl += s_exc[i];
+        }
+        const RowResult rr = row_result(tp.valid, m, xt, et, s, s_excl, accurate, p.c);
+
+        if constexpr (BWD) {
+            // pass 2: re-read the row and write the gradient over it
+            const GradCoef<DT> gc = grad_coef<DT>(m, mL, __log2f(s), p.c, p.log2c);
+            for (int cb = 0; cb < w.nvec; cb += CH) {
+                Vec raw[K];
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    const int v = cb + tid + NT * k;
+                    if (v < w.nvec)
+                        raw[k] = w.xrow[v];
+                }
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    const int v = cb + tid + NT * k;
+                    if (v < w.nvec) {
+                        const Vec g = grad_vec<DT>(raw[k], gc, v == tp.vt, tp.jt, rr.gt);
+                        store_grad<DT>(w.xrow, v, g, w.head, p.V, p.aligned);
+                    }
+                }
+            }
+        }
+        if (tid == 0) {
+            if (p.reduction == RED_NONE)
+                p.out[row] = rr.loss;
+            else
+                acc += (double)rr.loss;
+        }
+        __syncthreads();   // s_xt and the LDS partials are reused by the next row
+    }
+    if (p.reduction != RED_NONE)
+        finish_reduction(p, acc);
+}
+
+}  // namespace cek

@@ -1,0 +1,16 @@
+// fp32 kernel instances, and the M == 0 reduction kernel.
+#define CE_DT DT_F32
+#define CE_GET_KERNEL get_kernel_f32
+#include "ce_kernels_inst.h"
+
+namespace cek {
+
+// M == 0: the mean of no rows is NaN, their sum is 0.
+__global__ void empty_reduce_kernel(float *out, float value)
+{
+    if (threadIdx.x == 0)
+        out[0] = value;
+}
+
+const void *empty_reduce_fn() { return (const void *)&empty_reduce_kernel; }
+}  // namespace cek

@@ -1,0 +1,121 @@
+"""Helpers shared by the GPU parity tests: run the HIP path through the C ABI
+binding, run the oracle on a host copy of the same inputs, and compare with the
+tolerances the tests state."""
+import math
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+from softmax_cross_entropy_fwd_amd import inputs  # noqa: E402
+
+# Loss tolerances: relative 1e-5 on the mean/sum for every storage type (the
+# arithmetic is fp32 on exactly widened inputs; the stated bar for 16-bit
+# inputs is 2e-3), and per row  rtol*|loss| + 4 ulp_fp32(max(|m|, |x_t|, 1)),
+# the floor covering the cancellation in lse - x_t.
+LOSS_RTOL = 1e-5
+# Gradients: at most 2 units in the last place of the storage type (+-0 equal);
+# fp32 storage: |d| <= 1e-5 |g| + 1e-7 c.
+GRAD_ULP = 2
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def ulp32(x):
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    x = np.maximum(x, 1.0)
+    return np.spacing(x.astype(np.float32)).astype(np.float64)
+
+
+def row_stats(xb, dtype):
+    """fp64 row max of the stored values (for the per-row loss floor)."""
+    w = widen(xb, dtype)
+    with np.errstate(invalid="ignore"):
+        return np.max(w, axis=1)
+
+
+def widen(xb, dtype):
+    if dtype == "f32":
+        return xb.astype(np.float64)
+    if dtype == "f16":
+        return xb.view(np.float16).astype(np.float64)
+    u = xb.astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def check_row_losses(got, want, xb, targets, dtype, rtol=LOSS_RTOL):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape
+    nan_w = np.isnan(want)
+    np.testing.assert_array_equal(np.isnan(got), nan_w)
+    ok = ~nan_w
+    if not ok.any():
+        return 0.0
+    w = widen(xb[ok], dtype)
+    m = np.max(w, axis=1)
+    t = np.asarray(targets)[ok]
+    xt = w[np.arange(w.shape[0]), t]
+    inf = np.isinf(want[ok])
+    np.testing.assert_array_equal(got[ok][inf], want[ok][inf])
+    fin = ~inf
+    floor = 4 * ulp32(np.maximum(np.abs(m), np.abs(xt)))
+    err = np.abs(got[ok] - want[ok])
+    bound = rtol * np.abs(want[ok]) + floor
+    bad = fin & (err > bound)
+    assert not bad.any(), "row loss mismatch at rows %s: got %s want %s" % (
+        np.nonzero(ok)[0][bad][:5], got[ok][bad][:5], want[ok][bad][:5])
+    return float(np.max(err[fin] / np.maximum(bound[fin], 1e-300))) if fin.any() else 0.0
+
+
+def check_scalar(got, want, rtol=LOSS_RTOL):
+    got, want = float(got), float(want)
+    if math.isnan(want):
+        assert math.isnan(got)
+        return
+    assert abs(got - want) <= rtol * abs(want) + 1e-30, (got, want)
+
+
+def ordered16(bits):
+    b = bits.astype(np.int32)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def check_grads(got_bits, want_bits, dtype, c, want64=None):
+    """got/want: uint16 bit patterns (fp16/bf16) or float32 arrays."""
+    if dtype == "f32":
+        g = np.asarray(got_bits, dtype=np.float64)
+        w = np.asarray(want64 if want64 is not None else want_bits, dtype=np.float64)
+        assert not np.isnan(g).any()
+        err = np.abs(g - w)
+        bound = 1e-5 * np.abs(w) + 1e-7 * c
+        bad = err > bound
+        assert not bad.any(), "fp32 grad mismatch at %s: got %s want %s" % (
+            np.argwhere(bad)[:5].tolist(), g[bad][:5], w[bad][:5])
+        return
+    gb = np.asarray(got_bits, dtype=np.uint16)
+    wb = np.asarray(want_bits, dtype=np.uint16)
+    nan_mask = 0x7C00 if dtype == "f16" else 0x7F80
+    frac_mask = 0x03FF if dtype == "f16" else 0x007F
+    gnan = ((gb & nan_mask) == nan_mask) & ((gb & frac_mask) != 0)
+    wnan = ((wb & nan_mask) == nan_mask) & ((wb & frac_mask) != 0)
+    np.testing.assert_array_equal(gnan, wnan)
+    d = np.abs(ordered16(gb) - ordered16(wb))
+    d[wnan] = 0
+    bad = d > GRAD_ULP
+    assert not bad.any(), "grad ulp mismatch (max %d) at %s: got %s want %s" % (
+        d.max(), np.argwhere(bad)[:5].tolist(), [hex(v) for v in gb[bad][:5]],
+        [hex(v) for v in wb[bad][:5]])
+    return int(d.max())
+
+
+def host_grad_bits(t):
+    return inputs.host_bits(t)

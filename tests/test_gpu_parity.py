@@ -1,0 +1,261 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, element by
+element, on seeded inputs that span several tiles and ragged tails.
+
+Tolerances (stated once in gpu_util): row and reduced losses 1e-5 relative
+(+ 4 fp32 ulps of the row's largest magnitude per row); gradients within 2
+ulps of the storage type; targets, NaN positions and untouched memory exact.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+from gpu_util import (check_grads, check_row_losses, check_scalar, host_grad_bits, oracle,
+                      inputs, say)
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ["f32", "f16", "bf16"]
+CANARY = {"f32": 0x7FC0DEAD, "f16": 0x7E5A, "bf16": 0x7FDA}
+
+
+@pytest.fixture(scope="module")
+def ce():
+    import torch
+    assert torch.cuda.is_available(), "GPU test run without a GPU"
+    import softmax_cross_entropy_fwd_amd as ce
+    ce.load_library()
+    return ce
+
+
+def place(x, offset, pad=24):
+    """Copy host logits into a device buffer at an element offset, with
+    canary elements before and after; returns (view, buffer)."""
+    import torch
+    M, V = x.shape
+    n = M * V
+    buf = torch.empty(offset + n + pad, dtype=x.dtype, device="cuda:0")
+    canary_bits = CANARY[inputs.dtype_name(x)]
+    bits_dtype = torch.int32 if x.dtype == torch.float32 else torch.int16
+    if bits_dtype == torch.int16 and canary_bits >= 0x8000:
+        canary_bits -= 0x10000
+    buf.view(bits_dtype).fill_(canary_bits)
+    view = buf[offset:offset + n].view(M, V)
+    view.copy_(x.to("cuda:0"))
+    return view, buf
+
+
+def canaries_intact(buf, offset, n, dtype):
+    import torch
+    bits_dtype = torch.int32 if dtype == "f32" else torch.int16
+    b = buf.view(bits_dtype).cpu().numpy().astype(np.int64) & (0xFFFFFFFF if dtype == "f32" else 0xFFFF)
+    c = CANARY[dtype]
+    return bool(np.all(b[:offset] == c) and np.all(b[offset + n:] == c))
+
+
+def run_and_check(ce, dtype, M, V, sigma=1.0, seed=0, structure=None, reduction="mean",
+                  op="fwd", offset=0, targets=None):
+    import torch
+    say("case", dtype, M, V, sigma, seed, structure, reduction, op, offset)
+    x, t = inputs.make(dtype, M, V, sigma, seed, structure, device="cpu")
+    if targets is not None:
+        t = torch.as_tensor(targets, dtype=torch.int64)
+    xb, tn = inputs.host_bits(x), t.numpy()
+    xg, buf = place(x, offset)
+    tg = t.to("cuda:0")
+    if op == "fwd":
+        got = ce.ce_fwd(xg, tg, reduction)
+    else:
+        got = ce.ce_fwd_bwd_inplace(xg, tg, reduction)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf, offset, M * V, dtype), "wrote outside the logits"
+    per_row = oracle.loss_rows(xb, tn, dtype=dtype)
+    if reduction == "none":
+        check_row_losses(got.cpu().numpy(), per_row, xb, tn, dtype)
+    else:
+        check_scalar(got.item(), oracle.reduce(per_row, reduction))
+    if op == "fwd_bwd":
+        c = 1.0 / M if reduction == "mean" else 1.0
+        want, want64 = oracle.grad_rows(xb, tn, dtype=dtype, c=c, want64=True)
+        check_grads(host_grad_bits(xg), want, dtype, c, want64)
+    else:
+        np.testing.assert_array_equal(inputs.host_bits(xg), xb)   # fwd leaves logits alone
+    return got
+
+
+# --------------------------------------------------------------- workloads
+
+def test_tiny_mean_and_none(ce):
+    c = inputs.CONFIGS["tiny"]
+    for red in ("mean", "none", "sum"):
+        run_and_check(ce, c["dtype"], c["M"], c["V"], c["sigma"], c["seed"], reduction=red)
+        run_and_check(ce, c["dtype"], c["M"], c["V"], c["sigma"], c["seed"], reduction=red,
+                      op="fwd_bwd")
+
+
+@pytest.mark.parametrize("name,M", [("classifier", 96), ("lmhead", 12), ("stress", 300),
+                                    ("skinny", 4099)])
+def test_workload_shapes_small_m(ce, name, M):
+    c = inputs.CONFIGS[name]
+    for red in ("none", "mean"):
+        for op in ("fwd", "fwd_bwd"):
+            run_and_check(ce, c["dtype"], M, c["V"], c["sigma"], c["seed"], c["structure"],
+                          reduction=red, op=op)
+
+
+# ----------------------------------------------------------- V and alignment
+
+V_SWEEP = [1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256,
+           257, 511, 512, 513, 1000, 1023, 1024, 1025, 2047, 2048, 2049, 4095, 4096, 4097, 8191,
+           8192, 8193, 16383, 16384, 16385, 32768, 50257, 65536, 65537, 131071, 131072, 131073,
+           262151]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_v_sweep(ce, dtype):
+    for V in V_SWEEP:
+        M = 7 if V < 100000 else 3
+        sigma = 8.0 if dtype == "f16" else 3.0
+        run_and_check(ce, dtype, M, V, sigma, seed=V, reduction="none")
+        run_and_check(ce, dtype, M, V, sigma, seed=V + 1, reduction="mean", op="fwd_bwd")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_alignment_sweep(ce, dtype):
+    E = 4 if dtype == "f32" else 8
+    for V in (1, 3, 127, 1000, 4097, 50257, 131072):
+        for off in range(1, E):
+            M = 5 if V < 100000 else 2
+            run_and_check(ce, dtype, M, V, 2.0, seed=17 * off + V, reduction="none", offset=off)
+            run_and_check(ce, dtype, M, V, 2.0, seed=17 * off + V + 1, reduction="sum",
+                          op="fwd_bwd", offset=off)
+
+
+# --------------------------------------------------------- every kernel shape
+
+SHAPES = ["rows:1:1", "rows:1:2", "rows:1:4", "rows:2:4", "rows:4:4", "rows:8:4", "rows:16:4",
+          "rows:32:4", "rows:64:4", "rows:64:8", "rows:64:16", "rows:4:8", "rows:8:2",
+          "rows:16:2", "rows:32:1", "rows:32:8", "rows:32:16",
+          "wg:4:8", "wg:8:8", "wg:8:12", "wg:8:16", "wg:16:8", "wg:16:12", "wg:16:16",
+          "wg:4:16", "wg:16:4", "stream:4:8", "stream:8:4", "stream:8:8", "stream:16:4",
+          "stream:4:16"]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_every_kernel_shape(ce, shape, monkeypatch):
+    kind, a, b = shape.split(":")
+    a, b = int(a), int(b)
+    cap = a * b if kind == "rows" else (a * 64 * b if kind == "wg" else 1 << 30)
+    monkeypatch.setenv("CE_FORCE_PLAN", shape)
+    for dtype in DTYPES:
+        E = 4 if dtype == "f32" else 8
+        for V in (1, 5, 13 * E + 3, 64 * E, 64 * E + 1, 3000, 20000):
+            if (V + 2 * E - 2) // E > cap:
+                continue
+            M = 37 if V < 4000 else 9
+            plan = ce.ce_plan_describe(M, V, {"f32": 0, "f16": 1, "bf16": 2}[dtype], "none")
+            if V % E == 0:
+                assert plan.startswith(shape), (plan, shape)
+            run_and_check(ce, dtype, M, V, 4.0, seed=V, reduction="none", offset=V % 3)
+            run_and_check(ce, dtype, M, V, 4.0, seed=V + 5, reduction="mean", op="fwd_bwd",
+                          offset=(V // 2) % 2)
+
+
+# ------------------------------------------------------------------ edge cases
+
+def test_empty_batch(ce):
+    import torch
+    for dtype in DTYPES:
+        x = torch.empty(0, 10, dtype=inputs.TORCH_DTYPE[dtype], device="cuda:0")
+        t = torch.empty(0, dtype=torch.int64, device="cuda:0")
+        assert math.isnan(ce.ce_fwd(x, t, "mean").item())
+        assert ce.ce_fwd(x, t, "sum").item() == 0.0
+        assert ce.ce_fwd(x, t, "none").numel() == 0
+        assert math.isnan(ce.ce_fwd_bwd_inplace(x, t, "mean").item())
+
+
+def test_out_of_range_targets(ce):
+    for dtype in DTYPES:
+        M, V = 6, 300
+        targets = [0, -1, V, 5, 1 << 40, V - 1]
+        run_and_check(ce, dtype, M, V, 2.0, seed=3, reduction="none", targets=targets)
+        run_and_check(ce, dtype, M, V, 2.0, seed=3, reduction="sum", op="fwd_bwd",
+                      targets=targets)
+        got = run_and_check(ce, dtype, M, V, 2.0, seed=3, reduction="mean", targets=targets)
+        assert math.isnan(got.item())
+
+
+def test_stress_structure_rows(ce):
+    # dominant targets, all-equal rows and -inf entries at a size the oracle
+    # does in a blink; the fractions make sure every kind of row is present
+    for dtype in DTYPES:
+        for V in (50257, 1000, 96):
+            run_and_check(ce, dtype, 200, V, 8.0, seed=104, structure="stress", reduction="none")
+            run_and_check(ce, dtype, 200, V, 8.0, seed=104, structure="stress", reduction="mean",
+                          op="fwd_bwd")
+
+
+def test_dominant_target_loss_and_grad_accuracy(ce):
+    import torch
+    # p_t close to 1: the target's gradient and the small loss keep their
+    # relative accuracy (recomputed from the other terms)
+    for dtype in DTYPES:
+        for V in (7, 1000, 50257):
+            for gap in (3.0, 9.0, 15.0):
+                M = 8
+                x, t = inputs.make(dtype, M, V, 1.0, seed=int(gap) + V)
+                xf = x.float()
+                xf[torch.arange(M), t] = xf.max(dim=1).values + gap
+                xd = xf.to(x.dtype)
+                xb, tn = inputs.host_bits(xd), t.numpy()
+                xg = xd.to("cuda:0")
+                got = ce.ce_fwd_bwd_inplace(xg, t.to("cuda:0"), "none")
+                torch.cuda.synchronize()
+                check_row_losses(got.cpu().numpy(), oracle.loss_rows(xb, tn, dtype=dtype), xb,
+                                 tn, dtype, rtol=1e-4)
+                want, want64 = oracle.grad_rows(xb, tn, dtype=dtype, c=1.0, want64=True)
+                check_grads(host_grad_bits(xg), want, dtype, 1.0, want64)
+
+
+def test_uniform_rows_closed_form(ce):
+    import torch
+    for dtype in DTYPES:
+        for V in (1000, 4096, 50257, 131072, 128):
+            for L in (0.0, -7.25, 30.5):
+                x = torch.full((3, V), L, dtype=inputs.TORCH_DTYPE[dtype], device="cuda:0")
+                t = torch.tensor([0, V // 2, V - 1], device="cuda:0")
+                got = ce.ce_fwd(x, t, "none").cpu().numpy()
+                np.testing.assert_allclose(got, math.log(V), rtol=1e-5,
+                                           atol=4 * np.spacing(np.float32(max(abs(L), 1))))
+
+
+def test_deterministic_bits(ce):
+    import torch
+    for name, M in (("classifier", 2048), ("skinny", 70000), ("stress", 256)):
+        c = inputs.CONFIGS[name]
+        x, t = inputs.make(c["dtype"], M, c["V"], c["sigma"], c["seed"], c["structure"],
+                           device="cuda:0")
+        a = ce.ce_fwd(x, t, "mean").item()
+        b = ce.ce_fwd(x, t, "mean").item()
+        assert np.float32(a).tobytes() == np.float32(b).tobytes()
+        y = x.clone()
+        la = ce.ce_fwd_bwd_inplace(x, t, "mean").item()
+        lb = ce.ce_fwd_bwd_inplace(y, t, "mean").item()
+        torch.cuda.synchronize()
+        assert np.float32(la).tobytes() == np.float32(lb).tobytes()
+        assert torch.equal(x.view(torch.int16 if x.element_size() == 2 else torch.int32),
+                           y.view(torch.int16 if y.element_size() == 2 else torch.int32))
+
+
+def test_workspace_reuse_and_streams(ce):
+    import torch
+    x, t = inputs.make("f32", 5000, 333, 1.0, seed=9, device="cuda:0")
+    want = oracle.fwd(inputs.host_bits(x), t.cpu().numpy(), reduction="mean")
+    s = torch.cuda.Stream()
+    for i in range(5):
+        check_scalar(ce.ce_fwd(x, t, "mean").item(), want)
+        with torch.cuda.stream(s):
+            r = ce.ce_fwd(x, t, "mean")
+        s.synchronize()
+        check_scalar(r.item(), want)
