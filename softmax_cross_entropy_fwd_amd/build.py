@@ -3,7 +3,8 @@
     python -m softmax_cross_entropy_fwd_amd.build [-v]
 
 Each csrc/*.hip unit is compiled to an object in parallel, then linked into
-softmax_cross_entropy_fwd_amd/libce.so.  Packed-fp32 VALU forms are disabled
+softmax_cross_entropy_fwd_amd/libce.so; probe/bw_probe.hip (HBM bandwidth
+probes for the bench) goes into libce_probe.so.  Packed-fp32 VALU forms are disabled
 for device code; no fast-math, so fp32 rounding and denormals follow IEEE.
 """
 import concurrent.futures as cf
@@ -17,6 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libce.so")
+PROBE_SRC = os.path.join(PKG, "probe", "bw_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libce_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -55,6 +58,12 @@ def build(verbose=False, jobs=None):
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    # the bandwidth probes the bench measures the ceiling with (own library)
+    pobj = _compile(PROBE_SRC, verbose)
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    subprocess.run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", pobj, "-o", tmp],
+                   check=True)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

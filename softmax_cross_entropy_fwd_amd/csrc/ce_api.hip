@@ -27,19 +27,31 @@ size_t elem_size(int dtype) { return dtype == CE_F32 ? 4 : 2; }
 
 struct Plan {
     int kind = 0, a = 0, b = 0;
+    bool exact = false;
+    int nbuf = 1;
     KernelRef k{nullptr, 0};
     int64_t grid = 0;
     int occupancy = 0;
     int cus = 0;
 };
 
-KernelRef lookup(int dtype, int kind, int a, int b, bool bwd)
+KernelRef lookup(int dtype, int kind, int a, int b, bool bwd, bool exact, int nbuf)
 {
     switch (dtype) {
-    case CE_F32: return cek::get_kernel_f32(kind, a, b, bwd);
-    case CE_F16: return cek::get_kernel_f16(kind, a, b, bwd);
-    default: return cek::get_kernel_bf16(kind, a, b, bwd);
+    case CE_F32: return cek::get_kernel_f32(kind, a, b, bwd, exact, nbuf);
+    case CE_F16: return cek::get_kernel_f16(kind, a, b, bwd, exact, nbuf);
+    default: return cek::get_kernel_bf16(kind, a, b, bwd, exact, nbuf);
     }
+}
+
+// Vectors one tile of a shape covers (0 for the stream kernels: any row).
+int64_t tile_vectors(int kind, int a, int b)
+{
+    if (kind == cek::KIND_ROWS)
+        return (int64_t)a * b;
+    if (kind == cek::KIND_WG)
+        return (int64_t)a * 64 * b;
+    return 0;
 }
 
 int pow2ceil(int64_t n)
@@ -50,39 +62,52 @@ int pow2ceil(int64_t n)
     return p;
 }
 
-// Mapping and tile for a row of nvec 16-byte vectors (worst case over rows).
-void choose_shape(int64_t nvec, int *kind, int *a, int *b)
+// Mapping and tile for a row of nvec 16-byte vectors (worst case over rows),
+// from measurements on MI355X:
+//  - rows up to 16 KB sit in the registers of 1..64 lanes (rows kernel);
+//  - longer rows are streamed by a 16- or 8-wave workgroup for the forward;
+//  - the fused backward keeps rows up to 256 KB in the registers of a
+//    16-wave workgroup (one HBM read per element), longer ones re-read.
+void choose_shape(int64_t nvec, bool bwd, int *kind, int *a, int *b, int *nbuf)
 {
+    *nbuf = 1;
+    *kind = cek::KIND_ROWS;
     if (nvec <= 4) {
-        *kind = cek::KIND_ROWS;
         *a = 1;
         *b = nvec <= 1 ? 1 : nvec <= 2 ? 2 : 4;
+    } else if (nvec <= 8) {
+        *a = 2;
+        *b = 4;
+    } else if (nvec <= 16) {
+        *a = 4;
+        *b = 4;
+    } else if (nvec <= 32) {
+        *a = 4;
+        *b = 8;
+        *nbuf = 2;
+    } else if (nvec <= 64) {
+        *a = 16;
+        *b = 4;
+    } else if (nvec <= 128) {
+        *a = 32;
+        *b = 4;
     } else if (nvec <= 256) {
-        *kind = cek::KIND_ROWS;
-        *a = pow2ceil((nvec + 3) / 4);
+        *a = 64;
         *b = 4;
     } else if (nvec <= 512) {
-        *kind = cek::KIND_ROWS;
         *a = 64;
         *b = 8;
     } else if (nvec <= 1024) {
-        *kind = cek::KIND_ROWS;
         *a = 64;
         *b = 16;
-    } else if (nvec <= 16384) {
-        static const int cand[][2] = {{4, 8}, {8, 8}, {8, 12}, {8, 16}, {16, 12}, {16, 16}};
+    } else if (bwd && nvec <= 16384) {
         *kind = cek::KIND_WG;
-        for (const auto &c : cand) {
-            if ((int64_t)c[0] * 64 * c[1] >= nvec) {
-                *a = c[0];
-                *b = c[1];
-                break;
-            }
-        }
+        *a = 16;
+        *b = nvec <= 4096 ? 4 : nvec <= 8192 ? 8 : nvec <= 12288 ? 12 : 16;
     } else {
         *kind = cek::KIND_STREAM;
-        *a = 8;
-        *b = 8;
+        *a = nvec >= 16384 ? 16 : 8;
+        *b = 4;
     }
 }
 
@@ -158,23 +183,27 @@ int make_plan(int64_t M, int64_t V, int dtype, bool bwd, bool aligned, Plan *pla
 {
     const int E = 16 / (int)elem_size(dtype);
     const int64_t nvec = window_vectors(V, E, aligned);
-    int kind = 0, a = 0, b = 0;
-    choose_shape(nvec, &kind, &a, &b);
+    int kind = 0, a = 0, b = 0, nbuf = 1;
+    choose_shape(nvec, bwd, &kind, &a, &b, &nbuf);
     int fk, fa, fb;
     if (forced_shape(&fk, &fa, &fb)) {
-        KernelRef f = lookup(dtype, fk, fa, fb, bwd);
-        bool fits = fk == cek::KIND_STREAM ||
-                    (fk == cek::KIND_ROWS ? (int64_t)fa * fb >= nvec : (int64_t)fa * 64 * fb >= nvec);
-        if (f.fn && fits) {
+        const int64_t tile = tile_vectors(fk, fa, fb);
+        if (lookup(dtype, fk, fa, fb, bwd, false, 1).fn && (fk == cek::KIND_STREAM || tile >= nvec)) {
             kind = fk;
             a = fa;
             b = fb;
+            nbuf = 1;
         }
     }
     plan->kind = kind;
     plan->a = a;
     plan->b = b;
-    plan->k = lookup(dtype, kind, a, b, bwd);
+    plan->exact = aligned && tile_vectors(kind, a, b) == nvec;
+    plan->nbuf = kind == cek::KIND_ROWS ? nbuf : 1;
+    const char *nb = std::getenv("CE_FORCE_NBUF");
+    if (kind == cek::KIND_ROWS && nb && (std::atoi(nb) == 1 || std::atoi(nb) == 2))
+        plan->nbuf = std::atoi(nb);
+    plan->k = lookup(dtype, kind, a, b, bwd, plan->exact, plan->nbuf);
     if (!plan->k.fn)
         return CE_ERR_HIP;
     int dev = 0;
@@ -188,7 +217,17 @@ int make_plan(int64_t M, int64_t V, int dtype, bool bwd, bool aligned, Plan *pla
         return rc;
     int64_t rows_per_wg = kind == cek::KIND_ROWS ? (plan->k.block / 64) * (64 / a) : 1;
     int64_t needed = (M + rows_per_wg - 1) / rows_per_wg;
-    int64_t cap = (int64_t)plan->cus * plan->occupancy;
+    // Few deep waves beat many shallow ones here (measured): each wave keeps
+    // a whole row of loads in flight, so the rows kernel runs 4 waves per CU
+    // and the workgroup kernels 16.
+    const int waves_per_wg = plan->k.block / 64;
+    const int target_waves = kind == cek::KIND_ROWS ? 4 : 16;
+    int wg_per_cu = target_waves / waves_per_wg;
+    if (wg_per_cu < 1)
+        wg_per_cu = 1;
+    if (wg_per_cu > plan->occupancy)
+        wg_per_cu = plan->occupancy;
+    int64_t cap = (int64_t)plan->cus * wg_per_cu;
     const char *g = std::getenv("CE_FORCE_GRID");
     if (g && *g && std::atoll(g) > 0)
         cap = std::atoll(g);
@@ -279,6 +318,8 @@ int run(const void *logits, const int64_t *targets, int64_t M, int64_t V, int dt
     p.V = V;
     p.head0 = head0;
     p.aligned = aligned ? 1 : 0;
+    const char *map = std::getenv("CE_ROW_MAP");
+    p.blocked = (map && !std::strcmp(map, "blocked")) ? 1 : 0;
     p.reduction = reduction;
     const double c = reduction == CE_MEAN ? 1.0 / (double)M : 1.0;
     p.c = (float)c;
@@ -356,8 +397,9 @@ int ce_plan_describe(int64_t M, int64_t V, ce_dtype_t dtype, ce_reduction_t redu
     if (rc)
         return rc;
     static const char *names[] = {"rows", "wg", "stream"};
-    std::snprintf(buf, buf_len, "%s:%d:%d block=%d grid=%lld occupancy=%d cus=%d",
-                  names[plan.kind], plan.a, plan.b, plan.k.block, (long long)plan.grid,
+    std::snprintf(buf, buf_len, "%s:%d:%d%s%s block=%d grid=%lld occupancy=%d cus=%d",
+                  names[plan.kind], plan.a, plan.b, plan.exact ? " exact" : "",
+                  plan.nbuf == 2 ? " nbuf=2" : "", plan.k.block, (long long)plan.grid,
                   plan.occupancy, plan.cus);
     return CE_OK;
 }

@@ -57,6 +57,7 @@ struct Params {
     int64_t V;
     int head0;               // elements between x and logits[0]
     int aligned;             // every row starts and ends on a 16-byte boundary
+    int blocked;             // each workgroup takes a contiguous band of rows
     int reduction;
     float c;                 // gradient scale
     float log2c;             // log2(c)
@@ -242,12 +243,15 @@ __device__ __forceinline__ TargetPos target_pos(int64_t t, int64_t V, int head)
 // Keeps the compiler from carrying values derived from the row (widened
 // elements, exponentials) from one pass to the next: each pass recomputes
 // them from the packed registers, which bounds register use to the packed row.
-template <int K>
+template <int DT, int K>
 __device__ __forceinline__ void opt_barrier(Vec (&raw)[K])
 {
+    if constexpr (DT != DT_F32) {   // fp32 elements need no widening
 #pragma unroll
-    for (int k = 0; k < K; ++k)
-        asm volatile("" : "+v"(raw[k].w[0]), "+v"(raw[k].w[1]), "+v"(raw[k].w[2]), "+v"(raw[k].w[3]));
+        for (int k = 0; k < K; ++k)
+            asm volatile("" : "+v"(raw[k].w[0]), "+v"(raw[k].w[1]), "+v"(raw[k].w[2]),
+                         "+v"(raw[k].w[3]));
+    }
 }
 
 // Loads window vectors lidx + STRIDE*k (k < K) of a row whose window has nvec
@@ -461,16 +465,7 @@ __device__ __forceinline__ void store_grad(Vec *xrow, int v, const Vec &g, int h
 // G lanes of one wavefront per row.
 template <int G>
 struct GroupRed {
-    float xt_local = 0.0f;
-    int owner = 0;
-    __device__ __forceinline__ void publish_xt(float v, bool is_owner, int owner_idx)
-    {
-        if (is_owner)
-            xt_local = v;
-        owner = owner_idx;
-    }
     __device__ __forceinline__ float max(float v) { return group_reduce<G>(v, OpMax()); }
-    __device__ __forceinline__ float xt() { return group_bcast<G>(xt_local, owner); }
     __device__ __forceinline__ float sum(float v) { return group_reduce<G>(v, OpSum()); }
     __device__ __forceinline__ float sum_excl(float v) { return group_reduce<G>(v, OpSum()); }
 };
@@ -481,13 +476,8 @@ struct GroupRed {
 // after it, so the slots are safely reused row after row.
 template <int W>
 struct WgRed {
-    float *smax, *ssum, *sexc, *sxt;
+    float *smax, *ssum, *sexc;
     int wave, lane;
-    __device__ __forceinline__ void publish_xt(float v, bool is_owner, int)
-    {
-        if (is_owner)
-            *sxt = v;
-    }
     __device__ __forceinline__ float combine(float v, float *slot, bool is_max)
     {
         v = is_max ? group_reduce<64>(v, OpMax()) : group_reduce<64>(v, OpSum());
@@ -501,74 +491,207 @@ struct WgRed {
         return r;
     }
     __device__ __forceinline__ float max(float v) { return combine(v, smax, true); }
-    __device__ __forceinline__ float xt() { return *sxt; }
     __device__ __forceinline__ float sum(float v) { return combine(v, ssum, false); }
     __device__ __forceinline__ float sum_excl(float v) { return combine(v, sexc, false); }
 };
 
-// One row held in registers: K vectors per lane, lane lidx of STRIDE lanes.
-// Returns the row's loss (identical in every lane of the row).  Lanes with
-// write == false take part in the reductions but store nothing.
-template <int DT, int K, int STRIDE, bool BWD, class Red>
-__device__ __forceinline__ float row_in_registers(const Params &p, Red &red, Vec *xrow, int lidx,
-                                                  int nvec, int kfull, int head, int64_t t,
-                                                  bool write)
+// The logit x[row, t] read straight from memory (the row's own lines are being
+// fetched at the same time, so this costs a cache hit), widened to fp32.
+template <int DT>
+__device__ __forceinline__ float load_logit(const Params &p, int64_t row, int64_t t)
 {
-    Vec raw[K];
-    load_window<DT, K, STRIDE>(raw, xrow, lidx, nvec, kfull, head, p.V, p.aligned);
-    const TargetPos tp = target_pos<DT>(t, p.V, head);
-    const int kt = tp.valid ? tp.vt / STRIDE : -1;
-    const int owner = tp.valid ? tp.vt % STRIDE : 0;
-    const bool is_owner = tp.valid && lidx == owner;
+    const int64_t e = row * p.V + p.head0 + t;
+    if constexpr (DT == DT_F32) {
+        return reinterpret_cast<const float *>(p.x)[e];
+    } else {
+        const uint16_t b = reinterpret_cast<const uint16_t *>(p.x)[e];
+        if constexpr (DT == DT_BF16)
+            return __uint_as_float((uint32_t)b << 16);
+        else
+            return (float)__builtin_bit_cast(_Float16, b);
+    }
+}
 
-    float xt_l = 0.0f;
-    float lm = -__builtin_inff();
+// Issues the loads of a row's window vectors lidx + STRIDE*k into raw.  EXACT:
+// every row's window is exactly STRIDE*K vectors (aligned rows), so no index
+// is clamped.  Otherwise a lane past the window re-reads the window's last
+// vector (a cache hit) and the sums drop that copy (vec_valid).
+template <int DT, int K, int STRIDE, bool EXACT>
+__device__ __forceinline__ void issue_loads(Vec (&raw)[K], const Vec *xrow, int lidx, int nvec)
+{
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        lm = vec_max<DT>(raw[k], lm);
-        if (k == kt && is_owner)
-            xt_l = vec_elem_dyn<DT>(raw[k], tp.jt);
+        const int v = lidx + STRIDE * k;
+        raw[k] = xrow[(EXACT || v < nvec) ? v : nvec - 1];
     }
-    red.publish_xt(xt_l, is_owner, owner);
+}
+
+// -inf over the window elements outside the row (unaligned rows only): only
+// the window's first vector, its last and copies of the last hold any.
+template <int DT, int K, int STRIDE>
+__device__ __forceinline__ void mask_window(Vec (&raw)[K], int lidx, int nvec, int kfull, int head,
+                                            int64_t V)
+{
+    constexpr int E = Traits<DT>::E;
+    if (lidx == 0 && head > 0)
+        mask_outside<DT>(raw[0], head, E);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        if (k + 1 >= kfull) {
+            const int v = lidx + STRIDE * k;
+            if (v >= nvec - 1)
+                mask_outside<DT>(raw[k], 0, (int)(head + V - (int64_t)(nvec - 1) * E));
+        }
+    }
+}
+
+template <int STRIDE, bool EXACT>
+__device__ __forceinline__ bool vec_valid(int k, int kfull, int lidx, int nvec)
+{
+    return EXACT || k < kfull || lidx + STRIDE * k < nvec;
+}
+
+// Sum over the row leaving out the target's term, re-read from memory one
+// vector at a time: the rare rows whose target carries more than half of the
+// mass (p_t > 1/2).  Kept serial so it adds no register pressure.
+template <int DT, int K, int STRIDE, bool EXACT>
+__device__ __attribute__((noinline)) float sum_without_target(const Params &p, const Vec *xrow,
+                                                              int lidx, int nvec, int head,
+                                                              float mL, int vt, int jt)
+{
+    constexpr int E = Traits<DT>::E;
+    float lx = 0.0f;
+#pragma unroll 1
+    for (int k = 0; k < K; ++k) {
+        const int v = lidx + STRIDE * k;
+        if (v >= nvec)
+            break;
+        Vec r = xrow[v];
+        if (!EXACT && !p.aligned) {
+            if (v == 0 && head > 0)
+                mask_outside<DT>(r, head, E);
+            if (v == nvec - 1)
+                mask_outside<DT>(r, 0, (int)(head + p.V - (int64_t)v * E));
+        }
+        lx += (v == vt) ? vec_sumexp_skip<DT>(r, mL, jt) : vec_sumexp<DT>(r, mL);
+    }
+    return lx;
+}
+
+// Element jt of a packed vector replaced by val (rounded to the storage type).
+template <int DT>
+__device__ __forceinline__ void set_elem(Vec &g, int jt, float val)
+{
+    constexpr int E = Traits<DT>::E;
+    if constexpr (DT == DT_F32) {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            if (j == jt)
+                g.w[j] = __float_as_uint(val);
+    } else {
+        const uint32_t b = pack2<DT>(val, val) & 0xffffu;
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            if (j == jt)
+                g.w[j >> 1] = (j & 1) ? ((g.w[j >> 1] & 0x0000ffffu) | (b << 16))
+                                      : ((g.w[j >> 1] & 0xffff0000u) | b);
+    }
+}
+
+// Window geometry of one row.
+struct Window {
+    Vec *xrow;
+    int head;
+    int nvec;
+};
+
+template <int DT>
+__device__ __forceinline__ Window row_window(const Params &p, int64_t row)
+{
+    constexpr int E = Traits<DT>::E;
+    const int64_t e0 = row * p.V + p.head0;
+    Window w;
+    w.xrow = p.x + (e0 / E);
+    w.head = (int)(e0 % E);
+    w.nvec = (int)((w.head + p.V + E - 1) / E);
+    return w;
+}
+
+// Row state carried by the register pipeline: the row in raw[] was loaded
+// (by the previous iteration) from window w.
+struct RowRef {
+    int64_t row;     // the row held (clamped to a real row for idle lanes)
+    bool active;     // this lane's row is a real row
+    int64_t t;       // its target, -1 for idle lanes
+    Window w;
+};
+
+// One pipeline step on a row held in registers (K vectors per lane, lane lidx
+// of STRIDE lanes): the loads of `next` are issued as soon as the registers
+// are free (during the sum pass for the forward; right after each gradient
+// vector is stored for the fused backward), so memory stays busy while this
+// row is reduced and written.  After the last row, `next` is the same row
+// again (a cache hit, never used), which keeps the loads unconditional.
+// Returns the row's loss (same in every lane).
+template <int DT, int K, int STRIDE, bool BWD, bool EXACT, class Red>
+__device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&raw)[K],
+                                               const RowRef &cur, const RowRef &next, int lidx,
+                                               int kfull)
+{
+    const Window &w = cur.w;
+    const int64_t t = cur.t;
+    const TargetPos tp = target_pos<DT>(t, p.V, w.head);
+    const float xt = tp.valid ? load_logit<DT>(p, cur.row, t) : __builtin_nanf("");
+    if (!EXACT && !p.aligned)
+        mask_window<DT, K, STRIDE>(raw, lidx, w.nvec, kfull, w.head, p.V);
+
+    float lm = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        lm = vec_max<DT>(raw[k], lm);
     const float m = red.max(lm);
-    const float xt = tp.valid ? red.xt() : __builtin_nanf("");
     const float mL = m * kLog2e;
 
-    opt_barrier<K>(raw);
+    opt_barrier<DT, K>(raw);
     float ls = 0.0f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const float e = vec_sumexp<DT>(raw[k], mL);
-        ls += vec_valid<STRIDE>(k, kfull, lidx, nvec) ? e : 0.0f;
+        ls += vec_valid<STRIDE, EXACT>(k, kfull, lidx, w.nvec) ? e : 0.0f;
+        if constexpr (!BWD) {
+            const int v = lidx + STRIDE * k;
+            raw[k] = next.w.xrow[(EXACT || v < next.w.nvec) ? v : next.w.nvec - 1];
+            // keep each load after the use of the register it refills
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
     const float s = red.sum(ls);
 
     const float et = fast_exp2(__builtin_fmaf(xt, kLog2e, -mL));
     const bool accurate = tp.valid && et > 0.5f * s;
     float s_excl = s - et;
-    if (accurate) {
-        opt_barrier<K>(raw);
-        float lx = 0.0f;
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const float e = (k == kt && is_owner) ? vec_sumexp_skip<DT>(raw[k], mL, tp.jt)
-                                                  : vec_sumexp<DT>(raw[k], mL);
-            lx += vec_valid<STRIDE>(k, kfull, lidx, nvec) ? e : 0.0f;
-        }
-        s_excl = red.sum_excl(lx);
-    }
+    if (accurate)
+        s_excl = red.sum_excl(sum_without_target<DT, K, STRIDE, EXACT>(
+            p, w.xrow, lidx, w.nvec, w.head, mL, tp.vt, tp.jt));
     const RowResult rr = row_result(tp.valid, m, xt, et, s, s_excl, accurate, p.c);
 
     if constexpr (BWD) {
-        opt_barrier<K>(raw);
+        opt_barrier<DT, K>(raw);
         const GradCoef<DT> gc = grad_coef<DT>(m, mL, __log2f(s), p.c, p.log2c);
+        const int kt = tp.valid ? tp.vt / STRIDE : -1;
+        const bool is_owner = tp.valid && lidx == tp.vt % STRIDE;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int v = lidx + STRIDE * k;
-            if (write && vec_valid<STRIDE>(k, kfull, lidx, nvec)) {
-                const Vec g = grad_vec<DT>(raw[k], gc, k == kt && is_owner, tp.jt, rr.gt);
-                store_grad<DT>(xrow, v, g, head, p.V, p.aligned);
+            Vec g = grad_vec<DT>(raw[k], gc, false, 0, 0.0f);
+            if (k == kt) {
+                if (is_owner)
+                    set_elem<DT>(g, tp.jt, rr.gt);
             }
+            if (cur.active && vec_valid<STRIDE, EXACT>(k, kfull, lidx, w.nvec))
+                store_grad<DT>(w.xrow, v, g, w.head, p.V, EXACT || p.aligned);
+            raw[k] = next.w.xrow[(EXACT || v < next.w.nvec) ? v : next.w.nvec - 1];
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     return rr.loss;
@@ -608,56 +731,93 @@ __device__ __forceinline__ void finish_reduction(const Params &p, double wg_sum)
     }
 }
 
-// Window geometry of one row.
-struct Window {
-    Vec *xrow;
-    int head;
-    int nvec;
-};
-
-template <int DT>
-__device__ __forceinline__ Window row_window(const Params &p, int64_t row)
-{
-    constexpr int E = Traits<DT>::E;
-    const int64_t e0 = row * p.V + p.head0;
-    Window w;
-    w.xrow = p.x + (e0 / E);
-    w.head = (int)(e0 % E);
-    w.nvec = (int)((w.head + p.V + E - 1) / E);
-    return w;
-}
+// ================================================================ kernels
 
 // ================================================================ kernels
 
+template <int DT>
+__device__ __forceinline__ RowRef row_ref(const Params &p, int64_t row)
+{
+    RowRef r;
+    r.active = row < p.M;
+    r.row = r.active ? row : 0;   // idle lanes redo row 0, store nothing, drop the loss
+    // The target is read here, a step before it is used and before the row's
+    // own loads: vector loads retire in order, so a late target load would
+    // make the wave wait for every prefetch issued before it.
+    r.t = r.active ? p.targets[r.row] : -1;
+    r.w = row_window<DT>(p, r.row);
+    return r;
+}
+
 // ---- G lanes per row, row in registers ------------------------------------
-template <int DT, int G, int K, bool BWD>
+// NBUF row buffers per lane: with 2, the rows a wave handles alternate between
+// two register sets, so each row's loads are issued a whole row ahead.
+template <int DT, int G, int K, bool BWD, bool EXACT, int NBUF>
 __global__ void __launch_bounds__(256) rows_kernel(Params p)
 {
+    static_assert(NBUF == 1 || NBUF == 2, "NBUF");
     constexpr int E = Traits<DT>::E;
     constexpr int GPW = 64 / G;               // rows per wavefront
     const int lane = threadIdx.x & 63;
     const int lig = lane & (G - 1);
-    const int wave = threadIdx.x >> 6;
+    // wave-uniform, and known to be: keeps the row loop a scalar loop
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nwaves = blockDim.x >> 6;
-    const int64_t wave_id = (int64_t)blockIdx.x * nwaves + wave;
-    const int64_t row_step = (int64_t)gridDim.x * nwaves * GPW;
     const int kfull = (int)((p.V + E - 1) / E) / G;
     double acc = 0.0;
 
-    for (int64_t rb = wave_id * GPW; rb < p.M; rb += row_step) {
-        const int64_t row = rb + lane / G;
-        const bool active = row < p.M;
-        const int64_t r = active ? row : 0;   // idle groups redo row 0 and discard it
-        const Window w = row_window<DT>(p, r);
-        const int64_t t = active ? p.targets[r] : -1;
-        GroupRed<G> red;
-        const float loss = row_in_registers<DT, K, G, BWD>(p, red, w.xrow, lig, w.nvec, kfull,
-                                                           w.head, t, active);
-        if (active && lig == 0) {
+    // Rows of this wave: rb, rb + row_step, ... below row_end.  Interleaved:
+    // the whole grid strides over the rows.  Blocked: each workgroup owns a
+    // contiguous band of rows and walks it front to back.
+    int64_t rb, row_step, row_end;
+    if (p.blocked) {
+        const int64_t per_wg = (int64_t)nwaves * GPW;
+        const int64_t band = (p.M + (int64_t)gridDim.x * per_wg - 1) / ((int64_t)gridDim.x * per_wg) * per_wg;
+        rb = (int64_t)blockIdx.x * band + (int64_t)wave * GPW;
+        row_step = per_wg;
+        row_end = (int64_t)(blockIdx.x + 1) * band < p.M ? (int64_t)(blockIdx.x + 1) * band : p.M;
+    } else {
+        rb = ((int64_t)blockIdx.x * nwaves + wave) * GPW;
+        row_step = (int64_t)gridDim.x * nwaves * GPW;
+        row_end = p.M;
+    }
+    auto record = [&](const RowRef &r, float loss) {
+        if (r.active && lig == 0) {
             if (p.reduction == RED_NONE)
-                p.out[row] = loss;
+                p.out[r.row] = loss;
             else
                 acc += (double)loss;
+        }
+    };
+    // the group's row in the wave's row block `base`, or fallback past the end
+    auto ref_at = [&](int64_t base, const RowRef &fallback) {
+        return base < row_end ? row_ref<DT>(p, base + lane / G) : fallback;
+    };
+    GroupRed<G> red;
+    if (rb < row_end) {
+        RowRef a = row_ref<DT>(p, rb + lane / G);
+        Vec ra[K];
+        issue_loads<DT, K, G, EXACT>(ra, a.w.xrow, lig, a.w.nvec);
+        if constexpr (NBUF == 1) {
+            for (; rb < row_end; rb += row_step) {
+                const RowRef an = ref_at(rb + row_step, a);
+                record(a, pipeline_step<DT, K, G, BWD, EXACT>(p, red, ra, a, an, lig, kfull));
+                a = an;
+            }
+        } else {
+            RowRef b = ref_at(rb + row_step, a);
+            Vec rbuf[K];
+            issue_loads<DT, K, G, EXACT>(rbuf, b.w.xrow, lig, b.w.nvec);
+            for (; rb < row_end; rb += 2 * row_step) {
+                const RowRef an = ref_at(rb + 2 * row_step, a);
+                record(a, pipeline_step<DT, K, G, BWD, EXACT>(p, red, ra, a, an, lig, kfull));
+                if (rb + row_step >= row_end)
+                    break;
+                const RowRef bn = ref_at(rb + 3 * row_step, b);
+                record(b, pipeline_step<DT, K, G, BWD, EXACT>(p, red, rbuf, b, bn, lig, kfull));
+                a = an;
+                b = bn;
+            }
         }
     }
 
@@ -676,31 +836,49 @@ __global__ void __launch_bounds__(256) rows_kernel(Params p)
 }
 
 // ---- one row per workgroup, row in registers --------------------------------
-template <int DT, int W, int K, bool BWD>
+template <int DT, int W, int K, bool BWD, bool EXACT>
 __global__ void __launch_bounds__(W * 64) wg_kernel(Params p)
 {
     constexpr int E = Traits<DT>::E;
     constexpr int NT = W * 64;
-    __shared__ float s_max[W], s_sum[W], s_exc[W], s_xt;
+    __shared__ float s_max[W], s_sum[W], s_exc[W];
     WgRed<W> red;
     red.smax = s_max;
     red.ssum = s_sum;
     red.sexc = s_exc;
-    red.sxt = &s_xt;
     red.wave = threadIdx.x >> 6;
     red.lane = threadIdx.x & 63;
     const int kfull = (int)((p.V + E - 1) / E) / NT;
     double acc = 0.0;
 
-    for (int64_t row = blockIdx.x; row < p.M; row += gridDim.x) {
-        const Window w = row_window<DT>(p, row);
-        const float loss = row_in_registers<DT, K, NT, BWD>(p, red, w.xrow, threadIdx.x, w.nvec,
-                                                            kfull, w.head, p.targets[row], true);
-        if (threadIdx.x == 0) {
-            if (p.reduction == RED_NONE)
-                p.out[row] = loss;
-            else
-                acc += (double)loss;
+    // interleaved (grid stride) or blocked (a contiguous band per workgroup)
+    int64_t row, row_step, row_end;
+    if (p.blocked) {
+        const int64_t band = (p.M + gridDim.x - 1) / gridDim.x;
+        row = (int64_t)blockIdx.x * band;
+        row_step = 1;
+        row_end = row + band < p.M ? row + band : p.M;
+    } else {
+        row = blockIdx.x;
+        row_step = gridDim.x;
+        row_end = p.M;
+    }
+    if (row < row_end) {
+        RowRef cur = row_ref<DT>(p, row);
+        Vec raw[K];
+        issue_loads<DT, K, NT, EXACT>(raw, cur.w.xrow, threadIdx.x, cur.w.nvec);
+        for (; row < row_end; row += row_step) {
+            const bool has_next = row + row_step < row_end;
+            const RowRef next = has_next ? row_ref<DT>(p, row + row_step) : cur;
+            const float loss =
+                pipeline_step<DT, K, NT, BWD, EXACT>(p, red, raw, cur, next, threadIdx.x, kfull);
+            if (threadIdx.x == 0) {
+                if (p.reduction == RED_NONE)
+                    p.out[row] = loss;
+                else
+                    acc += (double)loss;
+            }
+            cur = next;
         }
     }
     if (p.reduction != RED_NONE)

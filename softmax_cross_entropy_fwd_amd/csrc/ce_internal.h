@@ -12,9 +12,12 @@ struct KernelRef {
 
 // (kind, a, b): rows (G lanes per row, K vectors per lane), wg (W waves,
 // K vectors per lane) or stream (W waves, K vectors per lane per chunk).
-KernelRef get_kernel_f32(int kind, int a, int b, bool bwd);
-KernelRef get_kernel_f16(int kind, int a, int b, bool bwd);
-KernelRef get_kernel_bf16(int kind, int a, int b, bool bwd);
+// exact: every row window is exactly the tile (aligned rows of G*K or
+// W*64*K vectors); no stream kernel is exact.  nbuf: row buffers per lane of
+// the rows kernel (1 or 2).
+KernelRef get_kernel_f32(int kind, int a, int b, bool bwd, bool exact, int nbuf);
+KernelRef get_kernel_f16(int kind, int a, int b, bool bwd, bool exact, int nbuf);
+KernelRef get_kernel_bf16(int kind, int a, int b, bool bwd, bool exact, int nbuf);
 
 const void *empty_reduce_fn();
 

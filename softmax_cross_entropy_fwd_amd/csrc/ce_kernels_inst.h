@@ -6,13 +6,15 @@
 namespace cek {
 namespace {
 
-template <int DT, bool BWD>
-KernelRef pick(int kind, int a, int b)
+template <int DT, bool BWD, bool EXACT>
+KernelRef pick(int kind, int a, int b, int nbuf)
 {
-#define CE_ROWS(G, K) \
-    if (a == G && b == K) return KernelRef{(const void *)&rows_kernel<DT, G, K, BWD>, 256};
+#define CE_ROWS(G, K)                                                                           \
+    if (a == G && b == K)                                                                       \
+        return nbuf == 2 ? KernelRef{(const void *)&rows_kernel<DT, G, K, BWD, EXACT, 2>, 256}  \
+                         : KernelRef{(const void *)&rows_kernel<DT, G, K, BWD, EXACT, 1>, 256};
 #define CE_WG(W, K) \
-    if (a == W && b == K) return KernelRef{(const void *)&wg_kernel<DT, W, K, BWD>, W * 64};
+    if (a == W && b == K) return KernelRef{(const void *)&wg_kernel<DT, W, K, BWD, EXACT>, W * 64};
 #define CE_STREAM(W, K) \
     if (a == W && b == K) return KernelRef{(const void *)&stream_kernel<DT, W, K, BWD>, W * 64};
     if (kind == KIND_ROWS) {
@@ -22,8 +24,10 @@ KernelRef pick(int kind, int a, int b)
     } else if (kind == KIND_WG) {
         CE_WG(4, 8) CE_WG(8, 8) CE_WG(8, 12) CE_WG(8, 16) CE_WG(16, 8) CE_WG(16, 12) CE_WG(16, 16)
         CE_WG(4, 16) CE_WG(16, 4)
-    } else if (kind == KIND_STREAM) {
+    } else if (kind == KIND_STREAM && !EXACT) {
         CE_STREAM(4, 8) CE_STREAM(8, 4) CE_STREAM(8, 8) CE_STREAM(16, 4) CE_STREAM(4, 16)
+        CE_STREAM(1, 4) CE_STREAM(2, 4) CE_STREAM(4, 4) CE_STREAM(1, 8) CE_STREAM(2, 8)
+        CE_STREAM(1, 16) CE_STREAM(16, 2) CE_STREAM(16, 1) CE_STREAM(8, 2)
     }
 #undef CE_ROWS
 #undef CE_WG
@@ -33,9 +37,13 @@ KernelRef pick(int kind, int a, int b)
 
 }  // namespace
 
-KernelRef CE_GET_KERNEL(int kind, int a, int b, bool bwd)
+KernelRef CE_GET_KERNEL(int kind, int a, int b, bool bwd, bool exact, int nbuf)
 {
-    return bwd ? pick<CE_DT, true>(kind, a, b) : pick<CE_DT, false>(kind, a, b);
+    if (exact)
+        return bwd ? pick<CE_DT, true, true>(kind, a, b, nbuf)
+                   : pick<CE_DT, false, true>(kind, a, b, nbuf);
+    return bwd ? pick<CE_DT, true, false>(kind, a, b, nbuf)
+               : pick<CE_DT, false, false>(kind, a, b, nbuf);
 }
 
 }  // namespace cek
