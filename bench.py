@@ -58,16 +58,95 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def traffic_path(workload, op, reduction):
+    return os.path.join(ROOT, "profiles", "traffic_%s_%s_%s.txt" % (workload, op, reduction))
+
+
 def load_traffic(workload, op, reduction):
-    """Counter-based HBM bytes per launch from a committed rocprofv3 summary,
-    or None when absent or taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", "traffic_%s_%s_%s.json" % (workload, op, reduction))
+    """Counter-based HBM bytes per launch from a committed rocprofv3 summary
+    (key = value lines), or None when absent or taken on another kernel source."""
+    path = traffic_path(workload, op, reduction)
     if not os.path.exists(path):
         return None
-    d = json.load(open(path))
+    d = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            d[k.strip()] = v.strip()
     if d.get("kernel_source_sha") != kernel_source_hash():
         return None
-    return d.get("hbm_bytes_per_launch")
+    try:
+        return int(float(d["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+COPY_BYTES = 1 << 30
+
+
+def calibrate_copy(log):
+    """A plain device copy of known size (COPY_BYTES read, COPY_BYTES written;
+    the probe library's copy_kernel), run for the counter passes: FETCH_SIZE
+    and WRITE_SIZE of the CE kernel are scaled by what the same counters read
+    for this copy."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "softmax_cross_entropy_fwd_amd", "libce_probe.so"))
+    lib.probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                               ctypes.c_int, ctypes.c_void_p]
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    st = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        rc = lib.probe_copy(dst.data_ptr(), src.data_ptr(), COPY_BYTES, 2048, 4, st)
+        assert rc == 0, rc
+    torch.cuda.synchronize()
+    log("calibration copy: %d bytes read and written, 3 times" % COPY_BYTES)
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def summarize_pmc(fetch_csv, write_csv, workload, op, reduction, kernel_prefix, command):
+    """Turns two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE and
+    WRITE_SIZE, KiB per dispatch) into the traffic summary bench.py reads."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        rows = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            rows.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return rows
+
+    f, w = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+
+    def pick(d, pred):
+        vals = [v for k, vs in d.items() if pred(k) for v in vs]
+        return statistics.median(vals) if vals else None
+
+    ce_kernel = lambda k: kernel_prefix in k
+    is_probe_copy = lambda k: "(anonymous namespace)::copy_kernel<" in k and "native" not in k
+    f_copy = pick(f, is_probe_copy)
+    w_copy = pick(w, is_probe_copy)
+    f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
+    f_ce, w_ce = pick(f, ce_kernel), pick(w, ce_kernel)
+    hbm = f_ce * f_scale + w_ce * w_scale
+    lines = [
+        "# HBM traffic of the %s %s (%s) kernel, from rocprofv3 counters" % (workload, op, reduction),
+        "# command: %s" % command,
+        "kernel = %s" % kernel_prefix,
+        "kernel_source_sha = %s" % kernel_source_hash(),
+        "fetch_size_bytes_per_launch_raw = %.0f" % f_ce,
+        "write_size_bytes_per_launch_raw = %.0f" % w_ce,
+        "copy_fetch_raw = %.0f" % f_copy,
+        "copy_write_raw = %.0f" % w_copy,
+        "fetch_scale = %.4f" % f_scale,
+        "write_scale = %.4f" % w_scale,
+        "hbm_bytes_per_launch = %.0f" % hbm,
+    ]
+    return "\n".join(lines) + "\n"
 
 
 def time_workload(ce, workload, op, reduction, steps, warmup, log):
@@ -170,7 +249,23 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the LM-head lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a 1 GiB device copy first (for counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL"),
+                    help="write the traffic summary from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--pmc-command", default="", help="the profiled command, for the summary")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        from softmax_cross_entropy_fwd_amd import inputs as _inp
+        c = _inp.CONFIGS[args.workload]
+        op = args.op or c["ops"][0]
+        red = args.reduction or c["reductions"][0]
+        text = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, op,
+                             red, args.summarize_pmc[2], args.pmc_command)
+        open(traffic_path(args.workload, op, red), "w").write(text)
+        print(text)
+        return
 
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -194,6 +289,8 @@ def main():
     log("device: %s, torch %s, hip %s" % (torch.cuda.get_device_name(0), torch.__version__,
                                           torch.version.hip))
 
+    if args.calibrate_copy:
+        calibrate_copy(log)
     head = time_workload(ce, args.workload, op, red, args.steps, args.warmup, log)
     also = []
     if not args.no_extra and args.workload == "classifier":
