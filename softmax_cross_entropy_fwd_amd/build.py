@@ -31,9 +31,9 @@ CFLAGS = [
 ]
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + CFLAGS + ["-c", src, "-o", obj]
+def _compile(src, verbose, defines=(), build_dir=None):
+    obj = os.path.join(build_dir or BUILD, os.path.basename(src) + ".o")
+    cmd = [HIPCC] + CFLAGS + ["-D" + d for d in defines] + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -46,18 +46,24 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose=False, jobs=None):
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose=False, jobs=None, defines=(), out=None):
+    """Compile csrc/ into libce.so (or `out`, with extra -D `defines`, for
+    experiments; the probes are only built for the default library)."""
+    build_dir = BUILD if not defines else BUILD + "_" + "_".join(d.replace("=", "") for d in defines)
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 2)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda s: _compile(s, verbose, defines, build_dir), srcs))
+    lib = out or LIB
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+    if out:
+        return out
     # the bandwidth probes the bench measures the ceiling with (own library)
     pobj = _compile(PROBE_SRC, verbose)
     tmp = PROBE_LIB + ".tmp%d" % os.getpid()
@@ -68,4 +74,7 @@ def build(verbose=False, jobs=None):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    args = sys.argv[1:]
+    defs = [a[2:] for a in args if a.startswith("-D")]
+    outs = [a[6:] for a in args if a.startswith("--out=")]
+    print(build(verbose="-v" in args, defines=defs, out=outs[0] if outs else None))

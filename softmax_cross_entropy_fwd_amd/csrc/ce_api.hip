@@ -127,6 +127,8 @@ bool forced_shape(int *kind, int *a, int *b)
         *kind = cek::KIND_WG;
     else if (!std::strcmp(name, "stream"))
         *kind = cek::KIND_STREAM;
+    else if (!std::strcmp(name, "wstream"))
+        *kind = cek::KIND_WSTREAM;
     else
         return false;
     *a = x;
@@ -188,7 +190,8 @@ int make_plan(int64_t M, int64_t V, int dtype, bool bwd, bool aligned, Plan *pla
     int fk, fa, fb;
     if (forced_shape(&fk, &fa, &fb)) {
         const int64_t tile = tile_vectors(fk, fa, fb);
-        if (lookup(dtype, fk, fa, fb, bwd, false, 1).fn && (fk == cek::KIND_STREAM || tile >= nvec)) {
+        if (lookup(dtype, fk, fa, fb, bwd, false, 1).fn &&
+            (fk == cek::KIND_STREAM || fk == cek::KIND_WSTREAM || tile >= nvec)) {
             kind = fk;
             a = fa;
             b = fb;
@@ -201,9 +204,14 @@ int make_plan(int64_t M, int64_t V, int dtype, bool bwd, bool aligned, Plan *pla
     plan->exact = aligned && tile_vectors(kind, a, b) == nvec;
     plan->nbuf = kind == cek::KIND_ROWS ? nbuf : 1;
     const char *nb = std::getenv("CE_FORCE_NBUF");
-    if (kind == cek::KIND_ROWS && nb && (std::atoi(nb) == 1 || std::atoi(nb) == 2))
+    if (kind == cek::KIND_ROWS && nb &&
+        (std::atoi(nb) == 1 || std::atoi(nb) == 2 || std::atoi(nb) == 17 || std::atoi(nb) == 18))
         plan->nbuf = std::atoi(nb);
     plan->k = lookup(dtype, kind, a, b, bwd, plan->exact, plan->nbuf);
+    if (!plan->k.fn && plan->nbuf != nbuf) {   // an override with no such instance
+        plan->nbuf = kind == cek::KIND_ROWS ? nbuf : 1;
+        plan->k = lookup(dtype, kind, a, b, bwd, plan->exact, plan->nbuf);
+    }
     if (!plan->k.fn)
         return CE_ERR_HIP;
     int dev = 0;
@@ -215,13 +223,18 @@ int make_plan(int64_t M, int64_t V, int dtype, bool bwd, bool aligned, Plan *pla
     rc = blocks_per_cu(dev, plan->k, &plan->occupancy);
     if (rc)
         return rc;
-    int64_t rows_per_wg = kind == cek::KIND_ROWS ? (plan->k.block / 64) * (64 / a) : 1;
+    int64_t rows_per_wg = kind == cek::KIND_ROWS      ? (plan->k.block / 64) * (64 / a)
+                          : kind == cek::KIND_WSTREAM ? plan->k.block / 64
+                                                      : 1;
     int64_t needed = (M + rows_per_wg - 1) / rows_per_wg;
     // Few deep waves beat many shallow ones here (measured): each wave keeps
     // a whole row of loads in flight, so the rows kernel runs 4 waves per CU
     // and the workgroup kernels 16.
     const int waves_per_wg = plan->k.block / 64;
-    const int target_waves = kind == cek::KIND_ROWS ? 4 : 16;
+    const char *tw = std::getenv("CE_WAVES_PER_CU");
+    const int target_waves = (tw && std::atoi(tw) > 0) ? std::atoi(tw)
+                             : kind == cek::KIND_ROWS  ? 4
+                                                       : 16;
     int wg_per_cu = target_waves / waves_per_wg;
     if (wg_per_cu < 1)
         wg_per_cu = 1;
@@ -396,7 +409,7 @@ int ce_plan_describe(int64_t M, int64_t V, ce_dtype_t dtype, ce_reduction_t redu
     int rc = make_plan(M, V, (int)dtype, fwd_bwd != 0, aligned, &plan);
     if (rc)
         return rc;
-    static const char *names[] = {"rows", "wg", "stream"};
+    static const char *names[] = {"rows", "wg", "stream", "wstream"};
     std::snprintf(buf, buf_len, "%s:%d:%d%s%s block=%d grid=%lld occupancy=%d cus=%d",
                   names[plan.kind], plan.a, plan.b, plan.exact ? " exact" : "",
                   plan.nbuf == 2 ? " nbuf=2" : "", plan.k.block, (long long)plan.grid,

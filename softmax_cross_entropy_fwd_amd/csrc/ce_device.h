@@ -166,6 +166,39 @@ __device__ __forceinline__ void store_partial(Vec *p, const Vec &v, int lo, int 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Row data is read once and written once: loads and stores can carry the
+// non-temporal (streaming) hint.
+#ifndef CE_NT_LOAD
+#define CE_NT_LOAD 0
+#endif
+#ifndef CE_NT_STORE
+#define CE_NT_STORE 1
+#endif
+
+__device__ __forceinline__ Vec ldv(const Vec *p)
+{
+#if CE_NT_LOAD
+    Vec v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        v.w[i] = __builtin_nontemporal_load(&p->w[i]);
+    return v;
+#else
+    return *p;
+#endif
+}
+
+__device__ __forceinline__ void stv(Vec *p, const Vec &v)
+{
+#if CE_NT_STORE
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        __builtin_nontemporal_store(v.w[i], &p->w[i]);
+#else
+    *p = v;
+#endif
+}
+
 // ------------------------------------------------------- lane reductions
 // DPP within 16-lane rows, a lane swap for 32, and readlane for 64.  Every
 // lane of a G-lane group ends with the same (bitwise) result.
@@ -270,7 +303,7 @@ __device__ __forceinline__ void load_window(Vec (&raw)[K], const Vec *xrow, int 
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int v = lidx + STRIDE * k;
-        raw[k] = xrow[v < nvec ? v : nvec - 1];
+        raw[k] = ldv(&xrow[v < nvec ? v : nvec - 1]);
     }
     if (!aligned) {
         if (lidx == 0 && head > 0)
@@ -449,50 +482,80 @@ __device__ __forceinline__ void store_grad(Vec *xrow, int v, const Vec &g, int h
 {
     constexpr int E = Traits<DT>::E;
     if (aligned) {
-        xrow[v] = g;
+        stv(&xrow[v], g);
         return;
     }
     const int64_t lo = head - (int64_t)v * E;
     const int64_t hi = lo + V;
     if (lo <= 0 && hi >= E)
-        xrow[v] = g;
+        stv(&xrow[v], g);
     else
         store_partial<DT>(xrow + v, g, (int)(lo > 0 ? lo : 0), (int)(hi < E ? hi : E));
 }
 
 // ------------------------------------------- reductions across a row's lanes
 
+// Combining per-lane online pairs (m, s) -- s being a sum of 2^((x - m) log2 e)
+// -- into the row's (M, S): M = max m, S = sum s * 2^((m - M) log2 e).  A lane
+// whose m equals M keeps its s exactly.
+__device__ __forceinline__ float rescale_to(float s, float m, float M)
+{
+    return m == M ? s : s * fast_exp2((m - M) * kLog2e);
+}
+
 // G lanes of one wavefront per row.
 template <int G>
 struct GroupRed {
-    __device__ __forceinline__ float max(float v) { return group_reduce<G>(v, OpMax()); }
-    __device__ __forceinline__ float sum(float v) { return group_reduce<G>(v, OpSum()); }
+    __device__ __forceinline__ void combine(float m, float s, float &M, float &S)
+    {
+        M = group_reduce<G>(m, OpMax());
+        S = group_reduce<G>(rescale_to(s, m, M), OpSum());
+    }
     __device__ __forceinline__ float sum_excl(float v) { return group_reduce<G>(v, OpSum()); }
+    __device__ __forceinline__ void next_row() {}
 };
 
 // W wavefronts of one workgroup per row: DPP within each wavefront, LDS across
-// them, partials added in wavefront order.  Every call is made by the whole
-// workgroup.  Each LDS slot is read before the next barrier and rewritten only
-// after it, so the slots are safely reused row after row.
+// them, partials combined in wavefront order, one barrier per row.  Slots
+// alternate between two banks row by row: a wavefront can run at most one
+// barrier ahead, so it never overwrites a bank another is still reading.
 template <int W>
 struct WgRed {
-    float *smax, *ssum, *sexc;
-    int wave, lane;
-    __device__ __forceinline__ float combine(float v, float *slot, bool is_max)
+    float (*smax)[W];
+    float (*ssum)[W];
+    float (*sexc)[W];
+    int wave, lane, bank;
+    __device__ __forceinline__ void combine(float m, float s, float &M, float &S)
     {
-        v = is_max ? group_reduce<64>(v, OpMax()) : group_reduce<64>(v, OpSum());
-        if (lane == 0)
-            slot[wave] = v;
+        const float mw = group_reduce<64>(m, OpMax());
+        const float sw = group_reduce<64>(rescale_to(s, m, mw), OpSum());
+        if (lane == 0) {
+            smax[bank][wave] = mw;
+            ssum[bank][wave] = sw;
+        }
         __syncthreads();
-        float r = slot[0];
+        M = smax[bank][0];
 #pragma unroll
         for (int w = 1; w < W; ++w)
-            r = is_max ? fmaxf(r, slot[w]) : r + slot[w];
+            M = fmaxf(M, smax[bank][w]);
+        S = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+            S += rescale_to(ssum[bank][w], smax[bank][w], M);
+    }
+    __device__ __forceinline__ float sum_excl(float v)
+    {
+        v = group_reduce<64>(v, OpSum());
+        if (lane == 0)
+            sexc[bank][wave] = v;
+        __syncthreads();
+        float r = sexc[bank][0];
+#pragma unroll
+        for (int w = 1; w < W; ++w)
+            r += sexc[bank][w];
         return r;
     }
-    __device__ __forceinline__ float max(float v) { return combine(v, smax, true); }
-    __device__ __forceinline__ float sum(float v) { return combine(v, ssum, false); }
-    __device__ __forceinline__ float sum_excl(float v) { return combine(v, sexc, false); }
+    __device__ __forceinline__ void next_row() { bank ^= 1; }
 };
 
 // The logit x[row, t] read straight from memory (the row's own lines are being
@@ -522,7 +585,7 @@ __device__ __forceinline__ void issue_loads(Vec (&raw)[K], const Vec *xrow, int 
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int v = lidx + STRIDE * k;
-        raw[k] = xrow[(EXACT || v < nvec) ? v : nvec - 1];
+        raw[k] = ldv(&xrow[(EXACT || v < nvec) ? v : nvec - 1]);
     }
 }
 
@@ -552,22 +615,19 @@ __device__ __forceinline__ bool vec_valid(int k, int kfull, int lidx, int nvec)
 }
 
 // Sum over the row leaving out the target's term, re-read from memory one
-// vector at a time: the rare rows whose target carries more than half of the
-// mass (p_t > 1/2).  Kept serial so it adds no register pressure.
-template <int DT, int K, int STRIDE, bool EXACT>
+// vector at a time (lane lidx takes window vectors lidx, lidx + stride, ...):
+// the rare rows whose target carries more than half of the mass (p_t > 1/2).
+// Kept serial and out of line so it adds no register pressure.
+template <int DT>
 __device__ __attribute__((noinline)) float sum_without_target(const Params &p, const Vec *xrow,
-                                                              int lidx, int nvec, int head,
-                                                              float mL, int vt, int jt)
+                                                              int lidx, int stride, int nvec,
+                                                              int head, float mL, int vt, int jt)
 {
     constexpr int E = Traits<DT>::E;
     float lx = 0.0f;
-#pragma unroll 1
-    for (int k = 0; k < K; ++k) {
-        const int v = lidx + STRIDE * k;
-        if (v >= nvec)
-            break;
+    for (int v = lidx; v < nvec; v += stride) {
         Vec r = xrow[v];
-        if (!EXACT && !p.aligned) {
+        if (!p.aligned) {
             if (v == 0 && head > 0)
                 mask_outside<DT>(r, head, E);
             if (v == nvec - 1)
@@ -638,41 +698,55 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
                                                const RowRef &cur, const RowRef &next, int lidx,
                                                int kfull)
 {
+    constexpr int E = Traits<DT>::E;
     const Window &w = cur.w;
-    const int64_t t = cur.t;
-    const TargetPos tp = target_pos<DT>(t, p.V, w.head);
-    const float xt = tp.valid ? load_logit<DT>(p, cur.row, t) : __builtin_nanf("");
-    if (!EXACT && !p.aligned)
-        mask_window<DT, K, STRIDE>(raw, lidx, w.nvec, kfull, w.head, p.V);
+    const TargetPos tp = target_pos<DT>(cur.t, p.V, w.head);
+    const float xt = tp.valid ? load_logit<DT>(p, cur.row, cur.t) : __builtin_nanf("");
+    const bool masked = !EXACT && !p.aligned;
 
-    float lm = -__builtin_inff();
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-        lm = vec_max<DT>(raw[k], lm);
-    const float m = red.max(lm);
-    const float mL = m * kLog2e;
-
-    opt_barrier<DT, K>(raw);
-    float ls = 0.0f;
+    // One pass: each vector is folded into the lane's running (max, sum) as
+    // it arrives -- the sum is rescaled by 2^((m_old - m_new) log2 e) when the
+    // max grows -- and (forward) its registers are refilled at once with the
+    // next row's vector.
+    float m_run = -__builtin_inff();
+    float s_run = 0.0f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const float e = vec_sumexp<DT>(raw[k], mL);
-        ls += vec_valid<STRIDE, EXACT>(k, kfull, lidx, w.nvec) ? e : 0.0f;
+        const int v = lidx + STRIDE * k;
+        Vec x = raw[k];
+        if (masked) {
+            if (k == 0 && lidx == 0 && w.head > 0)
+                mask_outside<DT>(x, w.head, E);
+            if (k + 1 >= kfull && v >= w.nvec - 1)
+                mask_outside<DT>(x, 0, (int)(w.head + p.V - (int64_t)(w.nvec - 1) * E));
+        }
+        if constexpr (BWD) {
+            if (masked)
+                raw[k] = x;
+        }
+        const bool valid = vec_valid<STRIDE, EXACT>(k, kfull, lidx, w.nvec);
+        const float mn = vec_max<DT>(x, m_run);
+        const float mnL = mn == -__builtin_inff() ? 0.0f : mn * kLog2e;
+        const float add = vec_sumexp<DT>(x, mnL);
+        const float s_new = __builtin_fmaf(rescale_to(s_run, m_run, mn), 1.0f, add);
+        s_run = valid ? s_new : s_run;
+        m_run = valid ? mn : m_run;
         if constexpr (!BWD) {
-            const int v = lidx + STRIDE * k;
-            raw[k] = next.w.xrow[(EXACT || v < next.w.nvec) ? v : next.w.nvec - 1];
+            raw[k] = ldv(&next.w.xrow[(EXACT || v < next.w.nvec) ? v : next.w.nvec - 1]);
             // keep each load after the use of the register it refills
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    const float s = red.sum(ls);
+    float m, s;
+    red.combine(m_run, s_run, m, s);
+    const float mL = m * kLog2e;
 
     const float et = fast_exp2(__builtin_fmaf(xt, kLog2e, -mL));
     const bool accurate = tp.valid && et > 0.5f * s;
     float s_excl = s - et;
     if (accurate)
-        s_excl = red.sum_excl(sum_without_target<DT, K, STRIDE, EXACT>(
-            p, w.xrow, lidx, w.nvec, w.head, mL, tp.vt, tp.jt));
+        s_excl = red.sum_excl(sum_without_target<DT>(p, w.xrow, lidx, STRIDE, w.nvec, w.head,
+                                                     mL, tp.vt, tp.jt));
     const RowResult rr = row_result(tp.valid, m, xt, et, s, s_excl, accurate, p.c);
 
     if constexpr (BWD) {
@@ -690,10 +764,11 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
             }
             if (cur.active && vec_valid<STRIDE, EXACT>(k, kfull, lidx, w.nvec))
                 store_grad<DT>(w.xrow, v, g, w.head, p.V, EXACT || p.aligned);
-            raw[k] = next.w.xrow[(EXACT || v < next.w.nvec) ? v : next.w.nvec - 1];
+            raw[k] = ldv(&next.w.xrow[(EXACT || v < next.w.nvec) ? v : next.w.nvec - 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    red.next_row();
     return rr.loss;
 }
 
@@ -752,8 +827,8 @@ __device__ __forceinline__ RowRef row_ref(const Params &p, int64_t row)
 // ---- G lanes per row, row in registers ------------------------------------
 // NBUF row buffers per lane: with 2, the rows a wave handles alternate between
 // two register sets, so each row's loads are issued a whole row ahead.
-template <int DT, int G, int K, bool BWD, bool EXACT, int NBUF>
-__global__ void __launch_bounds__(256) rows_kernel(Params p)
+template <int DT, int G, int K, bool BWD, bool EXACT, int NBUF, int NW = 4>
+__global__ void __launch_bounds__(NW * 64) rows_kernel(Params p)
 {
     static_assert(NBUF == 1 || NBUF == 2, "NBUF");
     constexpr int E = Traits<DT>::E;
@@ -823,7 +898,7 @@ __global__ void __launch_bounds__(256) rows_kernel(Params p)
 
     if (p.reduction == RED_NONE)
         return;
-    __shared__ double s_grp[256 / G];
+    __shared__ double s_grp[NW * 64 / G];
     if (lig == 0)
         s_grp[threadIdx.x / G] = acc;
     __syncthreads();
@@ -841,13 +916,14 @@ __global__ void __launch_bounds__(W * 64) wg_kernel(Params p)
 {
     constexpr int E = Traits<DT>::E;
     constexpr int NT = W * 64;
-    __shared__ float s_max[W], s_sum[W], s_exc[W];
+    __shared__ float s_max[2][W], s_sum[2][W], s_exc[2][W];
     WgRed<W> red;
     red.smax = s_max;
     red.ssum = s_sum;
     red.sexc = s_exc;
     red.wave = threadIdx.x >> 6;
     red.lane = threadIdx.x & 63;
+    red.bank = 0;
     const int kfull = (int)((p.V + E - 1) / E) / NT;
     double acc = 0.0;
 
@@ -883,6 +959,88 @@ __global__ void __launch_bounds__(W * 64) wg_kernel(Params p)
     }
     if (p.reduction != RED_NONE)
         finish_reduction(p, acc);
+}
+
+// ---- one row per wavefront, streamed in chunks ------------------------------
+// Every wavefront walks its own rows (grid stride over wavefronts); a row is
+// read in chunks of 64*K vectors folded into per-lane online (max, sum)
+// pairs, then combined with DPP.  No LDS and no barriers: many wavefronts per
+// CU keep memory busy.  Forward only.
+template <int DT, int K>
+__global__ void __launch_bounds__(256) wstream_kernel(Params p)
+{
+    constexpr int E = Traits<DT>::E;
+    constexpr int CH = 64 * K;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nwaves = blockDim.x >> 6;
+    const int64_t step = (int64_t)gridDim.x * nwaves;
+    GroupRed<64> red;
+    double acc = 0.0;
+
+    for (int64_t row = (int64_t)blockIdx.x * nwaves + wave; row < p.M; row += step) {
+        const Window w = row_window<DT>(p, row);
+        const int64_t t = p.targets[row];
+        const TargetPos tp = target_pos<DT>(t, p.V, w.head);
+        const float xt = tp.valid ? load_logit<DT>(p, row, t) : __builtin_nanf("");
+        float m_run = -__builtin_inff();
+        float s_run = 0.0f;
+        for (int cb = 0; cb < w.nvec; cb += CH) {
+            const int n = w.nvec - cb;          // window vectors from this chunk on
+            const Vec *xc = w.xrow + cb;
+            Vec raw[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int v = lane + 64 * k;
+                raw[k] = ldv(&xc[v < n ? v : n - 1]);
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int v = lane + 64 * k;
+                Vec x = raw[k];
+                if (!p.aligned) {
+                    if (cb == 0 && v == 0 && w.head > 0)
+                        mask_outside<DT>(x, w.head, E);
+                    if (v >= n - 1)
+                        mask_outside<DT>(x, 0, (int)(w.head + p.V - (int64_t)(w.nvec - 1) * E));
+                }
+                const bool valid = v < n;
+                const float mn = vec_max<DT>(x, m_run);
+                const float mnL = mn == -__builtin_inff() ? 0.0f : mn * kLog2e;
+                const float add = vec_sumexp<DT>(x, mnL);
+                const float s_new = rescale_to(s_run, m_run, mn) + add;
+                s_run = valid ? s_new : s_run;
+                m_run = valid ? mn : m_run;
+            }
+        }
+        float m, s;
+        red.combine(m_run, s_run, m, s);
+        const float mL = m * kLog2e;
+        const float et = fast_exp2(__builtin_fmaf(xt, kLog2e, -mL));
+        const bool accurate = tp.valid && et > 0.5f * s;
+        float s_excl = s - et;
+        if (accurate)
+            s_excl = red.sum_excl(sum_without_target<DT>(p, w.xrow, lane, 64, w.nvec, w.head, mL,
+                                                         tp.vt, tp.jt));
+        const RowResult rr = row_result(tp.valid, m, xt, et, s, s_excl, accurate, p.c);
+        if (lane == 0) {
+            if (p.reduction == RED_NONE)
+                p.out[row] = rr.loss;
+            else
+                acc += (double)rr.loss;
+        }
+    }
+    if (p.reduction == RED_NONE)
+        return;
+    __shared__ double s_wave[4];
+    if (lane == 0)
+        s_wave[wave] = acc;
+    __syncthreads();
+    double wg_sum = 0.0;
+    if (threadIdx.x == 0)
+        for (int i = 0; i < nwaves; ++i)
+            wg_sum += s_wave[i];
+    finish_reduction(p, wg_sum);
 }
 
 // ---- one row per workgroup, streamed in chunks ---------------------------------
@@ -1000,7 +1158,7 @@ __global__ void __launch_bounds__(W * 64) stream_kernel(Params p)
                 for (int k = 0; k < K; ++k) {
                     const int v = cb + tid + NT * k;
                     if (v < w.nvec)
-                        raw[k] = w.xrow[v];
+                        raw[k] = ldv(&w.xrow[v]);
                 }
 #pragma unroll
                 for (int k = 0; k < K; ++k) {

@@ -3,7 +3,7 @@
 
 namespace cek {
 
-enum Kind : int { KIND_ROWS = 0, KIND_WG = 1, KIND_STREAM = 2 };
+enum Kind : int { KIND_ROWS = 0, KIND_WG = 1, KIND_STREAM = 2, KIND_WSTREAM = 3 };
 
 struct KernelRef {
     const void *fn;   // host stub of a __global__ instance, or nullptr
@@ -11,7 +11,8 @@ struct KernelRef {
 };
 
 // (kind, a, b): rows (G lanes per row, K vectors per lane), wg (W waves,
-// K vectors per lane) or stream (W waves, K vectors per lane per chunk).
+// K vectors per lane), stream (W waves, K vectors per lane per chunk) or
+// wstream (a = 1 wave per row, K vectors per lane per chunk; forward only).
 // exact: every row window is exactly the tile (aligned rows of G*K or
 // W*64*K vectors); no stream kernel is exact.  nbuf: row buffers per lane of
 // the rows kernel (1 or 2).

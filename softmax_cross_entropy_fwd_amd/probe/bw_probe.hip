@@ -12,9 +12,9 @@ struct alignas(16) V4 {
     uint32_t w[4];
 };
 
-template <int U>
-__global__ void __launch_bounds__(256) read_kernel(const V4 *__restrict__ src, int64_t nvec,
-                                                   float *__restrict__ out)
+template <int U, int NT>
+__global__ void __launch_bounds__(NT) read_kernel(const V4 *__restrict__ src, int64_t nvec,
+                                                  float *__restrict__ out)
 {
     float acc = 0.0f;
     const int64_t step = (int64_t)gridDim.x * blockDim.x * U;
@@ -30,7 +30,7 @@ __global__ void __launch_bounds__(256) read_kernel(const V4 *__restrict__ src, i
         for (int u = 0; u < U; ++u)
             acc += __uint_as_float(r[u].w[0] ^ r[u].w[1] ^ r[u].w[2] ^ r[u].w[3]) * 0.0f + 1.0f;
     }
-    __shared__ float s[256];
+    __shared__ float s[NT];
     s[threadIdx.x] = acc;
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -64,28 +64,61 @@ __global__ void __launch_bounds__(256) copy_kernel(V4 *__restrict__ dst, const V
     }
 }
 
+// The copy with non-temporal loads and stores (streaming hint).
+template <int U>
+__global__ void __launch_bounds__(256) copy_nt_kernel(V4 *__restrict__ dst,
+                                                      const V4 *__restrict__ src, int64_t nvec)
+{
+    const int64_t step = (int64_t)gridDim.x * blockDim.x * U;
+    for (int64_t base = (int64_t)blockIdx.x * blockDim.x * U + threadIdx.x; base < nvec;
+         base += step) {
+        V4 r[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + (int64_t)u * blockDim.x;
+            if (i < nvec) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    r[u].w[j] = __builtin_nontemporal_load(&src[i].w[j]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + (int64_t)u * blockDim.x;
+            if (i < nvec) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    __builtin_nontemporal_store(r[u].w[j], &dst[i].w[j]);
+            }
+        }
+    }
+}
+
 }  // namespace
 
 extern "C" {
 
-// Read `bytes` (a multiple of 16) from src; out needs `grid` floats.
-int probe_read(const void *src, int64_t bytes, int grid, int unroll, float *out, void *stream)
+// Read `bytes` (a multiple of 16) from src with `block` (256 or 1024) threads
+// per workgroup; out needs `grid` floats.
+int probe_read(const void *src, int64_t bytes, int grid, int unroll, int block, float *out,
+               void *stream)
 {
     const int64_t nvec = bytes / 16;
-    if (!src || !out || nvec < 1 || grid < 1)
+    if (!src || !out || nvec < 1 || grid < 1 || (block != 256 && block != 1024))
         return -1;
     hipStream_t s = (hipStream_t)stream;
     const V4 *p = (const V4 *)src;
-    switch (unroll) {
-    case 1: hipLaunchKernelGGL(read_kernel<1>, dim3(grid), dim3(256), 0, s, p, nvec, out); break;
-    case 4: hipLaunchKernelGGL(read_kernel<4>, dim3(grid), dim3(256), 0, s, p, nvec, out); break;
-    case 8: hipLaunchKernelGGL(read_kernel<8>, dim3(grid), dim3(256), 0, s, p, nvec, out); break;
-    case 16: hipLaunchKernelGGL(read_kernel<16>, dim3(grid), dim3(256), 0, s, p, nvec, out); break;
-    default: return -1;
-    }
-    return hipGetLastError() == hipSuccess ? 0 : -6;
+#define PROBE_READ(U, NT) \
+    if (unroll == U && block == NT) { \
+        hipLaunchKernelGGL((read_kernel<U, NT>), dim3(grid), dim3(NT), 0, s, p, nvec, out); \
+        return hipGetLastError() == hipSuccess ? 0 : -6; }
+    PROBE_READ(1, 256) PROBE_READ(4, 256) PROBE_READ(8, 256) PROBE_READ(16, 256)
+    PROBE_READ(1, 1024) PROBE_READ(2, 1024) PROBE_READ(4, 1024) PROBE_READ(8, 1024)
+#undef PROBE_READ
+    return -1;
 }
 
+// unroll 1, 4, 8: plain copy; 101, 102, 104: non-temporal copy unrolled 1, 2, 4.
 int probe_copy(void *dst, const void *src, int64_t bytes, int grid, int unroll, void *stream)
 {
     const int64_t nvec = bytes / 16;
@@ -96,6 +129,9 @@ int probe_copy(void *dst, const void *src, int64_t bytes, int grid, int unroll, 
     case 1: hipLaunchKernelGGL(copy_kernel<1>, dim3(grid), dim3(256), 0, s, (V4 *)dst, (const V4 *)src, nvec); break;
     case 4: hipLaunchKernelGGL(copy_kernel<4>, dim3(grid), dim3(256), 0, s, (V4 *)dst, (const V4 *)src, nvec); break;
     case 8: hipLaunchKernelGGL(copy_kernel<8>, dim3(grid), dim3(256), 0, s, (V4 *)dst, (const V4 *)src, nvec); break;
+    case 104: hipLaunchKernelGGL(copy_nt_kernel<4>, dim3(grid), dim3(256), 0, s, (V4 *)dst, (const V4 *)src, nvec); break;
+    case 102: hipLaunchKernelGGL(copy_nt_kernel<2>, dim3(grid), dim3(256), 0, s, (V4 *)dst, (const V4 *)src, nvec); break;
+    case 101: hipLaunchKernelGGL(copy_nt_kernel<1>, dim3(grid), dim3(256), 0, s, (V4 *)dst, (const V4 *)src, nvec); break;
     default: return -1;
     }
     return hipGetLastError() == hipSuccess ? 0 : -6;

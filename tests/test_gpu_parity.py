@@ -136,10 +136,15 @@ def test_alignment_sweep(ce, dtype):
 
 SHAPES = ["rows:1:1", "rows:1:2", "rows:1:4", "rows:2:4", "rows:4:4", "rows:8:4", "rows:16:4",
           "rows:32:4", "rows:64:4", "rows:64:8", "rows:64:16", "rows:4:8", "rows:8:2",
-          "rows:16:2", "rows:32:1", "rows:32:8", "rows:32:16",
+          "rows:16:2", "rows:32:1", "rows:32:8", "rows:32:16", "rows:32:32", "rows:2:16",
           "wg:4:8", "wg:8:8", "wg:8:12", "wg:8:16", "wg:16:8", "wg:16:12", "wg:16:16",
           "wg:4:16", "wg:16:4", "stream:4:8", "stream:8:4", "stream:8:8", "stream:16:4",
-          "stream:4:16"]
+          "stream:4:16", "stream:1:4", "stream:2:4", "stream:4:4", "stream:1:8", "stream:2:8",
+          "stream:1:16", "stream:16:2", "stream:16:1", "stream:8:2",
+          "wstream:1:2", "wstream:1:4", "wstream:1:8"]
+# row buffers of the rows kernel: 1 or 2 with 4-wave workgroups, 17 or 18 with
+# 16-wave workgroups (64:16 and 4:8 only)
+NBUFS = {"rows:64:16": ("1", "2", "17", "18"), "rows:4:8": ("1", "2", "17", "18")}
 
 
 @pytest.mark.parametrize("shape", SHAPES)
@@ -148,6 +153,12 @@ def test_every_kernel_shape(ce, shape, monkeypatch):
     a, b = int(a), int(b)
     cap = a * b if kind == "rows" else (a * 64 * b if kind == "wg" else 1 << 30)
     monkeypatch.setenv("CE_FORCE_PLAN", shape)
+    for nbuf in NBUFS.get(shape, ("1", "2") if kind == "rows" else ("1",)):
+        monkeypatch.setenv("CE_FORCE_NBUF", nbuf)
+        _check_shape(ce, shape, kind, cap)
+
+
+def _check_shape(ce, shape, kind, cap):
     for dtype in DTYPES:
         E = 4 if dtype == "f32" else 8
         for V in (1, 5, 13 * E + 3, 64 * E, 64 * E + 1, 3000, 20000):
@@ -160,6 +171,7 @@ def test_every_kernel_shape(ce, shape, monkeypatch):
             run_and_check(ce, dtype, M, V, 4.0, seed=V, reduction="none", offset=V % 3)
             run_and_check(ce, dtype, M, V, 4.0, seed=V + 5, reduction="mean", op="fwd_bwd",
                           offset=(V // 2) % 2)
+            run_and_check(ce, dtype, M, V, 4.0, seed=V + 9, reduction="sum", offset=0)
 
 
 # ------------------------------------------------------------------ edge cases
