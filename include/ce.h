@@ -61,15 +61,16 @@ enum {
     CE_ERR_REDUCTION = -4,   /* reduction is not a ce_reduction_t */
     CE_ERR_WORKSPACE = -5,   /* workspace NULL, too small or not 8-byte aligned */
     CE_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed */
-    CE_ERR_ALIGNMENT = -7,   /* logits not aligned to its element size */
-    CE_ERR_ALIAS = -8        /* in-place logits overlap targets, output or workspace */
+    CE_ERR_ALIGNMENT = -7,   /* a pointer not aligned to its element size, or an
+                                output not at the logits' address modulo 16 */
+    CE_ERR_ALIAS = -8        /* an output overlaps another output or an input */
 };
 
 /* Largest supported row length (classes per row). */
 #define CE_MAX_V 2147483647LL
 
 /*
- * Bytes of device workspace ce_fwd / ce_fwd_bwd_inplace need for these
+ * Bytes of device workspace ce_fwd / ce_fwd_lse / ce_fwd_bwd_inplace need for these
  * arguments: 0 for CE_NONE and for M == 0, otherwise a fixed 33 KiB
  * (a ticket word and up to 4096 fp64 partial sums).
  *
@@ -89,11 +90,29 @@ size_t ce_workspace_bytes(int64_t M, int64_t V, ce_dtype_t dtype,
  *            M == 0 writes NaN (mean) or 0 (sum) and nothing for none.
  *   workspace, workspace_bytes: see ce_workspace_bytes (NULL, 0 for none).
  *   stream   hipStream_t the work is queued on.
+ * out and the workspace must not overlap logits or targets (CE_ERR_ALIAS).
  * Returns CE_OK or a CE_ERR_* code.
  */
 int ce_fwd(const void *logits, const int64_t *targets, int64_t M, int64_t V,
            ce_dtype_t dtype, ce_reduction_t reduction, float *out,
            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Forward that also saves each row's log-sum-exp, for a later ce_bwd:
+ * the loss exactly as ce_fwd (same kernels, same bits) and
+ *   lse      [M] fp32, lse_i = max_j x_ij + log sum_j exp(x_ij - max_j x_ij).
+ * Keeping this one statistic per row (4 bytes) is what lets a later backward
+ * be a single streaming pass that writes the gradient to a buffer of its own:
+ * the unfused alternative that "9 Triton kernels in 9 weeks", week 7,
+ * contrasts with its in-place fused kernel (there the separate [N, V]
+ * gradient tensor is what the fused kernel saves).
+ * lse must not overlap any other argument (CE_ERR_ALIAS); NULL is
+ * CE_ERR_NULL for M > 0.
+ */
+int ce_fwd_lse(const void *logits, const int64_t *targets, int64_t M,
+               int64_t V, ce_dtype_t dtype, ce_reduction_t reduction,
+               float *out, float *lse, void *workspace,
+               size_t workspace_bytes, void *stream);
 
 /*
  * Fused forward + backward in place: computes the loss exactly as ce_fwd
@@ -106,16 +125,64 @@ int ce_fwd_bwd_inplace(void *logits, const int64_t *targets, int64_t M,
                        float *loss_out, void *workspace,
                        size_t workspace_bytes, void *stream);
 
+/*
+ * Backward from a saved log-sum-exp (the split form of the week-7 gradient):
+ *   grad_ij = d_i * c * (exp(x_ij - lse_i) - [j == t_i])
+ * with c = 1/M for CE_MEAN and 1 otherwise, and d the upstream gradient of
+ * the loss: dloss[i] for CE_NONE (one per row loss), dloss[0] for CE_MEAN and
+ * CE_SUM (the scalar), or 1 when dloss is NULL.  reduction only selects c and
+ * the shape of dloss; no loss is computed and no workspace is used.
+ *   logits   [M, V] of dtype, read.
+ *   lse      [M] fp32, as written by ce_fwd_lse for the same logits.
+ *   grad     [M, V] of dtype, written; it must have the same address modulo
+ *            16 bytes as logits (CE_ERR_ALIGNMENT).  grad == logits
+ *            overwrites the logits; any other overlap with an argument is
+ *            CE_ERR_ALIAS.
+ * A row whose target is outside [0, V) gets d_i c softmax(x_i), with no
+ * one-hot term.  Where p_t > 1/2, 1 - p_t is summed from the other terms of
+ * the row (one extra read of that row) so the target's gradient keeps its
+ * relative accuracy.
+ */
+int ce_bwd(const void *logits, const int64_t *targets, const float *lse,
+           const float *dloss, int64_t M, int64_t V, ce_dtype_t dtype,
+           ce_reduction_t reduction, void *grad, void *stream);
+
+/*
+ * Row softmax or log-softmax in one pass over the row: the fused softmax of
+ * "9 Triton kernels in 9 weeks", week 1 (the three memory passes of an
+ * unfused softmax folded into one), and the log_softmax that the problem
+ * statement of the POPCORNBENCH "Kimi-K2.6 l1_p95" trace applies before the
+ * negative log-likelihood:
+ *   out_ij = exp(x_ij - lse_i)   (log_softmax == 0)
+ *   out_ij = x_ij - lse_i        (log_softmax != 0)
+ * in the logits' dtype, rounded to nearest even.  out has the same
+ * alignment rule and may be logits (in place), as grad of ce_bwd.
+ *   lse      optional [M] fp32 row log-sum-exps (NULL: not written).
+ * A row that is entirely -inf gives NaN.
+ */
+int ce_softmax(const void *logits, int64_t M, int64_t V, ce_dtype_t dtype,
+               int log_softmax, void *out, float *lse, void *stream);
+
 /* A static, human-readable name for a status code. */
 const char *ce_status_string(int status);
 
+/* Operations ce_plan_describe can describe. */
+enum {
+    CE_OP_FWD = 0,         /* ce_fwd, ce_fwd_lse */
+    CE_OP_FWD_BWD = 1,     /* ce_fwd_bwd_inplace */
+    CE_OP_SOFTMAX = 2,     /* ce_softmax, log_softmax == 0 */
+    CE_OP_LOG_SOFTMAX = 3, /* ce_softmax, log_softmax != 0 */
+    CE_OP_BWD = 4          /* ce_bwd */
+};
+
 /*
- * Describes the launch plan a call with these arguments would use on the
- * current device (kernel mapping, tile, grid) into buf, NUL-terminated.
- * fwd_bwd selects the in-place variant.  Returns CE_OK or an error code.
+ * Describes the launch plan a call of operation op (CE_OP_*) with these
+ * arguments would use on the current device (kernel mapping, tile, grid)
+ * into buf, NUL-terminated, for a 16-byte aligned logits pointer.  Returns
+ * CE_OK or an error code (an unknown op is CE_ERR_SHAPE).
  */
 int ce_plan_describe(int64_t M, int64_t V, ce_dtype_t dtype,
-                     ce_reduction_t reduction, int fwd_bwd, char *buf,
+                     ce_reduction_t reduction, int op, char *buf,
                      size_t buf_len);
 
 #ifdef __cplusplus

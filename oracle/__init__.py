@@ -13,7 +13,8 @@ of the pages it follows, is documented in ``ce_oracle.c``:
   performance issue", loss_kernel's output line);
 * mean / sum over rows (same trace: mean reduction of ``F.cross_entropy``);
 * gradient (softmax - onehot) * c written in the storage type ("9 Triton
-  kernels in 9 weeks", week 7).
+  kernels in 9 weeks", week 7), optionally times a per-row upstream gradient;
+* row softmax and log-softmax (same page, week 1; the trace's log_softmax).
 
 Storage types are passed as raw bits: float32 arrays for fp32, uint16 arrays of
 the bit patterns for fp16 and bf16.
@@ -66,8 +67,10 @@ def _load():
     lib.oracle_ce_fwd.argtypes = [vp, i32, _i64p, i64, i64, i32, _dp, _dp]
     lib.oracle_ce_fwd.restype = i32
     lib.oracle_ce_grad_rows.argtypes = [vp, i32, _i64p, i64, i64, i64, i64,
-                                        ctypes.c_double, i32, vp, _dp]
+                                        ctypes.c_double, _dp, i32, vp, _dp]
     lib.oracle_ce_grad_rows.restype = i32
+    lib.oracle_softmax_rows.argtypes = [vp, i32, i64, i64, i64, i64, i32, i32, vp, _dp, _dp]
+    lib.oracle_softmax_rows.restype = i32
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i32
     _lib = lib
@@ -143,8 +146,9 @@ def fwd(x, targets, dtype="f32", reduction="mean"):
 
 
 def grad_rows(x, targets, dtype="f32", c=1.0, row0=0, nrows=None, out_dtype=None,
-              want64=False):
-    """Gradient rows [row0, row0 + nrows) scaled by c.
+              want64=False, d=None):
+    """Gradient rows [row0, row0 + nrows) scaled by c (and by d[i], the
+    upstream gradient of row i's loss, when d is given: [M] values).
 
     Returns the gradient rounded once to the storage type (float32 array, or
     uint16 bit patterns for fp16/bf16), and also the fp64 values if want64.
@@ -158,12 +162,43 @@ def grad_rows(x, targets, dtype="f32", c=1.0, row0=0, nrows=None, out_dtype=None
     ocode = code if out_dtype is None else dtype_code(out_dtype)
     g = np.empty((nrows, V), dtype=np.float32 if ocode == F32 else np.uint16)
     g64 = np.empty((nrows, V), dtype=np.float64) if want64 else None
+    if d is not None:
+        d = np.ascontiguousarray(d, dtype=np.float64)
+        if d.shape != (M,):
+            raise ValueError("d must hold one upstream gradient per row")
     rc = lib.oracle_ce_grad_rows(x.ctypes.data, code, t.ctypes.data_as(_i64p), M, V,
-                                 row0, nrows, float(c), ocode, g.ctypes.data,
-                                 g64.ctypes.data_as(_dp) if want64 else None)
+                                 row0, nrows, float(c),
+                                 d.ctypes.data_as(_dp) if d is not None else None, ocode,
+                                 g.ctypes.data, g64.ctypes.data_as(_dp) if want64 else None)
     if rc:
         raise ValueError("oracle_ce_grad_rows: bad arguments")
     return (g, g64) if want64 else g
+
+
+def softmax_rows(x, dtype="f32", log=False, row0=0, nrows=None, out_dtype=None,
+                 want64=False, with_lse=False):
+    """Row softmax (or log-softmax) of rows [row0, row0 + nrows), rounded once
+    to the storage type; optionally also the fp64 values and the fp64 lse."""
+    lib = _load()
+    x, code = _prep(x, dtype)
+    M, V = x.shape
+    if nrows is None:
+        nrows = M - row0
+    ocode = code if out_dtype is None else dtype_code(out_dtype)
+    y = np.empty((nrows, V), dtype=np.float32 if ocode == F32 else np.uint16)
+    y64 = np.empty((nrows, V), dtype=np.float64) if want64 else None
+    lse = np.empty(nrows, dtype=np.float64)
+    rc = lib.oracle_softmax_rows(x.ctypes.data, code, M, V, row0, nrows, int(bool(log)), ocode,
+                                 y.ctypes.data, y64.ctypes.data_as(_dp) if want64 else None,
+                                 lse.ctypes.data_as(_dp))
+    if rc:
+        raise ValueError("oracle_softmax_rows: bad arguments")
+    res = (y,)
+    if want64:
+        res += (y64,)
+    if with_lse:
+        res += (lse,)
+    return res[0] if len(res) == 1 else res
 
 
 def widen(bits, dtype):

@@ -20,7 +20,11 @@
  *  - The gradient of the reduced loss with respect to the logits,
  *    (softmax(x_i) - onehot(t_i)) * c  with c = 1/M for the mean and 1 for the
  *    sum or per-row losses: "9 Triton kernels in 9 weeks", week 7 (fused
- *    forward and backward that writes the gradient over the logits buffer).
+ *    forward and backward that writes the gradient over the logits buffer),
+ *    optionally times an upstream gradient per row (chain rule).
+ *  - Row softmax exp(x_ij - lse_i) and log-softmax x_ij - lse_i: same page,
+ *    week 1 (fused softmax), and the log_softmax step of the trace's problem
+ *    statement.
  *
  * Readings taken where the pages are silent (each is listed in the design
  * notes of the repository):
@@ -284,18 +288,30 @@ int oracle_ce_fwd(const void *x, int dtype, const int64_t *targets, int64_t M,
     return 0;
 }
 
+static void store_rounded(void *out, int out_dtype, size_t o, double v)
+{
+    if (out_dtype == OR_F32)
+        ((float *)out)[o] = oracle_round_f32(v);
+    else if (out_dtype == OR_F16)
+        ((uint16_t *)out)[o] = oracle_round_f16(v);
+    else
+        ((uint16_t *)out)[o] = oracle_round_bf16(v);
+}
+
 /*
- * Gradient of rows [row0, row0 + nrows) with scale c:
- *   g_ij = exp(x_ij - lse_i) * c          for j != t_i,
- *   g_it = expm1(-loss_i) * c             (= (p_t - 1) c).
+ * Gradient of rows [row0, row0 + nrows) with scale c (times d[i] when the
+ * upstream gradients d are given, one per row of the whole matrix: by the
+ * chain rule the gradient of sum_i d_i loss_i is d_i times that of loss_i):
+ *   g_ij = exp(x_ij - lse_i) * c d_i      for j != t_i,
+ *   g_it = expm1(-loss_i) * c d_i         (= (p_t - 1) c d_i).
  * A target outside [0, V) leaves out the one-hot term.  Results go to
  * grad64 (fp64, may be NULL) and to grad_out in out_dtype rounded once from
  * fp64 (may be NULL).  Both are indexed from row row0.
  */
 int oracle_ce_grad_rows(const void *x, int dtype, const int64_t *targets,
                         int64_t M, int64_t V, int64_t row0, int64_t nrows,
-                        double c, int out_dtype, void *grad_out,
-                        double *grad64)
+                        double c, const double *d, int out_dtype,
+                        void *grad_out, double *grad64)
 {
     if (!x || !targets || V < 1 || row0 < 0 || nrows < 0 ||
         row0 + nrows > M || dtype < OR_F32 || dtype > OR_BF16 ||
@@ -306,25 +322,60 @@ int oracle_ce_grad_rows(const void *x, int dtype, const int64_t *targets,
         int64_t i = row0 + k;
         const void *xr = row_ptr(x, dtype, i, V);
         int64_t t = targets[i];
+        double ci = d ? c * d[i] : c;
         double lse;
         double loss = row_loss(xr, dtype, V, t, &lse);
         for (int64_t j = 0; j < V; ++j) {
             double g;
             if (j == t)
-                g = expm1(-loss) * c;
+                g = expm1(-loss) * ci;
             else
-                g = exp(elem(xr, dtype, j) - lse) * c;
+                g = exp(elem(xr, dtype, j) - lse) * ci;
             size_t o = (size_t)k * (size_t)V + (size_t)j;
             if (grad64)
                 grad64[o] = g;
-            if (grad_out) {
-                if (out_dtype == OR_F32)
-                    ((float *)grad_out)[o] = oracle_round_f32(g);
-                else if (out_dtype == OR_F16)
-                    ((uint16_t *)grad_out)[o] = oracle_round_f16(g);
-                else
-                    ((uint16_t *)grad_out)[o] = oracle_round_bf16(g);
-            }
+            if (grad_out)
+                store_rounded(grad_out, out_dtype, o, g);
+        }
+    }
+    return 0;
+}
+
+/*
+ * Row softmax (log_softmax == 0) or log-softmax of rows [row0, row0 + nrows):
+ *   softmax_ij     = exp(x_ij - lse_i)
+ *   log_softmax_ij = x_ij - lse_i
+ * ("9 Triton kernels in 9 weeks", week 1: fused row softmax; the
+ * log_softmax of the POPCORNBENCH "Kimi-K2.6 l1_p95" trace's problem
+ * statement).  lse_i is the row's log-sum-exp as in row_loss.  A row that is
+ * entirely -inf has lse = -inf and gives NaN everywhere.  Outputs as for the
+ * gradient; lse_out (may be NULL) receives the fp64 lse of each row.
+ */
+int oracle_softmax_rows(const void *x, int dtype, int64_t M, int64_t V,
+                        int64_t row0, int64_t nrows, int log_softmax,
+                        int out_dtype, void *out, double *out64,
+                        double *lse_out)
+{
+    if (!x || V < 1 || row0 < 0 || nrows < 0 || row0 + nrows > M ||
+        dtype < OR_F32 || dtype > OR_BF16 || out_dtype < OR_F32 ||
+        out_dtype > OR_BF16)
+        return -1;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t k = 0; k < nrows; ++k) {
+        const void *xr = row_ptr(x, dtype, row0 + k, V);
+        double lse;
+        row_loss(xr, dtype, V, -1, &lse);
+        if (lse_out)
+            lse_out[k] = lse;
+        for (int64_t j = 0; j < V; ++j) {
+            double v = elem(xr, dtype, j) - lse;
+            if (!log_softmax)
+                v = exp(v);
+            size_t o = (size_t)k * (size_t)V + (size_t)j;
+            if (out64)
+                out64[o] = v;
+            if (out)
+                store_rounded(out, out_dtype, o, v);
         }
     }
     return 0;

@@ -8,6 +8,9 @@ in the library's HIP kernels; if the library is missing, every call raises.
 
     loss = ce_fwd(logits, targets, reduction="mean")
     loss = ce_fwd_bwd_inplace(logits, targets, reduction="mean")   # logits <- grad
+    loss, lse = ce_fwd_lse(logits, targets, reduction="mean")
+    grad = ce_bwd(logits, targets, lse, reduction="mean", dloss=None)
+    probs = ce_softmax(logits)                    # or log_softmax=True
 """
 import ctypes
 import os
@@ -21,6 +24,7 @@ CE_NONE, CE_MEAN, CE_SUM = 0, 1, 2
 CE_OK = 0
 CE_ERR_NULL, CE_ERR_SHAPE, CE_ERR_DTYPE, CE_ERR_REDUCTION = -1, -2, -3, -4
 CE_ERR_WORKSPACE, CE_ERR_HIP, CE_ERR_ALIGNMENT, CE_ERR_ALIAS = -5, -6, -7, -8
+CE_OP_FWD, CE_OP_FWD_BWD, CE_OP_SOFTMAX, CE_OP_LOG_SOFTMAX, CE_OP_BWD = 0, 1, 2, 3, 4
 REDUCTIONS = {"none": CE_NONE, "mean": CE_MEAN, "sum": CE_SUM}
 
 _lib = None
@@ -52,6 +56,12 @@ def load_library(path=None):
         lib.ce_fwd.restype = i32
         lib.ce_fwd_bwd_inplace.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, sz, vp]
         lib.ce_fwd_bwd_inplace.restype = i32
+        lib.ce_fwd_lse.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, vp, sz, vp]
+        lib.ce_fwd_lse.restype = i32
+        lib.ce_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, vp, vp]
+        lib.ce_bwd.restype = i32
+        lib.ce_softmax.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp]
+        lib.ce_softmax.restype = i32
         lib.ce_status_string.argtypes = [i32]
         lib.ce_status_string.restype = ctypes.c_char_p
         lib.ce_plan_describe.argtypes = [i64, i64, i32, i32, i32, ctypes.c_char_p, sz]
@@ -79,12 +89,14 @@ def ce_workspace_bytes(M, V, dtype, reduction):
     return int(load_library().ce_workspace_bytes(int(M), int(V), int(dtype), int(red)))
 
 
-def ce_plan_describe(M, V, dtype, reduction="mean", fwd_bwd=False):
-    """The launch plan the library picks on the current device."""
+def ce_plan_describe(M, V, dtype, reduction="mean", fwd_bwd=False, op=None):
+    """The launch plan the library picks on the current device (op: CE_OP_*;
+    by default the forward, or the fused backward when fwd_bwd)."""
     red = REDUCTIONS.get(reduction, reduction)
+    if op is None:
+        op = CE_OP_FWD_BWD if fwd_bwd else CE_OP_FWD
     buf = ctypes.create_string_buffer(256)
-    rc = load_library().ce_plan_describe(int(M), int(V), int(dtype), int(red), int(bool(fwd_bwd)),
-                                         buf, 256)
+    rc = load_library().ce_plan_describe(int(M), int(V), int(dtype), int(red), int(op), buf, 256)
     if rc:
         raise CEError(rc, "ce_plan_describe")
     return buf.value.decode()
@@ -102,19 +114,35 @@ def workspace_for(device, stream, nbytes):
     return ws
 
 
-def _check(logits, targets):
-    import torch
+def _check_logits(logits):
     if not logits.is_cuda:
         raise ValueError("logits must be a device tensor")
     if logits.dim() != 2 or not logits.is_contiguous():
         raise ValueError("logits must be a contiguous [M, V] tensor")
+
+
+def _check_rows(t, M, dev, what):
+    import torch
+    if t.dtype != torch.float32 or not t.is_contiguous() or t.device != dev or t.numel() != M:
+        raise ValueError("%s must be a contiguous float32 tensor of %d entries on %s" % (what, M, dev))
+
+
+def _check_like(out, logits, what):
+    if (out.dtype != logits.dtype or out.shape != logits.shape or not out.is_contiguous()
+            or out.device != logits.device):
+        raise ValueError("%s must be a contiguous tensor shaped and typed like the logits" % what)
+
+
+def _check(logits, targets):
+    import torch
+    _check_logits(logits)
     if targets.dtype != torch.int64 or targets.dim() != 1 or not targets.is_contiguous():
         raise ValueError("targets must be a contiguous int64 [M] tensor")
     if targets.device != logits.device or targets.numel() != logits.shape[0]:
         raise ValueError("targets must be on the logits' device with M entries")
 
 
-def _call(fn_name, logits, targets, reduction, out, workspace):
+def _call(fn_name, logits, targets, reduction, out, workspace, lse=None):
     import torch
     lib = load_library()
     _check(logits, targets)
@@ -129,10 +157,13 @@ def _call(fn_name, logits, targets, reduction, out, workspace):
         workspace = workspace_for(dev, stream, nbytes)
     ws_ptr = workspace.data_ptr() if nbytes else None
     ws_len = workspace.numel() * workspace.element_size() if nbytes else 0
+    args = [logits.data_ptr(), targets.data_ptr(), M, V, _dtype_code(logits), red,
+            out.data_ptr() if out.numel() else None]
+    if fn_name == "ce_fwd_lse":
+        _check_rows(lse, M, dev, "lse")
+        args.append(lse.data_ptr() if M else None)
     with torch.cuda.device(dev):
-        rc = getattr(lib, fn_name)(logits.data_ptr(), targets.data_ptr(), M, V, _dtype_code(logits),
-                                   red, out.data_ptr() if out.numel() else None, ws_ptr, ws_len,
-                                   stream.cuda_stream)
+        rc = getattr(lib, fn_name)(*args, ws_ptr, ws_len, stream.cuda_stream)
     if rc:
         raise CEError(rc, fn_name)
     return out
@@ -151,5 +182,66 @@ def ce_fwd_bwd_inplace(logits, targets, reduction="mean", out=None, workspace=No
     return _call("ce_fwd_bwd_inplace", logits, targets, reduction, out, workspace)
 
 
-__all__ = ["ce_fwd", "ce_fwd_bwd_inplace", "ce_workspace_bytes", "ce_status_string",
-           "ce_plan_describe", "load_library", "CEError", "LIB_PATH"]
+def ce_fwd_lse(logits, targets, reduction="mean", out=None, lse=None, workspace=None):
+    """Loss as ce_fwd, plus the [M] fp32 row log-sum-exps; returns (loss, lse)."""
+    import torch
+    if lse is None:
+        lse = torch.empty(logits.shape[0], dtype=torch.float32, device=logits.device)
+    return _call("ce_fwd_lse", logits, targets, reduction, out, workspace, lse=lse), lse
+
+
+def ce_bwd(logits, targets, lse, reduction="mean", dloss=None, grad=None):
+    """Gradient of the loss from saved row log-sum-exps, into grad (a new
+    tensor by default; grad=logits overwrites the logits).  dloss: the
+    upstream gradient, [M] for 'none', one element otherwise, or None for 1."""
+    import torch
+    lib = load_library()
+    _check(logits, targets)
+    red = REDUCTIONS[reduction]
+    M, V = logits.shape
+    dev = logits.device
+    _check_rows(lse, M, dev, "lse")
+    if dloss is not None:
+        _check_rows(dloss, M if red == CE_NONE else 1, dev, "dloss")
+    if grad is None:
+        grad = torch.empty_like(logits)
+    _check_like(grad, logits, "grad")
+    stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = lib.ce_bwd(logits.data_ptr(), targets.data_ptr(), lse.data_ptr() if M else None,
+                        dloss.data_ptr() if dloss is not None else None, M, V,
+                        _dtype_code(logits), red, grad.data_ptr() if M else None,
+                        stream.cuda_stream)
+    if rc:
+        raise CEError(rc, "ce_bwd")
+    return grad
+
+
+def ce_softmax(logits, log_softmax=False, out=None, lse=None):
+    """Row softmax (or log-softmax) of logits [M, V] in their dtype, into out
+    (a new tensor by default; out=logits works in place).  lse: optional [M]
+    fp32 tensor that receives the row log-sum-exps."""
+    import torch
+    lib = load_library()
+    _check_logits(logits)
+    M, V = logits.shape
+    dev = logits.device
+    if out is None:
+        out = torch.empty_like(logits)
+    _check_like(out, logits, "out")
+    if lse is not None:
+        _check_rows(lse, M, dev, "lse")
+    stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = lib.ce_softmax(logits.data_ptr(), M, V, _dtype_code(logits), int(bool(log_softmax)),
+                            out.data_ptr() if M else None,
+                            lse.data_ptr() if (lse is not None and M) else None,
+                            stream.cuda_stream)
+    if rc:
+        raise CEError(rc, "ce_softmax")
+    return out
+
+
+__all__ = ["ce_fwd", "ce_fwd_lse", "ce_fwd_bwd_inplace", "ce_bwd", "ce_softmax",
+           "ce_workspace_bytes", "ce_status_string", "ce_plan_describe", "load_library",
+           "CEError", "LIB_PATH"]

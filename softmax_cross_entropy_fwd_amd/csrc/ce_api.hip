@@ -35,12 +35,19 @@ struct Plan {
     int cus = 0;
 };
 
-KernelRef lookup(int dtype, int kind, int a, int b, bool bwd, bool exact, int nbuf)
+KernelRef lookup(int dtype, int op, int kind, int a, int b, bool exact, int nbuf)
 {
+    const bool fwd = op == cek::EPI_NONE;
     switch (dtype) {
-    case CE_F32: return cek::get_kernel_f32(kind, a, b, bwd, exact, nbuf);
-    case CE_F16: return cek::get_kernel_f16(kind, a, b, bwd, exact, nbuf);
-    default: return cek::get_kernel_bf16(kind, a, b, bwd, exact, nbuf);
+    case CE_F32:
+        return fwd ? cek::get_kernel_f32_fwd(op, kind, a, b, exact, nbuf)
+                   : cek::get_kernel_f32_epi(op, kind, a, b, exact, nbuf);
+    case CE_F16:
+        return fwd ? cek::get_kernel_f16_fwd(op, kind, a, b, exact, nbuf)
+                   : cek::get_kernel_f16_epi(op, kind, a, b, exact, nbuf);
+    default:
+        return fwd ? cek::get_kernel_bf16_fwd(op, kind, a, b, exact, nbuf)
+                   : cek::get_kernel_bf16_epi(op, kind, a, b, exact, nbuf);
     }
 }
 
@@ -181,36 +188,49 @@ int64_t window_vectors(int64_t V, int E, bool aligned)
     return aligned ? V / E : (V + 2 * E - 2) / E;
 }
 
-int make_plan(int64_t M, int64_t V, int dtype, bool bwd, bool aligned, Plan *plan)
+// The split backward streams each row once (chunks of G*4 vectors per G
+// lanes): a few lanes per row for short rows, a whole wave for long ones.
+void choose_lse_grad_shape(int64_t nvec, int *a, int *b)
+{
+    *a = nvec <= 16 ? 4 : nvec <= 64 ? 16 : 64;
+    *b = 4;
+}
+
+int make_plan(int64_t M, int64_t V, int dtype, int op, bool aligned, Plan *plan)
 {
     const int E = 16 / (int)elem_size(dtype);
     const int64_t nvec = window_vectors(V, E, aligned);
     int kind = 0, a = 0, b = 0, nbuf = 1;
-    choose_shape(nvec, bwd, &kind, &a, &b, &nbuf);
-    int fk, fa, fb;
-    if (forced_shape(&fk, &fa, &fb)) {
-        const int64_t tile = tile_vectors(fk, fa, fb);
-        if (lookup(dtype, fk, fa, fb, bwd, false, 1).fn &&
-            (fk == cek::KIND_STREAM || fk == cek::KIND_WSTREAM || tile >= nvec)) {
-            kind = fk;
-            a = fa;
-            b = fb;
-            nbuf = 1;
+    if (op == cek::EPI_LSE_GRAD) {
+        kind = cek::KIND_ROWS;
+        choose_lse_grad_shape(nvec, &a, &b);
+    } else {
+        choose_shape(nvec, op != cek::EPI_NONE, &kind, &a, &b, &nbuf);
+        int fk, fa, fb;
+        if (forced_shape(&fk, &fa, &fb)) {
+            const int64_t tile = tile_vectors(fk, fa, fb);
+            if (lookup(dtype, op, fk, fa, fb, false, 1).fn &&
+                (fk == cek::KIND_STREAM || fk == cek::KIND_WSTREAM || tile >= nvec)) {
+                kind = fk;
+                a = fa;
+                b = fb;
+                nbuf = 1;
+            }
         }
     }
     plan->kind = kind;
     plan->a = a;
     plan->b = b;
-    plan->exact = aligned && tile_vectors(kind, a, b) == nvec;
+    plan->exact = op != cek::EPI_LSE_GRAD && aligned && tile_vectors(kind, a, b) == nvec;
     plan->nbuf = kind == cek::KIND_ROWS ? nbuf : 1;
     const char *nb = std::getenv("CE_FORCE_NBUF");
-    if (kind == cek::KIND_ROWS && nb &&
+    if (kind == cek::KIND_ROWS && op != cek::EPI_LSE_GRAD && nb &&
         (std::atoi(nb) == 1 || std::atoi(nb) == 2 || std::atoi(nb) == 17 || std::atoi(nb) == 18))
         plan->nbuf = std::atoi(nb);
-    plan->k = lookup(dtype, kind, a, b, bwd, plan->exact, plan->nbuf);
+    plan->k = lookup(dtype, op, kind, a, b, plan->exact, plan->nbuf);
     if (!plan->k.fn && plan->nbuf != nbuf) {   // an override with no such instance
         plan->nbuf = kind == cek::KIND_ROWS ? nbuf : 1;
-        plan->k = lookup(dtype, kind, a, b, bwd, plan->exact, plan->nbuf);
+        plan->k = lookup(dtype, op, kind, a, b, plan->exact, plan->nbuf);
     }
     if (!plan->k.fn)
         return CE_ERR_HIP;
@@ -229,10 +249,12 @@ int make_plan(int64_t M, int64_t V, int dtype, bool bwd, bool aligned, Plan *pla
     int64_t needed = (M + rows_per_wg - 1) / rows_per_wg;
     // Few deep waves beat many shallow ones here (measured): each wave keeps
     // a whole row of loads in flight, so the rows kernel runs 4 waves per CU
-    // and the workgroup kernels 16.
+    // and the workgroup kernels 16.  The split backward has only one chunk
+    // of loads in flight per lane and wants more waves.
     const int waves_per_wg = plan->k.block / 64;
     const char *tw = std::getenv("CE_WAVES_PER_CU");
     const int target_waves = (tw && std::atoi(tw) > 0) ? std::atoi(tw)
+                             : op == cek::EPI_LSE_GRAD ? 32
                              : kind == cek::KIND_ROWS  ? 4
                                                        : 16;
     int wg_per_cu = target_waves / waves_per_wg;
@@ -260,84 +282,140 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb)
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-int check_args(const void *logits, const int64_t *targets, int64_t M, int64_t V, int dtype,
-               int reduction, const float *out, const void *ws, size_t ws_bytes, bool bwd)
+// Everything one call hands over.  Pointers a given operation does not use
+// are null.
+struct Call {
+    int op = cek::EPI_NONE;
+    const void *logits = nullptr;
+    const int64_t *targets = nullptr;
+    int64_t M = 0, V = 0;
+    int dtype = CE_F32;
+    int reduction = CE_NONE;
+    float *out = nullptr;          // losses: [M] (none) or [1]
+    float *lse_out = nullptr;      // [M] or null
+    const float *lse_in = nullptr; // [M] (split backward)
+    const float *dloss = nullptr;  // [M] (none) or [1] (split backward), or null
+    void *y = nullptr;             // [M, V] epilogue output (may equal logits)
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    bool loss = true;              // computes losses (needs targets and out)
+};
+
+struct Region {
+    const void *p;
+    size_t n;
+};
+
+int check_args(const Call &c)
 {
-    if (dtype != CE_F32 && dtype != CE_F16 && dtype != CE_BF16)
+    if (c.dtype != CE_F32 && c.dtype != CE_F16 && c.dtype != CE_BF16)
         return CE_ERR_DTYPE;
-    if (reduction != CE_NONE && reduction != CE_MEAN && reduction != CE_SUM)
+    if (c.reduction != CE_NONE && c.reduction != CE_MEAN && c.reduction != CE_SUM)
         return CE_ERR_REDUCTION;
-    if (M < 0 || V < 1 || V > CE_MAX_V)
+    if (c.M < 0 || c.V < 1 || c.V > CE_MAX_V)
         return CE_ERR_SHAPE;
-    const size_t s = elem_size(dtype);
-    if (M > 0 && (uint64_t)M > (uint64_t)INT64_MAX / (uint64_t)V / s)
+    const size_t s = elem_size(c.dtype);
+    if (c.M > 0 && (uint64_t)c.M > (uint64_t)INT64_MAX / (uint64_t)c.V / s)
         return CE_ERR_SHAPE;
-    if (M == 0) {
-        if (reduction != CE_NONE && !out)
+    const bool reduced = c.loss && c.reduction != CE_NONE;
+    if (c.M == 0) {
+        if (reduced && !c.out)
             return CE_ERR_NULL;
         return CE_OK;
     }
-    if (!logits || !targets || !out)
+    const bool needs_targets = c.loss || c.op == cek::EPI_LSE_GRAD;
+    const bool has_y = c.op != cek::EPI_NONE;
+    if (!c.logits || (needs_targets && !c.targets) || (c.loss && !c.out) || (has_y && !c.y) ||
+        (c.op == cek::EPI_LSE_GRAD && !c.lse_in))
         return CE_ERR_NULL;
-    if ((uintptr_t)logits % s)
+    if ((uintptr_t)c.logits % s || (uintptr_t)c.targets % 8 || (uintptr_t)c.out % 4 ||
+        (uintptr_t)c.lse_out % 4 || (uintptr_t)c.lse_in % 4 || (uintptr_t)c.dloss % 4)
         return CE_ERR_ALIGNMENT;
-    if (reduction != CE_NONE) {
-        if (!ws || ws_bytes < kWorkspaceBytes || (uintptr_t)ws % 8)
+    // the output is written with the vectors the input is read with
+    if (has_y && (uintptr_t)c.y % 16 != (uintptr_t)c.logits % 16)
+        return CE_ERR_ALIGNMENT;
+    if (reduced) {
+        if (!c.ws || c.ws_bytes < kWorkspaceBytes || (uintptr_t)c.ws % 8)
             return CE_ERR_WORKSPACE;
     }
-    if (bwd) {
-        const size_t xb = (size_t)M * (size_t)V * s;
-        const size_t ob = reduction == CE_NONE ? (size_t)M * 4 : 4;
-        if (overlaps(logits, xb, targets, (size_t)M * 8) || overlaps(logits, xb, out, ob) ||
-            (reduction != CE_NONE && overlaps(logits, xb, ws, kWorkspaceBytes)))
-            return CE_ERR_ALIAS;
+    // Outputs may not overlap one another or any input; the epilogue output
+    // may be the logits themselves (exactly, in place).
+    const size_t xb = (size_t)c.M * (size_t)c.V * s;
+    const size_t per_row = (size_t)c.M * 4;
+    const size_t nd = c.reduction == CE_NONE ? per_row : 4;
+    const Region outs[] = {
+        {c.out, c.loss ? (c.reduction == CE_NONE ? per_row : 4) : 0},
+        {c.lse_out, per_row},
+        {c.y == c.logits ? nullptr : c.y, has_y ? xb : 0},
+        {c.y == c.logits ? c.y : nullptr, has_y ? xb : 0},
+        {c.ws, reduced ? kWorkspaceBytes : 0},
+    };
+    const Region ins[] = {
+        {c.y == c.logits ? nullptr : c.logits, xb},
+        {c.targets, needs_targets ? (size_t)c.M * 8 : 0},
+        {c.lse_in, c.op == cek::EPI_LSE_GRAD ? per_row : 0},
+        {c.dloss, c.op == cek::EPI_LSE_GRAD ? nd : 0},
+    };
+    const int no = sizeof(outs) / sizeof(outs[0]), ni = sizeof(ins) / sizeof(ins[0]);
+    for (int i = 0; i < no; ++i) {
+        for (int j = i + 1; j < no; ++j)
+            if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+                return CE_ERR_ALIAS;
+        for (int j = 0; j < ni; ++j)
+            if (overlaps(outs[i].p, outs[i].n, ins[j].p, ins[j].n))
+                return CE_ERR_ALIAS;
     }
     return CE_OK;
 }
 
-int run(const void *logits, const int64_t *targets, int64_t M, int64_t V, int dtype,
-        int reduction, float *out, void *ws, size_t ws_bytes, void *stream, bool bwd)
+int run(const Call &c, void *stream)
 {
-    int rc = check_args(logits, targets, M, V, dtype, reduction, out, ws, ws_bytes, bwd);
+    int rc = check_args(c);
     if (rc)
         return rc;
     hipStream_t st = (hipStream_t)stream;
-    if (M == 0) {
-        if (reduction == CE_NONE)
+    if (c.M == 0) {
+        if (!c.loss || c.reduction == CE_NONE)
             return CE_OK;
-        float value = reduction == CE_MEAN ? __builtin_nanf("") : 0.0f;
+        float value = c.reduction == CE_MEAN ? __builtin_nanf("") : 0.0f;
+        float *out = c.out;
         void *args[] = {&out, &value};
         if (hipLaunchKernel(cek::empty_reduce_fn(), dim3(1), dim3(64), args, 0, st) != hipSuccess)
             return CE_ERR_HIP;
         return CE_OK;
     }
-    const size_t s = elem_size(dtype);
+    const size_t s = elem_size(c.dtype);
     const int E = 16 / (int)s;
-    const uintptr_t base = (uintptr_t)logits;
+    const uintptr_t base = (uintptr_t)c.logits;
     const int head0 = (int)((base % 16) / s);
-    const bool aligned = head0 == 0 && V % E == 0;
+    const bool aligned = head0 == 0 && c.V % E == 0;
     Plan plan;
-    rc = make_plan(M, V, dtype, bwd, aligned, &plan);
+    rc = make_plan(c.M, c.V, c.dtype, c.op, aligned, &plan);
     if (rc)
         return rc;
 
+    const int reduction = c.loss ? c.reduction : CE_NONE;
     cek::Params p;
     p.x = (cek::Vec *)(base - (uintptr_t)head0 * s);
-    p.targets = targets;
-    p.out = out;
-    p.ticket = reduction == CE_NONE ? nullptr : (unsigned int *)ws;
-    p.partials = reduction == CE_NONE ? nullptr : (double *)((char *)ws + kTicketBytes);
-    p.M = M;
-    p.V = V;
+    p.y = c.y ? (cek::Vec *)((uintptr_t)c.y - (uintptr_t)head0 * s) : nullptr;
+    p.targets = c.targets;
+    p.out = c.loss ? c.out : nullptr;
+    p.ticket = reduction == CE_NONE ? nullptr : (unsigned int *)c.ws;
+    p.partials = reduction == CE_NONE ? nullptr : (double *)((char *)c.ws + kTicketBytes);
+    p.M = c.M;
+    p.V = c.V;
     p.head0 = head0;
     p.aligned = aligned ? 1 : 0;
     const char *map = std::getenv("CE_ROW_MAP");
     p.blocked = (map && !std::strcmp(map, "blocked")) ? 1 : 0;
-    p.reduction = reduction;
-    const double c = reduction == CE_MEAN ? 1.0 / (double)M : 1.0;
-    p.c = (float)c;
-    p.log2c = (float)std::log2(c);
-    p.out_scale = c;
+    // the split backward takes its reduction only for the gradient scale
+    p.reduction = c.op == cek::EPI_LSE_GRAD ? c.reduction : reduction;
+    const double scale = c.reduction == CE_MEAN ? 1.0 / (double)c.M : 1.0;
+    p.c = (float)scale;
+    p.out_scale = scale;
+    p.dloss = c.dloss;
+    p.lse_out = c.lse_out;
+    p.lse_in = c.lse_in;
     void *args[] = {&p};
     if (hipLaunchKernel(plan.k.fn, dim3((unsigned)plan.grid), dim3(plan.k.block), args, 0, st) !=
         hipSuccess)
@@ -364,16 +442,90 @@ int ce_fwd(const void *logits, const int64_t *targets, int64_t M, int64_t V, ce_
            ce_reduction_t reduction, float *out, void *workspace, size_t workspace_bytes,
            void *stream)
 {
-    return run(logits, targets, M, V, (int)dtype, (int)reduction, out, workspace,
-               workspace_bytes, stream, false);
+    Call c;
+    c.logits = logits;
+    c.targets = targets;
+    c.M = M;
+    c.V = V;
+    c.dtype = (int)dtype;
+    c.reduction = (int)reduction;
+    c.out = out;
+    c.ws = workspace;
+    c.ws_bytes = workspace_bytes;
+    return run(c, stream);
+}
+
+int ce_fwd_lse(const void *logits, const int64_t *targets, int64_t M, int64_t V,
+               ce_dtype_t dtype, ce_reduction_t reduction, float *out, float *lse,
+               void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (M > 0 && !lse)
+        return CE_ERR_NULL;
+    Call c;
+    c.logits = logits;
+    c.targets = targets;
+    c.M = M;
+    c.V = V;
+    c.dtype = (int)dtype;
+    c.reduction = (int)reduction;
+    c.out = out;
+    c.lse_out = lse;
+    c.ws = workspace;
+    c.ws_bytes = workspace_bytes;
+    return run(c, stream);
 }
 
 int ce_fwd_bwd_inplace(void *logits, const int64_t *targets, int64_t M, int64_t V,
                        ce_dtype_t dtype, ce_reduction_t reduction, float *loss_out,
                        void *workspace, size_t workspace_bytes, void *stream)
 {
-    return run(logits, targets, M, V, (int)dtype, (int)reduction, loss_out, workspace,
-               workspace_bytes, stream, true);
+    Call c;
+    c.op = cek::EPI_GRAD;
+    c.logits = logits;
+    c.y = logits;
+    c.targets = targets;
+    c.M = M;
+    c.V = V;
+    c.dtype = (int)dtype;
+    c.reduction = (int)reduction;
+    c.out = loss_out;
+    c.ws = workspace;
+    c.ws_bytes = workspace_bytes;
+    return run(c, stream);
+}
+
+int ce_bwd(const void *logits, const int64_t *targets, const float *lse, const float *dloss,
+           int64_t M, int64_t V, ce_dtype_t dtype, ce_reduction_t reduction, void *grad,
+           void *stream)
+{
+    Call c;
+    c.op = cek::EPI_LSE_GRAD;
+    c.loss = false;
+    c.logits = logits;
+    c.targets = targets;
+    c.lse_in = lse;
+    c.dloss = dloss;
+    c.M = M;
+    c.V = V;
+    c.dtype = (int)dtype;
+    c.reduction = (int)reduction;
+    c.y = grad;
+    return run(c, stream);
+}
+
+int ce_softmax(const void *logits, int64_t M, int64_t V, ce_dtype_t dtype, int log_softmax,
+               void *out, float *lse, void *stream)
+{
+    Call c;
+    c.op = log_softmax ? cek::EPI_LOGSOFTMAX : cek::EPI_SOFTMAX;
+    c.loss = false;
+    c.logits = logits;
+    c.M = M;
+    c.V = V;
+    c.dtype = (int)dtype;
+    c.y = out;
+    c.lse_out = lse;
+    return run(c, stream);
 }
 
 const char *ce_status_string(int status)
@@ -386,14 +538,16 @@ const char *ce_status_string(int status)
     case CE_ERR_REDUCTION: return "unknown reduction";
     case CE_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case CE_ERR_HIP: return "HIP runtime error or launch failure";
-    case CE_ERR_ALIGNMENT: return "logits not aligned to its element size";
-    case CE_ERR_ALIAS: return "in-place logits overlap targets, output or workspace";
+    case CE_ERR_ALIGNMENT:
+        return "a pointer not aligned to its element size, or an output not at the logits' "
+               "address modulo 16";
+    case CE_ERR_ALIAS: return "an output overlaps another output or an input";
     default: return "unknown status";
     }
 }
 
-int ce_plan_describe(int64_t M, int64_t V, ce_dtype_t dtype, ce_reduction_t reduction,
-                     int fwd_bwd, char *buf, size_t buf_len)
+int ce_plan_describe(int64_t M, int64_t V, ce_dtype_t dtype, ce_reduction_t reduction, int op,
+                     char *buf, size_t buf_len)
 {
     if (!buf || !buf_len)
         return CE_ERR_NULL;
@@ -403,10 +557,14 @@ int ce_plan_describe(int64_t M, int64_t V, ce_dtype_t dtype, ce_reduction_t redu
         return CE_ERR_REDUCTION;
     if (M < 1 || V < 1 || V > CE_MAX_V)
         return CE_ERR_SHAPE;
+    static const int ops[] = {cek::EPI_NONE, cek::EPI_GRAD, cek::EPI_SOFTMAX, cek::EPI_LOGSOFTMAX,
+                              cek::EPI_LSE_GRAD};
+    if (op < CE_OP_FWD || op > CE_OP_BWD)
+        return CE_ERR_SHAPE;
     const int E = 16 / (int)elem_size(dtype);
     const bool aligned = V % E == 0;   // for a 16-byte aligned base
     Plan plan;
-    int rc = make_plan(M, V, (int)dtype, fwd_bwd != 0, aligned, &plan);
+    int rc = make_plan(M, V, (int)dtype, ops[op], aligned, &plan);
     if (rc)
         return rc;
     static const char *names[] = {"rows", "wg", "stream", "wstream"};

@@ -38,6 +38,8 @@ namespace cek {
 
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 enum : int { RED_NONE = 0, RED_MEAN = 1, RED_SUM = 2 };
+// What the kernels write over (or next to) the row once its log-sum-exp is known.
+enum : int { EPI_NONE = 0, EPI_GRAD = 1, EPI_SOFTMAX = 2, EPI_LOGSOFTMAX = 3 };
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
@@ -59,9 +61,12 @@ struct Params {
     int aligned;             // every row starts and ends on a 16-byte boundary
     int blocked;             // each workgroup takes a contiguous band of rows
     int reduction;
-    float c;                 // gradient scale
-    float log2c;             // log2(c)
+    float c;                 // gradient scale (1/M for mean, 1 otherwise)
     double out_scale;        // 1/M (mean) or 1 (sum)
+    Vec *y;                  // epilogue output, same 16-byte phase as x (== x in place)
+    const float *dloss;      // upstream gradient, [M] (none) or [1]; null means 1
+    float *lse_out;          // optional [M] row log-sum-exps
+    const float *lse_in;     // [M] given log-sum-exps (backward from saved statistics)
 };
 
 // ------------------------------------------------------------ storage types
@@ -326,64 +331,63 @@ __device__ __forceinline__ bool vec_valid(int k, int kfull, int lidx, int nvec)
     return k < kfull || lidx + STRIDE * k < nvec;
 }
 
-// Gradient coefficients for one row: g = 2^(x*log2e - bias) * post.
-// fp16: the scale c is folded into the exponent.  bf16, whose range reaches
-// below fp32's normal range: the exponent is lifted by 64 and the product
-// scaled back by 2^-64, so gradients that round to bf16 subnormals are formed
-// from normal fp32 values.  fp32: g = 2^((x - m)*log2e - log2 s) * c, which
-// keeps the exponent small and the relative error near 1e-6.
+// Per-row constants of the write epilogue, with p = 2^(x log2e - lse log2e):
+//   GRAD        g = (p - [j == t]) * c      (the target's element is patched)
+//   SOFTMAX     y = p
+//   LOGSOFTMAX  y = x - lse
+// log2|c| is folded into the exponent and the sign of c applied afterwards
+// (c = 0 gives 0).  bf16, whose range reaches below fp32's normal range: the
+// exponent is lifted by 64 and the product scaled by 2^-64, so results that
+// round to bf16 subnormals are formed from normal fp32 values.  fp32: the
+// exponent is (x - m) log2e - (log2 s - log2|c|), keeping it small and the
+// relative error near 1e-6.
 template <int DT>
-struct GradCoef {
+struct EpiCoef {
     float m;
     float bias;
-    float post;
+    float post;     // sign of c (and the 2^-64 lift for bf16)
+    float lse;
 };
 
-template <int DT>
-__device__ __forceinline__ GradCoef<DT> grad_coef(float m, float mL, float log2s, float c, float log2c)
+template <int DT, int OP>
+__device__ __forceinline__ EpiCoef<DT> epi_coef(float m, float mL, float log2s, float c)
 {
-    GradCoef<DT> g;
-    g.m = m;
+    EpiCoef<DT> e;
+    e.m = m;
+    e.lse = m + kLn2 * log2s;
+    const float ac = OP == EPI_GRAD ? fabsf(c) : 1.0f;
+    const float sgn = (OP == EPI_GRAD && c < 0.0f) ? -1.0f : 1.0f;
+    const float l2c = __log2f(ac);
     if constexpr (DT == DT_F32) {
-        g.bias = log2s;
-        g.post = c;
+        e.bias = log2s - l2c;
+        e.post = sgn;
     } else if constexpr (DT == DT_F16) {
-        g.bias = mL + log2s - log2c;
-        g.post = 1.0f;
+        e.bias = mL + log2s - l2c;
+        e.post = sgn;
     } else {
-        g.bias = mL + log2s - log2c - 64.0f;
-        g.post = 5.42101086242752217e-20f;   // 2^-64
+        e.bias = mL + log2s - l2c - 64.0f;
+        e.post = sgn * 5.42101086242752217e-20f;   // 2^-64
     }
-    return g;
+    return e;
 }
 
-template <int DT>
-__device__ __forceinline__ float grad_elem(float x, const GradCoef<DT> &gc)
-{
-    if constexpr (DT == DT_F32)
-        return fast_exp2(__builtin_fmaf(x - gc.m, kLog2e, -gc.bias)) * gc.post;
-    else if constexpr (DT == DT_F16)
-        return fast_exp2(__builtin_fmaf(x, kLog2e, -gc.bias));
-    else
-        return fast_exp2(__builtin_fmaf(x, kLog2e, -gc.bias)) * gc.post;
-}
-
-// Gradients of one vector, with the target's element replaced by gt when
-// is_target; returns the packed vector.
-template <int DT>
-__device__ __forceinline__ Vec grad_vec(const Vec &in, const GradCoef<DT> &gc, bool is_target,
-                                        int jt, float gt)
+// The epilogue of one vector, packed to the storage type.
+template <int DT, int OP>
+__device__ __forceinline__ Vec epi_vec(const Vec &in, const EpiCoef<DT> &ec)
 {
     constexpr int E = Traits<DT>::E;
     float g[E];
 #pragma unroll
-    for (int j = 0; j < E; ++j)
-        g[j] = grad_elem<DT>(elem<DT>(in, j), gc);
-    if (is_target) {
-#pragma unroll
-        for (int j = 0; j < E; ++j)
-            if (j == jt)
-                g[j] = gt;
+    for (int j = 0; j < E; ++j) {
+        const float x = elem<DT>(in, j);
+        if constexpr (OP == EPI_LOGSOFTMAX)
+            g[j] = x - ec.lse;
+        else if constexpr (DT == DT_F32)
+            g[j] = fast_exp2(__builtin_fmaf(x - ec.m, kLog2e, -ec.bias)) * ec.post;
+        else if constexpr (DT == DT_F16)
+            g[j] = fast_exp2(__builtin_fmaf(x, kLog2e, -ec.bias));
+        else
+            g[j] = fast_exp2(__builtin_fmaf(x, kLog2e, -ec.bias)) * ec.post;
     }
     Vec out;
     if constexpr (DT == DT_F32) {
@@ -394,6 +398,13 @@ __device__ __forceinline__ Vec grad_vec(const Vec &in, const GradCoef<DT> &gc, b
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             out.w[j] = pack2<DT>(g[2 * j], g[2 * j + 1]);
+        if constexpr (DT == DT_F16 && OP != EPI_LOGSOFTMAX) {
+            if (ec.post < 0.0f) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    out.w[j] ^= 0x80008000u;
+            }
+        }
     }
     return out;
 }
@@ -474,8 +485,8 @@ __device__ __forceinline__ RowResult row_result(bool tvalid, float m, float xt, 
     return r;
 }
 
-// Writes the gradient of window vector v (lane's k-th vector) over the row,
-// leaving elements outside the row untouched.
+// Writes window vector v of the epilogue output row, leaving elements outside
+// the row untouched.
 template <int DT>
 __device__ __forceinline__ void store_grad(Vec *xrow, int v, const Vec &g, int head, int64_t V,
                                            bool aligned)
@@ -660,7 +671,8 @@ __device__ __forceinline__ void set_elem(Vec &g, int jt, float val)
 
 // Window geometry of one row.
 struct Window {
-    Vec *xrow;
+    Vec *xrow;       // the row's first window vector
+    Vec *yrow;       // the same window in the epilogue output
     int head;
     int nvec;
 };
@@ -672,9 +684,19 @@ __device__ __forceinline__ Window row_window(const Params &p, int64_t row)
     const int64_t e0 = row * p.V + p.head0;
     Window w;
     w.xrow = p.x + (e0 / E);
+    w.yrow = p.y + (e0 / E);
     w.head = (int)(e0 % E);
     w.nvec = (int)((w.head + p.V + E - 1) / E);
     return w;
+}
+
+// The gradient scale of a row: 1/M (mean) or 1, times the upstream gradient
+// (per row for none, one value otherwise) when one is given.
+__device__ __forceinline__ float row_scale(const Params &p, int64_t row)
+{
+    if (!p.dloss)
+        return p.c;
+    return p.c * p.dloss[p.reduction == RED_NONE ? row : 0];
 }
 
 // Row state carried by the register pipeline: the row in raw[] was loaded
@@ -693,12 +715,13 @@ struct RowRef {
 // row is reduced and written.  After the last row, `next` is the same row
 // again (a cache hit, never used), which keeps the loads unconditional.
 // Returns the row's loss (same in every lane).
-template <int DT, int K, int STRIDE, bool BWD, bool EXACT, class Red>
+template <int DT, int K, int STRIDE, int OP, bool EXACT, class Red>
 __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&raw)[K],
                                                const RowRef &cur, const RowRef &next, int lidx,
                                                int kfull)
 {
     constexpr int E = Traits<DT>::E;
+    constexpr bool BWD = OP != EPI_NONE;
     const Window &w = cur.w;
     const TargetPos tp = target_pos<DT>(cur.t, p.V, w.head);
     const float xt = tp.valid ? load_logit<DT>(p, cur.row, cur.t) : __builtin_nanf("");
@@ -747,23 +770,27 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
     if (accurate)
         s_excl = red.sum_excl(sum_without_target<DT>(p, w.xrow, lidx, STRIDE, w.nvec, w.head,
                                                      mL, tp.vt, tp.jt));
-    const RowResult rr = row_result(tp.valid, m, xt, et, s, s_excl, accurate, p.c);
+    const float c = row_scale(p, cur.row);
+    const RowResult rr = row_result(tp.valid, m, xt, et, s, s_excl, accurate, c);
+    const float log2s = __log2f(s);
+    if (p.lse_out && cur.active && lidx == 0)
+        p.lse_out[cur.row] = m + kLn2 * log2s;
 
     if constexpr (BWD) {
         opt_barrier<DT, K>(raw);
-        const GradCoef<DT> gc = grad_coef<DT>(m, mL, __log2f(s), p.c, p.log2c);
-        const int kt = tp.valid ? tp.vt / STRIDE : -1;
+        const EpiCoef<DT> ec = epi_coef<DT, OP>(m, mL, log2s, c);
+        const int kt = (OP == EPI_GRAD && tp.valid) ? tp.vt / STRIDE : -1;
         const bool is_owner = tp.valid && lidx == tp.vt % STRIDE;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int v = lidx + STRIDE * k;
-            Vec g = grad_vec<DT>(raw[k], gc, false, 0, 0.0f);
+            Vec g = epi_vec<DT, OP>(raw[k], ec);
             if (k == kt) {
                 if (is_owner)
                     set_elem<DT>(g, tp.jt, rr.gt);
             }
             if (cur.active && vec_valid<STRIDE, EXACT>(k, kfull, lidx, w.nvec))
-                store_grad<DT>(w.xrow, v, g, w.head, p.V, EXACT || p.aligned);
+                store_grad<DT>(w.yrow, v, g, w.head, p.V, EXACT || p.aligned);
             raw[k] = ldv(&next.w.xrow[(EXACT || v < next.w.nvec) ? v : next.w.nvec - 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -808,7 +835,6 @@ __device__ __forceinline__ void finish_reduction(const Params &p, double wg_sum)
 
 // ================================================================ kernels
 
-// ================================================================ kernels
 
 template <int DT>
 __device__ __forceinline__ RowRef row_ref(const Params &p, int64_t row)
@@ -819,7 +845,7 @@ __device__ __forceinline__ RowRef row_ref(const Params &p, int64_t row)
     // The target is read here, a step before it is used and before the row's
     // own loads: vector loads retire in order, so a late target load would
     // make the wave wait for every prefetch issued before it.
-    r.t = r.active ? p.targets[r.row] : -1;
+    r.t = (r.active && p.targets) ? p.targets[r.row] : -1;
     r.w = row_window<DT>(p, r.row);
     return r;
 }
@@ -827,7 +853,7 @@ __device__ __forceinline__ RowRef row_ref(const Params &p, int64_t row)
 // ---- G lanes per row, row in registers ------------------------------------
 // NBUF row buffers per lane: with 2, the rows a wave handles alternate between
 // two register sets, so each row's loads are issued a whole row ahead.
-template <int DT, int G, int K, bool BWD, bool EXACT, int NBUF, int NW = 4>
+template <int DT, int G, int K, int OP, bool EXACT, int NBUF, int NW = 4>
 __global__ void __launch_bounds__(NW * 64) rows_kernel(Params p)
 {
     static_assert(NBUF == 1 || NBUF == 2, "NBUF");
@@ -858,10 +884,12 @@ __global__ void __launch_bounds__(NW * 64) rows_kernel(Params p)
     }
     auto record = [&](const RowRef &r, float loss) {
         if (r.active && lig == 0) {
-            if (p.reduction == RED_NONE)
-                p.out[r.row] = loss;
-            else
+            if (p.reduction == RED_NONE) {
+                if (p.out)
+                    p.out[r.row] = loss;
+            } else {
                 acc += (double)loss;
+            }
         }
     };
     // the group's row in the wave's row block `base`, or fallback past the end
@@ -876,7 +904,7 @@ __global__ void __launch_bounds__(NW * 64) rows_kernel(Params p)
         if constexpr (NBUF == 1) {
             for (; rb < row_end; rb += row_step) {
                 const RowRef an = ref_at(rb + row_step, a);
-                record(a, pipeline_step<DT, K, G, BWD, EXACT>(p, red, ra, a, an, lig, kfull));
+                record(a, pipeline_step<DT, K, G, OP, EXACT>(p, red, ra, a, an, lig, kfull));
                 a = an;
             }
         } else {
@@ -885,11 +913,11 @@ __global__ void __launch_bounds__(NW * 64) rows_kernel(Params p)
             issue_loads<DT, K, G, EXACT>(rbuf, b.w.xrow, lig, b.w.nvec);
             for (; rb < row_end; rb += 2 * row_step) {
                 const RowRef an = ref_at(rb + 2 * row_step, a);
-                record(a, pipeline_step<DT, K, G, BWD, EXACT>(p, red, ra, a, an, lig, kfull));
+                record(a, pipeline_step<DT, K, G, OP, EXACT>(p, red, ra, a, an, lig, kfull));
                 if (rb + row_step >= row_end)
                     break;
                 const RowRef bn = ref_at(rb + 3 * row_step, b);
-                record(b, pipeline_step<DT, K, G, BWD, EXACT>(p, red, rbuf, b, bn, lig, kfull));
+                record(b, pipeline_step<DT, K, G, OP, EXACT>(p, red, rbuf, b, bn, lig, kfull));
                 a = an;
                 b = bn;
             }
@@ -911,7 +939,7 @@ __global__ void __launch_bounds__(NW * 64) rows_kernel(Params p)
 }
 
 // ---- one row per workgroup, row in registers --------------------------------
-template <int DT, int W, int K, bool BWD, bool EXACT>
+template <int DT, int W, int K, int OP, bool EXACT>
 __global__ void __launch_bounds__(W * 64) wg_kernel(Params p)
 {
     constexpr int E = Traits<DT>::E;
@@ -947,12 +975,14 @@ __global__ void __launch_bounds__(W * 64) wg_kernel(Params p)
             const bool has_next = row + row_step < row_end;
             const RowRef next = has_next ? row_ref<DT>(p, row + row_step) : cur;
             const float loss =
-                pipeline_step<DT, K, NT, BWD, EXACT>(p, red, raw, cur, next, threadIdx.x, kfull);
+                pipeline_step<DT, K, NT, OP, EXACT>(p, red, raw, cur, next, threadIdx.x, kfull);
             if (threadIdx.x == 0) {
-                if (p.reduction == RED_NONE)
-                    p.out[row] = loss;
-                else
+                if (p.reduction == RED_NONE) {
+                    if (p.out)
+                        p.out[row] = loss;
+                } else {
                     acc += (double)loss;
+                }
             }
             cur = next;
         }
@@ -980,7 +1010,7 @@ __global__ void __launch_bounds__(256) wstream_kernel(Params p)
 
     for (int64_t row = (int64_t)blockIdx.x * nwaves + wave; row < p.M; row += step) {
         const Window w = row_window<DT>(p, row);
-        const int64_t t = p.targets[row];
+        const int64_t t = p.targets ? p.targets[row] : -1;
         const TargetPos tp = target_pos<DT>(t, p.V, w.head);
         const float xt = tp.valid ? load_logit<DT>(p, row, t) : __builtin_nanf("");
         float m_run = -__builtin_inff();
@@ -1024,10 +1054,14 @@ __global__ void __launch_bounds__(256) wstream_kernel(Params p)
                                                          tp.vt, tp.jt));
         const RowResult rr = row_result(tp.valid, m, xt, et, s, s_excl, accurate, p.c);
         if (lane == 0) {
-            if (p.reduction == RED_NONE)
-                p.out[row] = rr.loss;
-            else
+            if (p.lse_out)
+                p.lse_out[row] = m + kLn2 * __log2f(s);
+            if (p.reduction == RED_NONE) {
+                if (p.out)
+                    p.out[row] = rr.loss;
+            } else {
                 acc += (double)rr.loss;
+            }
         }
     }
     if (p.reduction == RED_NONE)
@@ -1043,10 +1077,72 @@ __global__ void __launch_bounds__(256) wstream_kernel(Params p)
     finish_reduction(p, wg_sum);
 }
 
+// ---- gradient from a saved log-sum-exp -------------------------------------
+// The split backward: lse comes from an earlier forward, so every row is a
+// single streaming pass (read, write) with no reduction, except the rare rows
+// whose target holds more than half of the mass: there 1 - p_t is summed from
+// the other terms (one extra read of the row) to keep its relative accuracy.
+// G lanes per row, chunks of G*K vectors.  The output may be the logits.
+template <int DT, int G, int K>
+__global__ void __launch_bounds__(256) lse_grad_kernel(Params p)
+{
+    constexpr int E = Traits<DT>::E;
+    constexpr int GPW = 64 / G;
+    constexpr int CH = G * K;
+    const int lane = threadIdx.x & 63;
+    const int lig = lane & (G - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nwaves = blockDim.x >> 6;
+    const int64_t row_step = (int64_t)gridDim.x * nwaves * GPW;
+    GroupRed<G> red;
+    for (int64_t rb = ((int64_t)blockIdx.x * nwaves + wave) * GPW; rb < p.M; rb += row_step) {
+        const int64_t row_l = rb + lane / G;
+        const bool active = row_l < p.M;
+        const int64_t row = active ? row_l : 0;
+        const Window w = row_window<DT>(p, row);
+        const int64_t t = active ? p.targets[row] : -1;
+        const TargetPos tp = target_pos<DT>(t, p.V, w.head);
+        const float lse = p.lse_in[row];
+        const float lseL = lse * kLog2e;
+        const float c = row_scale(p, row);
+        // 1 - p_t, accurately when the target dominates
+        const float xt = tp.valid ? load_logit<DT>(p, row, t) : 0.0f;
+        const float pt = fast_exp2(__builtin_fmaf(xt, kLog2e, -lseL));
+        const bool accurate = tp.valid && pt > 0.5f;
+        float gt = (pt - 1.0f) * c;
+        if (accurate) {
+            const float sx = red.sum_excl(
+                sum_without_target<DT>(p, w.xrow, lig, G, w.nvec, w.head, lseL, tp.vt, tp.jt));
+            gt = -sx * c;
+        }
+        // p = 2^(x log2e - lse log2e): the row max is replaced by lse (m = lse,
+        // log2 s = 0), which gives the same exponent
+        const EpiCoef<DT> ec = epi_coef<DT, EPI_GRAD>(lse, lseL, 0.0f, c);
+        for (int cb = 0; cb < w.nvec; cb += CH) {
+            Vec raw[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int v = cb + lig + G * k;
+                raw[k] = ldv(&w.xrow[v < w.nvec ? v : w.nvec - 1]);
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int v = cb + lig + G * k;
+                Vec g = epi_vec<DT, EPI_GRAD>(raw[k], ec);
+                if (v == tp.vt)
+                    set_elem<DT>(g, tp.jt, gt);
+                if (active && v < w.nvec)
+                    store_grad<DT>(w.yrow, v, g, w.head, p.V, p.aligned);
+            }
+        }
+    }
+}
+
 // ---- one row per workgroup, streamed in chunks ---------------------------------
-template <int DT, int W, int K, bool BWD>
+template <int DT, int W, int K, int OP>
 __global__ void __launch_bounds__(W * 64) stream_kernel(Params p)
 {
+    constexpr bool BWD = OP != EPI_NONE;
     constexpr int E = Traits<DT>::E;
     constexpr int NT = W * 64;
     constexpr int CH = NT * K;                  // vectors per chunk
@@ -1058,7 +1154,7 @@ __global__ void __launch_bounds__(W * 64) stream_kernel(Params p)
 
     for (int64_t row = blockIdx.x; row < p.M; row += gridDim.x) {
         const Window w = row_window<DT>(p, row);
-        const int64_t t = p.targets[row];
+        const int64_t t = p.targets ? p.targets[row] : -1;
         const TargetPos tp = target_pos<DT>(t, p.V, w.head);
 
         // pass 1: online (max, sum) per lane, rescaled once per chunk
@@ -1147,11 +1243,15 @@ __global__ void __launch_bounds__(W * 64) stream_kernel(Params p)
             for (int i = 1; i < W; ++i)
                 s_excl += s_exc[i];
         }
-        const RowResult rr = row_result(tp.valid, m, xt, et, s, s_excl, accurate, p.c);
+        const float c = row_scale(p, row);
+        const RowResult rr = row_result(tp.valid, m, xt, et, s, s_excl, accurate, c);
+        const float log2s = __log2f(s);
+        if (p.lse_out && tid == 0)
+            p.lse_out[row] = m + kLn2 * log2s;
 
         if constexpr (BWD) {
-            // pass 2: re-read the row and write the gradient over it
-            const GradCoef<DT> gc = grad_coef<DT>(m, mL, __log2f(s), p.c, p.log2c);
+            // pass 2: re-read the row and write the epilogue
+            const EpiCoef<DT> ec = epi_coef<DT, OP>(m, mL, log2s, c);
             for (int cb = 0; cb < w.nvec; cb += CH) {
                 Vec raw[K];
 #pragma unroll
@@ -1164,17 +1264,21 @@ __global__ void __launch_bounds__(W * 64) stream_kernel(Params p)
                 for (int k = 0; k < K; ++k) {
                     const int v = cb + tid + NT * k;
                     if (v < w.nvec) {
-                        const Vec g = grad_vec<DT>(raw[k], gc, v == tp.vt, tp.jt, rr.gt);
-                        store_grad<DT>(w.xrow, v, g, w.head, p.V, p.aligned);
+                        Vec g = epi_vec<DT, OP>(raw[k], ec);
+                        if (OP == EPI_GRAD && v == tp.vt)
+                            set_elem<DT>(g, tp.jt, rr.gt);
+                        store_grad<DT>(w.yrow, v, g, w.head, p.V, p.aligned);
                     }
                 }
             }
         }
         if (tid == 0) {
-            if (p.reduction == RED_NONE)
-                p.out[row] = rr.loss;
-            else
+            if (p.reduction == RED_NONE) {
+                if (p.out)
+                    p.out[row] = rr.loss;
+            } else {
                 acc += (double)rr.loss;
+            }
         }
         __syncthreads();   // s_xt and the LDS partials are reused by the next row
     }

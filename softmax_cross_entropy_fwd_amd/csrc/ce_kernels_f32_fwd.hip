@@ -1,6 +1,7 @@
-// fp32 kernel instances, and the M == 0 reduction kernel.
+// f32 kernel instances: forward.
 #define CE_DT DT_F32
-#define CE_GET_KERNEL get_kernel_f32
+#define CE_PART 0
+#define CE_GET_KERNEL get_kernel_f32_fwd
 #include "ce_kernels_inst.h"
 
 namespace cek {
@@ -13,4 +14,5 @@ __global__ void empty_reduce_kernel(float *out, float value)
 }
 
 const void *empty_reduce_fn() { return (const void *)&empty_reduce_kernel; }
+
 }  // namespace cek

@@ -119,3 +119,79 @@ def check_grads(got_bits, want_bits, dtype, c, want64=None):
 
 def host_grad_bits(t):
     return inputs.host_bits(t)
+
+
+# Row softmax: 16-bit outputs within GRAD_ULP units in the last place; fp32
+# outputs |d| <= 1e-5 |p| + 2^-125 (the floor is where the hardware exp2 may
+# flush a result below the normal range).
+# Log-softmax: the per-row loss bound (it is minus a row loss),
+# 1e-5 |y| + 4 ulp_fp32(max(|m|, |x|, 1)), plus one unit of the storage type
+# for 16-bit outputs.  Row log-sum-exps: 1e-5 (lse - m) + 4 ulp_fp32(max(|m|,
+# |lse|, 1)).
+
+
+def check_softmax(got_bits, want_bits, want64, dtype):
+    if dtype != "f32":
+        return check_grads(got_bits, want_bits, dtype, 1.0)
+    g = np.asarray(got_bits, dtype=np.float64)
+    w = np.asarray(want64, dtype=np.float64)
+    nan_w = np.isnan(w)
+    np.testing.assert_array_equal(np.isnan(g), nan_w)
+    err = np.abs(g - w)
+    err[nan_w] = 0
+    bound = 1e-5 * np.abs(np.where(nan_w, 0, w)) + 2.0 ** -125
+    bad = err > bound
+    assert not bad.any(), "fp32 softmax mismatch at %s: got %s want %s" % (
+        np.argwhere(bad)[:5].tolist(), g[bad][:5], w[bad][:5])
+
+
+def storage_ulp(values, dtype):
+    v = np.abs(np.asarray(values, dtype=np.float64))
+    v = np.where(np.isfinite(v), v, 0.0)
+    if dtype == "f32":
+        return np.spacing(v.astype(np.float32)).astype(np.float64)
+    if dtype == "f16":
+        return np.spacing(np.minimum(v, 65504).astype(np.float16)).astype(np.float64)
+    # bf16: 8 significant bits
+    e = np.floor(np.log2(np.maximum(v, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def check_log_softmax(got_bits, want64, xb, dtype):
+    g = widen(np.asarray(got_bits), dtype)
+    w = np.asarray(want64, dtype=np.float64)
+    x = widen(np.asarray(xb), dtype)
+    nan_w = np.isnan(w)
+    np.testing.assert_array_equal(np.isnan(g), nan_w)
+    inf_w = np.isinf(w)
+    np.testing.assert_array_equal(g[inf_w], w[inf_w])
+    fin = ~nan_w & ~inf_w
+    with np.errstate(invalid="ignore"):
+        m = np.max(x, axis=1, keepdims=True)
+    scale = np.maximum(np.abs(np.broadcast_to(m, x.shape)), np.abs(np.where(np.isfinite(x), x, 0)))
+    bound = 1e-5 * np.abs(w) + 4 * ulp32(scale)
+    if dtype != "f32":
+        bound = bound + storage_ulp(w, dtype)
+    with np.errstate(invalid="ignore"):
+        err = np.abs(np.where(fin, g, 0) - np.where(fin, w, 0))
+    bad = fin & (err > bound)
+    assert not bad.any(), "log-softmax mismatch at %s: got %s want %s" % (
+        np.argwhere(bad)[:5].tolist(), g[bad][:5], w[bad][:5])
+
+
+def check_lse(got, want, xb, dtype):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    nan_w = np.isnan(want)
+    np.testing.assert_array_equal(np.isnan(got), nan_w)
+    ok = ~nan_w & np.isfinite(want)
+    np.testing.assert_array_equal(got[~nan_w & ~ok], want[~nan_w & ~ok])
+    if not ok.any():
+        return
+    with np.errstate(invalid="ignore"):
+        m = np.max(widen(np.asarray(xb)[ok], dtype), axis=1)
+    bound = 1e-5 * np.abs(want[ok] - m) + 4 * ulp32(np.maximum(np.abs(m), np.abs(want[ok])))
+    err = np.abs(got[ok] - want[ok])
+    bad = err > bound
+    assert not bad.any(), "lse mismatch at rows %s: got %s want %s" % (
+        np.nonzero(ok)[0][bad][:5], got[ok][bad][:5], want[ok][bad][:5])

@@ -29,8 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("ce_fwd", "ce_fwd_bwd_inplace", "ce_workspace_bytes", "ce_status_string",
-              "ce_plan_describe"):
+    for n in ("ce_fwd", "ce_fwd_lse", "ce_fwd_bwd_inplace", "ce_bwd", "ce_softmax",
+              "ce_workspace_bytes", "ce_status_string", "ce_plan_describe"):
         assert n in names
 
 
@@ -98,6 +98,100 @@ def test_inplace_alias_checks(lib):
     assert call(lib, "ce_fwd_bwd_inplace", ws=FAKE + xb - 8) == ce.CE_ERR_ALIAS
 
 
+def test_forward_output_may_not_overlap_inputs(lib):
+    import softmax_cross_entropy_fwd_amd as ce
+    xb = 4 * 8 * 4
+    assert call(lib, "ce_fwd", out=FAKE + xb - 4) == ce.CE_ERR_ALIAS
+    assert call(lib, "ce_fwd", red=0, ws=0, ws_bytes=0, out=FAKE + 8) == ce.CE_ERR_ALIAS
+
+
+def call_lse(lib, lse=FAKE + 12288, **kw):
+    kw.setdefault("logits", FAKE)
+    kw.setdefault("targets", FAKE + 2048)
+    kw.setdefault("M", 4)
+    kw.setdefault("V", 8)
+    kw.setdefault("dtype", 0)
+    kw.setdefault("red", 1)
+    kw.setdefault("out", FAKE + 4096)
+    kw.setdefault("ws", FAKE + 8192 * 4)
+    kw.setdefault("ws_bytes", 1 << 20)
+    return lib.ce_fwd_lse(VP(kw["logits"]) if kw["logits"] else None,
+                          VP(kw["targets"]) if kw["targets"] else None, kw["M"], kw["V"],
+                          kw["dtype"], kw["red"], VP(kw["out"]) if kw["out"] else None,
+                          VP(lse) if lse else None, VP(kw["ws"]) if kw["ws"] else None,
+                          kw["ws_bytes"], None)
+
+
+def test_fwd_lse_argument_errors(lib):
+    import softmax_cross_entropy_fwd_amd as ce
+    assert call_lse(lib, lse=0) == ce.CE_ERR_NULL
+    assert call_lse(lib, lse=FAKE + 12290) == ce.CE_ERR_ALIGNMENT
+    assert call_lse(lib, lse=FAKE + 4096) == ce.CE_ERR_ALIAS            # on the loss output
+    assert call_lse(lib, lse=FAKE + 64) == ce.CE_ERR_ALIAS              # inside the logits
+    assert call_lse(lib, lse=FAKE + 2048 + 16) == ce.CE_ERR_ALIAS       # on the targets
+    assert call_lse(lib, dtype=7) == ce.CE_ERR_DTYPE
+    assert call_lse(lib, M=0, red=0, lse=0, logits=0, targets=0, out=0, ws=0,
+                    ws_bytes=0) == ce.CE_OK
+
+
+def call_bwd(lib, logits=FAKE, targets=FAKE + 2048, lse=FAKE + 3072, dloss=None, M=4, V=8,
+             dtype=0, red=1, grad=FAKE + 65536):
+    return lib.ce_bwd(VP(logits) if logits else None, VP(targets) if targets else None,
+                      VP(lse) if lse else None, VP(dloss) if dloss else None, M, V, dtype, red,
+                      VP(grad) if grad else None, None)
+
+
+def test_bwd_argument_errors(lib):
+    import softmax_cross_entropy_fwd_amd as ce
+    assert call_bwd(lib, dtype=3) == ce.CE_ERR_DTYPE
+    assert call_bwd(lib, red=9) == ce.CE_ERR_REDUCTION
+    assert call_bwd(lib, M=-2) == ce.CE_ERR_SHAPE
+    assert call_bwd(lib, V=0) == ce.CE_ERR_SHAPE
+    assert call_bwd(lib, logits=0) == ce.CE_ERR_NULL
+    assert call_bwd(lib, targets=0) == ce.CE_ERR_NULL
+    assert call_bwd(lib, lse=0) == ce.CE_ERR_NULL
+    assert call_bwd(lib, grad=0) == ce.CE_ERR_NULL
+    assert call_bwd(lib, lse=FAKE + 3073) == ce.CE_ERR_ALIGNMENT
+    assert call_bwd(lib, dloss=FAKE + 4098) == ce.CE_ERR_ALIGNMENT
+    # the gradient is written with the logits' 16-byte vectors
+    assert call_bwd(lib, grad=FAKE + 65536 + 4) == ce.CE_ERR_ALIGNMENT
+    assert call_bwd(lib, dtype=2, grad=FAKE + 65536 + 2) == ce.CE_ERR_ALIGNMENT
+    # a gradient that overlaps the logits without being them
+    assert call_bwd(lib, grad=FAKE + 16) == ce.CE_ERR_ALIAS
+    # a gradient over the targets, the lse or the upstream gradient
+    assert call_bwd(lib, grad=FAKE + 2048) == ce.CE_ERR_ALIAS
+    assert call_bwd(lib, grad=FAKE + 3072 - 64) == ce.CE_ERR_ALIAS
+    assert call_bwd(lib, dloss=FAKE + 65536 + 32) == ce.CE_ERR_ALIAS
+    # nothing to do for M == 0
+    assert call_bwd(lib, M=0, logits=0, targets=0, lse=0, grad=0) == ce.CE_OK
+
+
+def call_softmax(lib, logits=FAKE, M=4, V=8, dtype=0, log=0, out=FAKE + 65536, lse=None):
+    return lib.ce_softmax(VP(logits) if logits else None, M, V, dtype, log,
+                          VP(out) if out else None, VP(lse) if lse else None, None)
+
+
+def test_softmax_argument_errors(lib):
+    import softmax_cross_entropy_fwd_amd as ce
+    assert call_softmax(lib, dtype=3) == ce.CE_ERR_DTYPE
+    assert call_softmax(lib, V=0) == ce.CE_ERR_SHAPE
+    assert call_softmax(lib, logits=0) == ce.CE_ERR_NULL
+    assert call_softmax(lib, out=0) == ce.CE_ERR_NULL
+    assert call_softmax(lib, out=FAKE + 65536 + 8) == ce.CE_ERR_ALIGNMENT
+    assert call_softmax(lib, out=FAKE + 32) == ce.CE_ERR_ALIAS
+    assert call_softmax(lib, lse=FAKE + 65536 + 16) == ce.CE_ERR_ALIAS
+    assert call_softmax(lib, lse=FAKE + 16) == ce.CE_ERR_ALIAS
+    assert call_softmax(lib, out=FAKE, lse=FAKE + 64) == ce.CE_ERR_ALIAS   # in place
+    assert call_softmax(lib, M=0, logits=0, out=0) == ce.CE_OK
+
+
+def test_plan_describe_rejects_unknown_op(lib):
+    import softmax_cross_entropy_fwd_amd as ce
+    buf = ctypes.create_string_buffer(64)
+    assert lib.ce_plan_describe(4, 8, 0, 1, 5, buf, 64) == ce.CE_ERR_SHAPE
+    assert lib.ce_plan_describe(4, 8, 0, 1, -1, buf, 64) == ce.CE_ERR_SHAPE
+
+
 def test_workspace_bytes(lib):
     assert lib.ce_workspace_bytes(100, 1000, 0, 0) == 0         # none
     mean = lib.ce_workspace_bytes(100, 1000, 0, 1)
@@ -117,7 +211,7 @@ def test_status_strings(lib):
         seen.add(s)
     assert len(seen) == 9
     assert lib.ce_status_string(-99).decode() == "unknown status"
-    assert ce.ce_status_string(ce.CE_ERR_ALIAS).startswith("in-place")
+    assert "overlaps" in ce.ce_status_string(ce.CE_ERR_ALIAS)
 
 
 def test_binding_rejects_host_tensors():

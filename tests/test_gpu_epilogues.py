@@ -1,0 +1,329 @@
+"""GPU parity of the entry points built on the same row pass: the forward that
+saves each row's log-sum-exp (ce_fwd_lse), the backward from a saved
+log-sum-exp (ce_bwd), and row softmax / log-softmax (ce_softmax), against the
+fp64 oracle on seeded inputs that span several tiles and ragged tails, every
+plan shape, misaligned bases, in place and out of place.
+
+Tolerances (stated in gpu_util): gradients and 16-bit softmax within 2 ulps of
+the storage type; fp32 softmax 1e-5 relative; log-softmax and lse within the
+per-row loss bound; canaries around every written buffer exact.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from gpu_util import (check_grads, check_log_softmax, check_lse, check_row_losses,
+                      check_scalar, check_softmax, host_grad_bits, oracle, inputs, say)
+from test_gpu_parity import DTYPES, canaries_intact, place
+
+pytestmark = pytest.mark.gpu
+
+DCODE = {"f32": 0, "f16": 1, "bf16": 2}
+# One V per plan shape of each entry point (thresholds in 16-byte vectors:
+# 4, 8, 16, 32, 64, 128, 256, 512, 1024 for the register rows, the
+# workgroup kernel up to 16384, the streamed kernel above), with ragged
+# neighbours.
+V_SWEEP = [1, 2, 5, 8, 13, 31, 33, 64, 100, 127, 129, 255, 257, 500, 513, 1000, 1025, 2047,
+           4095, 4097, 8193, 16385, 50257, 65537, 131072, 131073]
+
+
+@pytest.fixture(scope="module")
+def ce():
+    import torch
+    assert torch.cuda.is_available(), "GPU test run without a GPU"
+    import softmax_cross_entropy_fwd_amd as ce
+    ce.load_library()
+    return ce
+
+
+def rows_for(V):
+    return 9 if V < 20000 else (4 if V < 100000 else 2)
+
+
+def out_buffer(like, offset, pad=24):
+    """An output buffer at the same 16-byte phase as `like`'s offset, with
+    canaries around it; returns (view, buffer)."""
+    import torch
+    from test_gpu_parity import CANARY
+    M, V = like.shape
+    buf = torch.empty(offset + M * V + pad, dtype=like.dtype, device="cuda:0")
+    bits_dtype = torch.int32 if like.dtype == torch.float32 else torch.int16
+    canary = CANARY[inputs.dtype_name(like)]
+    if bits_dtype == torch.int16 and canary >= 0x8000:
+        canary -= 0x10000
+    buf.view(bits_dtype).fill_(canary)
+    return buf[offset:offset + M * V].view(M, V), buf
+
+
+# ------------------------------------------------------------- ce_fwd_lse
+
+def fwd_lse_case(ce, dtype, M, V, sigma, seed, structure=None, reduction="mean", offset=0):
+    import torch
+    say("fwd_lse", dtype, M, V, sigma, seed, structure, reduction, offset)
+    x, t = inputs.make(dtype, M, V, sigma, seed, structure)
+    xb, tn = inputs.host_bits(x), t.numpy()
+    xg, buf = place(x, offset)
+    tg = t.to("cuda:0")
+    lse = torch.full((M + 2,), 7.0, dtype=torch.float32, device="cuda:0")
+    loss, _ = ce.ce_fwd_lse(xg, tg, reduction, lse=lse[1:M + 1])
+    plain = ce.ce_fwd(xg, tg, reduction)
+    torch.cuda.synchronize()
+    # the same kernels as ce_fwd: the loss is the same bits
+    assert torch.equal(loss.reshape(-1).view(torch.int32), plain.reshape(-1).view(torch.int32))
+    assert canaries_intact(buf, offset, M * V, dtype)
+    np.testing.assert_array_equal(inputs.host_bits(xg), xb)
+    got_lse = lse.cpu().numpy()
+    assert got_lse[0] == 7.0 and got_lse[M + 1] == 7.0
+    per_row, want_lse = oracle.loss_rows(xb, tn, dtype=dtype, with_lse=True)
+    check_lse(got_lse[1:M + 1], want_lse, xb, dtype)
+    if reduction == "none":
+        check_row_losses(loss.cpu().numpy(), per_row, xb, tn, dtype)
+    else:
+        check_scalar(loss.item(), oracle.reduce(per_row, reduction))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_fwd_lse_v_sweep(ce, dtype):
+    for V in V_SWEEP:
+        fwd_lse_case(ce, dtype, rows_for(V), V, 3.0, seed=V + 11, reduction="none")
+        fwd_lse_case(ce, dtype, rows_for(V), V, 3.0, seed=V + 12, reduction="mean",
+                     offset=V % 3)
+
+
+def test_fwd_lse_workloads_small_m(ce):
+    for name, M in (("tiny", 64), ("classifier", 70), ("lmhead", 6), ("stress", 150),
+                    ("skinny", 3001)):
+        c = inputs.CONFIGS[name]
+        fwd_lse_case(ce, c["dtype"], M, c["V"], c["sigma"], c["seed"], c["structure"],
+                     reduction="mean")
+
+
+def test_fwd_lse_wave_stream_shapes(ce, monkeypatch):
+    # the wave-per-row streaming forward writes lse too
+    for shape in ("wstream:1:2", "wstream:1:4", "wstream:1:8", "stream:8:4", "stream:16:4"):
+        monkeypatch.setenv("CE_FORCE_PLAN", shape)
+        for dtype in DTYPES:
+            for V in (5, 3000, 20000):
+                fwd_lse_case(ce, dtype, 11, V, 4.0, seed=V + 3, reduction="sum", offset=V % 2)
+
+
+# ----------------------------------------------------------------- ce_bwd
+
+def bwd_case(ce, dtype, M, V, sigma, seed, structure=None, reduction="mean", offset=0,
+             inplace=False, upstream=True, lse_from="oracle", targets=None):
+    import torch
+    say("bwd", dtype, M, V, sigma, seed, structure, reduction, offset, inplace, upstream,
+        lse_from)
+    x, t = inputs.make(dtype, M, V, sigma, seed, structure)
+    if targets is not None:
+        t = torch.as_tensor(targets, dtype=torch.int64)
+    xb, tn = inputs.host_bits(x), t.numpy()
+    xg, buf = place(x, offset)
+    tg = t.to("cuda:0")
+    if lse_from == "oracle":
+        _, lse64 = oracle.loss_rows(xb, tn, dtype=dtype, with_lse=True)
+        lse = torch.from_numpy(lse64.astype(np.float32)).to("cuda:0")
+    else:
+        _, lse = ce.ce_fwd_lse(xg, tg, "none")
+    rng = np.random.default_rng(seed)
+    d = None
+    dd = np.ones(M)
+    if upstream:
+        if reduction == "none":
+            dd = rng.uniform(-2.0, 2.0, size=M).astype(np.float32).astype(np.float64)
+            d = torch.from_numpy(dd.astype(np.float32)).to("cuda:0")
+        else:
+            d0 = float(np.float32(rng.uniform(0.25, 3.0) * rng.choice([-1, 1])))
+            dd = np.full(M, d0)
+            d = torch.tensor([d0], dtype=torch.float32, device="cuda:0")
+    if inplace:
+        gv, gbuf, goff = xg, buf, offset
+    else:
+        goff = offset + 16 // xg.element_size() * 3
+        gv, gbuf = out_buffer(xg, goff)
+    ce.ce_bwd(xg, tg, lse, reduction, dloss=d, grad=gv)
+    torch.cuda.synchronize()
+    assert canaries_intact(gbuf, goff, M * V, dtype), "wrote outside the gradient"
+    if not inplace:
+        np.testing.assert_array_equal(inputs.host_bits(xg), xb)   # logits untouched
+        assert canaries_intact(buf, offset, M * V, dtype)
+    c = 1.0 / M if reduction == "mean" else 1.0
+    want, want64 = oracle.grad_rows(xb, tn, dtype=dtype, c=c, d=dd, want64=True)
+    check_grads(host_grad_bits(gv), want, dtype, c * float(np.max(np.abs(dd))), want64)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_bwd_v_sweep(ce, dtype):
+    for V in V_SWEEP:
+        M = rows_for(V)
+        bwd_case(ce, dtype, M, V, 3.0, seed=V + 21, reduction="none", offset=V % 3)
+        bwd_case(ce, dtype, M, V, 3.0, seed=V + 22, reduction="mean", inplace=True)
+        bwd_case(ce, dtype, M, V, 3.0, seed=V + 23, reduction="sum", upstream=False,
+                 offset=(V // 3) % 4)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_bwd_after_fwd_lse(ce, dtype):
+    # the chain the split backward is for: lse from the library's own forward
+    for V in (7, 1000, 4096, 50257):
+        bwd_case(ce, dtype, rows_for(V) + 5, V, 2.0, seed=V + 31, reduction="mean",
+                 lse_from="library")
+        bwd_case(ce, dtype, rows_for(V), V, 2.0, seed=V + 32, reduction="none",
+                 lse_from="library", inplace=True, offset=1)
+
+
+def test_bwd_workloads_small_m(ce):
+    for name, M in (("tiny", 64), ("classifier", 40), ("lmhead", 4), ("stress", 120),
+                    ("skinny", 2000)):
+        c = inputs.CONFIGS[name]
+        bwd_case(ce, c["dtype"], M, c["V"], c["sigma"], c["seed"], c["structure"],
+                 reduction="mean", lse_from="library")
+
+
+def test_bwd_out_of_range_targets_and_dominant_rows(ce):
+    import torch
+    for dtype in DTYPES:
+        M, V = 6, 300
+        bwd_case(ce, dtype, M, V, 2.0, seed=5, reduction="none",
+                 targets=[0, -1, V, 7, 1 << 40, V - 1])
+        # p_t close to 1 in every row: 1 - p_t summed from the other terms
+        for V in (9, 1000, 50257):
+            for gap in (3.0, 12.0):
+                x, t = inputs.make(dtype, 8, V, 1.0, seed=int(gap) + V)
+                xf = x.float()
+                xf[torch.arange(8), t] = xf.max(dim=1).values + gap
+                xd = xf.to(x.dtype)
+                xb, tn = inputs.host_bits(xd), t.numpy()
+                _, lse64 = oracle.loss_rows(xb, tn, dtype=dtype, with_lse=True)
+                xg = xd.to("cuda:0")
+                g = ce.ce_bwd(xg, t.to("cuda:0"),
+                              torch.from_numpy(lse64.astype(np.float32)).to("cuda:0"), "sum")
+                torch.cuda.synchronize()
+                want, want64 = oracle.grad_rows(xb, tn, dtype=dtype, c=1.0, want64=True)
+                check_grads(host_grad_bits(g), want, dtype, 1.0, want64)
+
+
+def test_bwd_stress_rows(ce):
+    for dtype in DTYPES:
+        for V in (50257, 1000):
+            bwd_case(ce, dtype, 200, V, 8.0, seed=104, structure="stress", reduction="mean",
+                     lse_from="library", offset=1)
+
+
+# -------------------------------------------------------------- ce_softmax
+
+def softmax_case(ce, dtype, M, V, sigma, seed, structure=None, log=False, offset=0,
+                 inplace=False, want_lse=True, x=None):
+    import torch
+    say("softmax", dtype, M, V, sigma, seed, structure, log, offset, inplace)
+    if x is None:
+        x, _ = inputs.make(dtype, M, V, sigma, seed, structure)
+    xb = inputs.host_bits(x)
+    xg, buf = place(x, offset)
+    lse = torch.full((M + 2,), 7.0, dtype=torch.float32, device="cuda:0") if want_lse else None
+    if inplace:
+        yv, ybuf, yoff = xg, buf, offset
+    else:
+        yoff = offset + 16 // xg.element_size() * 5
+        yv, ybuf = out_buffer(xg, yoff)
+    ce.ce_softmax(xg, log_softmax=log, out=yv, lse=lse[1:M + 1] if want_lse else None)
+    torch.cuda.synchronize()
+    assert canaries_intact(ybuf, yoff, M * V, dtype), "wrote outside the output"
+    if not inplace:
+        np.testing.assert_array_equal(inputs.host_bits(xg), xb)
+        assert canaries_intact(buf, offset, M * V, dtype)
+    want, want64, lse64 = oracle.softmax_rows(xb, dtype=dtype, log=log, want64=True,
+                                              with_lse=True)
+    got = host_grad_bits(yv)
+    if log:
+        check_log_softmax(got, want64, xb, dtype)
+    else:
+        check_softmax(got, want, want64, dtype)
+    if want_lse:
+        got_lse = lse.cpu().numpy()
+        assert got_lse[0] == 7.0 and got_lse[M + 1] == 7.0
+        check_lse(got_lse[1:M + 1], lse64, xb, dtype)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("log", [False, True])
+def test_softmax_v_sweep(ce, dtype, log):
+    for V in V_SWEEP:
+        M = rows_for(V)
+        softmax_case(ce, dtype, M, V, 3.0, seed=V + 41, log=log, offset=V % 3)
+        softmax_case(ce, dtype, M, V, 3.0, seed=V + 42, log=log, inplace=True,
+                     want_lse=False)
+
+
+@pytest.mark.parametrize("log", [False, True])
+def test_softmax_workloads_and_stress(ce, log):
+    for name, M in (("tiny", 64), ("classifier", 50), ("lmhead", 4), ("stress", 200),
+                    ("skinny", 2500)):
+        c = inputs.CONFIGS[name]
+        softmax_case(ce, c["dtype"], M, c["V"], c["sigma"], c["seed"], c["structure"], log=log,
+                     offset=1 if name == "stress" else 0)
+
+
+def test_softmax_degenerate_rows(ce):
+    import torch
+    for dtype in DTYPES:
+        for V in (1, 6, 1000, 20000):
+            # V = 1: softmax 1, log-softmax 0; an all -inf row: NaN
+            x, _ = inputs.make(dtype, 4, V, 2.0, seed=V)
+            x[1] = -math.inf
+            x[2] = 3.5
+            for log in (False, True):
+                softmax_case(ce, dtype, 4, V, 0, 0, log=log, x=x.clone())
+
+
+def test_every_softmax_and_grad_shape(ce, monkeypatch):
+    # the shapes the plan table gives softmax, log-softmax and the fused backward
+    for shape, cap in (("rows:1:1", 1), ("rows:1:2", 2), ("rows:1:4", 4), ("rows:2:4", 8),
+                       ("rows:4:4", 16), ("rows:4:8", 32), ("rows:16:4", 64),
+                       ("rows:32:4", 128), ("rows:64:4", 256), ("rows:64:8", 512),
+                       ("rows:64:16", 1024), ("wg:16:4", 4096), ("wg:16:8", 8192),
+                       ("wg:16:12", 12288), ("wg:16:16", 16384), ("stream:8:4", 1 << 30),
+                       ("stream:16:4", 1 << 30)):
+        monkeypatch.setenv("CE_FORCE_PLAN", shape)
+        for dtype in DTYPES:
+            E = 4 if dtype == "f32" else 8
+            for V in (3, 4 * E + 1, 64 * E, 3000, 20000):
+                if (V + 2 * E - 2) // E > cap:
+                    continue
+                M = 13 if V < 4000 else 5
+                for op in (ce.CE_OP_SOFTMAX, ce.CE_OP_LOG_SOFTMAX):
+                    plan = ce.ce_plan_describe(M, V, DCODE[dtype], "none", op=op)
+                    if V % E == 0:
+                        assert plan.startswith(shape), (plan, shape)
+                softmax_case(ce, dtype, M, V, 4.0, seed=V + 51, log=False, offset=V % 2)
+                softmax_case(ce, dtype, M, V, 4.0, seed=V + 52, log=True, inplace=True)
+
+
+def test_empty_batches(ce):
+    import torch
+    for dtype in DTYPES:
+        x = torch.empty(0, 10, dtype=inputs.TORCH_DTYPE[dtype], device="cuda:0")
+        t = torch.empty(0, dtype=torch.int64, device="cuda:0")
+        loss, lse = ce.ce_fwd_lse(x, t, "mean")
+        assert math.isnan(loss.item()) and lse.numel() == 0
+        lse0 = torch.empty(0, dtype=torch.float32, device="cuda:0")
+        assert ce.ce_bwd(x, t, lse0, "mean").numel() == 0
+        assert ce.ce_softmax(x).numel() == 0
+        assert ce.ce_softmax(x, log_softmax=True, lse=lse0).numel() == 0
+
+
+def test_fused_and_split_backward_agree(ce):
+    import torch
+    # both are checked against the oracle elsewhere; here the two library
+    # paths on the same rows stay within the gradient tolerance of each other
+    for dtype in DTYPES:
+        for V in (1000, 4096, 50257):
+            x, t = inputs.make(dtype, 16, V, 3.0, seed=V + 61, device="cuda:0")
+            _, lse = ce.ce_fwd_lse(x, t, "mean")
+            g = ce.ce_bwd(x, t, lse, "mean")
+            y = x.clone()
+            ce.ce_fwd_bwd_inplace(y, t, "mean")
+            torch.cuda.synchronize()
+            check_grads(host_grad_bits(g), host_grad_bits(y), dtype, 1.0 / 16,
+                        inputs.host_bits(y).astype(np.float64) if dtype == "f32" else None)

@@ -374,3 +374,148 @@ def test_grad_rounding_fp16_subnormals():
     np.testing.assert_array_equal(g16, want)
     sub = (g16 & 0x7c00) == 0
     assert sub.mean() > 0.5
+
+
+# ------------------------------------------------ softmax, log-softmax, dloss
+
+def test_log_softmax_worked_example(golden_dir):
+    # log_softmax at the target is minus the loss the page prints (1.407, cut
+    # to three decimals); softmax there is exp(-loss)
+    g = json.load(open(os.path.join(golden_dir, "worked_example.json")))
+    x = f32([g["logits"]])
+    t = g["target"]
+    step = 10.0 ** -g["printed_decimals"]
+    _, ls = oracle.softmax_rows(x, log=True, want64=True)
+    assert 0 <= -float(ls[0, t]) - g["printed"]["loss"] < step
+    # softmax of the max logit is 1 / (the page's shifted sum)
+    _, sm = oracle.softmax_rows(x, want64=True)
+    assert 0 <= 1.0 / float(sm[0, 2]) - g["printed"]["sum_exp_shifted"] < step
+    getcontext().prec = 50
+    e = [Decimal(v).exp() for v in g["logits"]]
+    for j in range(3):
+        exact = e[j] / (e[0] + e[1] + e[2])
+        assert abs(float(sm[0, j]) - float(exact)) <= 1e-15 * float(exact)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_softmax_uniform_rows_closed_form(golden_dir, dtype):
+    # all-equal rows: softmax 1/V, log-softmax -ln V (the uniform-row closed form)
+    g = json.load(open(os.path.join(golden_dir, "uniform_rows.json")))
+    for case in g["cases"]:
+        V = case["V"]
+        row = np.full((2, V), 3.25, dtype=np.float32)
+        x = row if dtype == "f32" else _to_bits(row, dtype)
+        _, p = oracle.softmax_rows(x, dtype=dtype, want64=True)
+        np.testing.assert_allclose(p, 1.0 / V, rtol=1e-14)
+        _, lp = oracle.softmax_rows(x, dtype=dtype, log=True, want64=True)
+        np.testing.assert_allclose(lp, -case["loss"], rtol=1e-14)
+
+
+def test_softmax_two_classes_is_sigmoid():
+    a = RNG.uniform(-20, 20, size=50)
+    x = f32(np.stack([a, np.zeros_like(a)], axis=1))
+    _, p = oracle.softmax_rows(x, want64=True)
+    xa = x[:, 0].astype(np.float64)
+
+    def sig(z):
+        return np.where(z >= 0, 1 / (1 + np.exp(-np.abs(z))), np.exp(-np.abs(z)) / (1 + np.exp(-np.abs(z))))
+    np.testing.assert_allclose(p[:, 0], sig(xa), rtol=1e-14)
+    np.testing.assert_allclose(p[:, 1], sig(-xa), rtol=1e-14)
+
+
+def test_softmax_rows_invariants():
+    x = f32(RNG.normal(size=(20, 257)) * 6)
+    x[3, 10] = -np.inf
+    _, p, lse = oracle.softmax_rows(x, want64=True, with_lse=True)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=1e-14)
+    assert p[3, 10] == 0.0
+    _, lp = oracle.softmax_rows(x, log=True, want64=True)
+    assert lp[3, 10] == -np.inf
+    fin = np.isfinite(lp)
+    np.testing.assert_allclose(np.exp(lp[fin]), p[fin], rtol=1e-13)
+    # shift invariance on an exact shift (2^-4 grid plus a power of two)
+    xs = f32(np.round(x * 16) / 16)
+    _, a = oracle.softmax_rows(xs, want64=True)
+    _, b = oracle.softmax_rows(xs + np.float32(64.0), want64=True)
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-300)
+    # lse is the loss plus the target logit, for any target
+    t = RNG.integers(0, 257, size=20)
+    t[3] = 0
+    loss, lse2 = oracle.loss_rows(x, t, with_lse=True)
+    np.testing.assert_allclose(lse, lse2, rtol=0)
+
+
+def test_softmax_all_minus_inf_row_is_nan():
+    x = f32([[-np.inf] * 4, [0.0, 1.0, -np.inf, 2.0]])
+    _, p = oracle.softmax_rows(x, want64=True)
+    assert np.isnan(p[0]).all() and np.isfinite(p[1]).all()
+    _, lp = oracle.softmax_rows(x, log=True, want64=True)
+    assert np.isnan(lp[0]).all()
+
+
+@pytest.mark.parametrize("name,rows", [("classifier", 16), ("lmhead", 2), ("stress", 40)])
+def test_softmax_against_torch_float64(name, rows):
+    c = inputs.CONFIGS[name]
+    x, _ = inputs.make(c["dtype"], rows, c["V"], c["sigma"], c["seed"], c["structure"])
+    xb, dt = inputs.host_bits(x), c["dtype"]
+    w = torch.from_numpy(_widen_all(xb, dt))
+    _, p = oracle.softmax_rows(xb, dtype=dt, want64=True)
+    np.testing.assert_allclose(p, torch.softmax(w, dim=1).numpy(), rtol=1e-12, atol=1e-300)
+    _, lp = oracle.softmax_rows(xb, dtype=dt, log=True, want64=True)
+    ref = torch.log_softmax(w, dim=1).numpy()
+    fin = np.isfinite(ref)
+    np.testing.assert_array_equal(np.isfinite(lp), fin)
+    np.testing.assert_allclose(lp[fin], ref[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_softmax_fp16_rounding_is_one_step():
+    # numpy converts float64 to float16 directly (one round to nearest even)
+    x = f32(RNG.normal(size=(6, 300)) * 3)
+    y, y64 = oracle.softmax_rows(x, out_dtype="f16", want64=True)
+    np.testing.assert_array_equal(y, y64.astype(np.float16).view(np.uint16))
+    y, y64 = oracle.softmax_rows(x, out_dtype="f16", log=True, want64=True)
+    np.testing.assert_array_equal(y, y64.astype(np.float16).view(np.uint16))
+
+
+@pytest.mark.parametrize("V", [1, 2, 3, 5, 8])
+def test_softmax_brute_force_small(V):
+    specials = [0.0, 1.0, -1.0, 80.0, -80.0, 1e4, -1e4, -np.inf, 3.0]
+    for trial in range(40):
+        if trial % 3 == 0:
+            row = list(RNG.choice(specials, size=V))
+        else:
+            row = list(RNG.normal(size=V) * RNG.choice([1e-3, 1.0, 30.0]))
+        row = [float(np.float32(v)) for v in row]
+        if all(v == -math.inf for v in row):
+            row[0] = 0.0
+        x = f32([row])
+        lse = _brute_lse(row)
+        _, p = oracle.softmax_rows(x, want64=True)
+        _, lp = oracle.softmax_rows(x, log=True, want64=True)
+        for j in range(V):
+            if row[j] == -math.inf:
+                assert p[0, j] == 0.0 and lp[0, j] == -math.inf
+                continue
+            want = Decimal(row[j]) - lse
+            assert lp[0, j] == pytest.approx(float(want), rel=1e-13, abs=1e-13 * max(1.0, abs(row[j]))), (row, j)
+            assert p[0, j] == pytest.approx(float(want.exp()), rel=1e-12, abs=1e-300), (row, j)
+
+
+@pytest.mark.parametrize("reduction", ["none", "mean", "sum"])
+def test_grad_with_upstream_gradient_matches_autograd(reduction):
+    M, V = 9, 131
+    x = f32(RNG.normal(size=(M, V)) * 3)
+    t = RNG.integers(0, V, size=M)
+    w = torch.from_numpy(x.astype(np.float64)).requires_grad_(True)
+    loss = F.cross_entropy(w, torch.from_numpy(t), reduction=reduction)
+    if reduction == "none":
+        d = RNG.uniform(-2, 2, size=M)
+        loss.backward(torch.from_numpy(d))
+        dd = d
+    else:
+        d0 = -0.37
+        loss.backward(torch.tensor(d0, dtype=torch.float64))
+        dd = np.full(M, d0)
+    c = 1.0 / M if reduction == "mean" else 1.0
+    _, g = oracle.grad_rows(x, t, c=c, d=dd, want64=True)
+    np.testing.assert_allclose(g, w.grad.numpy(), rtol=1e-12, atol=1e-16)
