@@ -16,8 +16,12 @@ GB/s = bytes the method must move / kernel time.  The same line carries:
                 when a summary taken on the current kernel source is committed
                 under profiles/;
   cpu_baseline  the fp64 oracle timed on the host cores over the whole workload;
-  also          the LM-head workload (bf16 [16384, 131072]) forward and fused
-                forward + in-place backward, timed the same way.
+  also          the LM-head workload (bf16 [16384, 131072]) forward, fused
+                forward + in-place backward, split backward from a saved
+                log-sum-exp and row softmax; the classifier's split backward
+                and softmax; the stress (fp16 [8192, 50257], misaligned rows)
+                forward and fused backward; the skinny (fp32 [1048576, 128])
+                forward; each timed the same way.
 
 Inputs rotate over enough buffers (>= 1 GiB in total) that no launch finds its
 rows in the 256 MB last-level cache; the in-place backward restores its logits
@@ -38,13 +42,24 @@ ELEM = {"f32": 4, "f16": 2, "bf16": 2}
 
 
 def alg_bytes(M, V, dtype, op, reduction):
-    """Bytes the method must move: logits read (and gradient written), int64
-    targets read, the output written."""
+    """Bytes the method must move: logits read (and the gradient or softmax
+    written), int64 targets read, losses / log-sum-exps written or read."""
     s = ELEM[dtype]
     out = 4 * M if reduction == "none" else 4
     if op == "fwd":
         return M * V * s + 8 * M + out
-    return 2 * M * V * s + 8 * M + out
+    if op == "fwd_lse":
+        return M * V * s + 8 * M + out + 4 * M
+    if op == "fwd_bwd":
+        return 2 * M * V * s + 8 * M + out
+    if op == "bwd":                       # logits, targets, lse in; gradient out
+        return 2 * M * V * s + 8 * M + 4 * M
+    if op in ("softmax", "log_softmax"):
+        return 2 * M * V * s
+    raise ValueError(op)
+
+
+OPS = ["fwd", "fwd_lse", "fwd_bwd", "bwd", "softmax", "log_softmax"]
 
 
 def kernel_source_hash():
@@ -157,19 +172,34 @@ def time_workload(ce, workload, op, reduction, steps, warmup, log):
     dev = torch.device("cuda:0")
     x0, t = inputs.make_config(workload, device=dev)
     nbytes = x0.numel() * x0.element_size()
-    nbuf = max(1, -(-(1 << 30) // nbytes)) if op == "fwd" else 1
+    # read-only ops rotate over >= 1 GiB of inputs; the others write a buffer
+    # as large as the logits, which already exceeds the last-level cache
+    nbuf = max(1, -(-(1 << 30) // nbytes)) if op in ("fwd", "fwd_lse") else 1
     xs = [x0] + [x0.clone() for _ in range(nbuf - 1)]
     pristine = x0.clone() if op == "fwd_bwd" else None
-    fn = ce.ce_fwd if op == "fwd" else ce.ce_fwd_bwd_inplace
     out = torch.empty((M,) if reduction == "none" else (), dtype=torch.float32, device=dev)
+    lse = torch.empty(M, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x0) if op in ("bwd", "softmax", "log_softmax") else None
+    if op == "bwd":
+        ce.ce_fwd_lse(x0, t, reduction, lse=lse)
+    launch = {
+        "fwd": lambda x: ce.ce_fwd(x, t, reduction, out=out),
+        "fwd_lse": lambda x: ce.ce_fwd_lse(x, t, reduction, out=out, lse=lse),
+        "fwd_bwd": lambda x: ce.ce_fwd_bwd_inplace(x, t, reduction, out=out),
+        "bwd": lambda x: ce.ce_bwd(x, t, lse, reduction, grad=y),
+        "softmax": lambda x: ce.ce_softmax(x, out=y),
+        "log_softmax": lambda x: ce.ce_softmax(x, log_softmax=True, out=y),
+    }[op]
+    code = {"fwd": ce.CE_OP_FWD, "fwd_lse": ce.CE_OP_FWD, "fwd_bwd": ce.CE_OP_FWD_BWD,
+            "bwd": ce.CE_OP_BWD, "softmax": ce.CE_OP_SOFTMAX,
+            "log_softmax": ce.CE_OP_LOG_SOFTMAX}[op]
     stream = torch.cuda.current_stream(dev)
-    plan = ce.ce_plan_describe(M, V, {"f32": 0, "f16": 1, "bf16": 2}[dtype], reduction,
-                               op == "fwd_bwd")
+    plan = ce.ce_plan_describe(M, V, {"f32": 0, "f16": 1, "bf16": 2}[dtype], reduction, op=code)
     log("workload %s op %s reduction %s plan %s buffers %d" % (workload, op, reduction, plan, nbuf))
     for i in range(warmup):
         if pristine is not None:
             xs[0].copy_(pristine)
-        fn(xs[i % nbuf], t, reduction, out=out)
+        launch(xs[i % nbuf])
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -179,13 +209,14 @@ def time_workload(ce, workload, op, reduction, steps, warmup, log):
         if pristine is not None:
             xs[0].copy_(pristine)
         starts[i].record(stream)
-        fn(xs[i % nbuf], t, reduction, out=out)
+        launch(xs[i % nbuf])
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_ms = sum(ms) / len(ms)
     ab = alg_bytes(M, V, dtype, op, reduction)
+    has_loss = op in ("fwd", "fwd_lse", "fwd_bwd") and reduction != "none"
     res = {
         "workload": workload, "op": op, "reduction": reduction, "M": M, "V": V,
         "storage": dtype, "plan": plan,
@@ -194,12 +225,12 @@ def time_workload(ce, workload, op, reduction, steps, warmup, log):
         "alg_bytes_per_launch": ab,
         "alg_GBps": ab / (avg_ms * 1e-3) / 1e9,
         "rows_per_s": M / (avg_ms * 1e-3),
-        "loss": float(out.float().mean().item()) if reduction != "none" else None,
+        "loss": float(out.float().mean().item()) if has_loss else None,
     }
     res["frac_of_peak"] = res["alg_GBps"] / PEAK_GBS
     log("  %.4f ms/launch (min %.4f), %.1f GB/s = %.1f%% of 8 TB/s, %.3g rows/s" % (
         avg_ms, min(ms), res["alg_GBps"], 100 * res["frac_of_peak"], res["rows_per_s"]))
-    del xs, pristine, x0
+    del xs, pristine, x0, y
     torch.cuda.empty_cache()
     return res
 
@@ -244,9 +275,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="classifier")
-    ap.add_argument("--op", default=None, choices=[None, "fwd", "fwd_bwd"])
+    ap.add_argument("--op", default=None, choices=[None] + OPS)
     ap.add_argument("--reduction", default=None, choices=[None, "mean", "none", "sum"])
-    ap.add_argument("--no-extra", action="store_true", help="skip the LM-head lines")
+    ap.add_argument("--no-extra", action="store_true", help="skip the extra lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -294,16 +325,18 @@ def main():
     head = time_workload(ce, args.workload, op, red, args.steps, args.warmup, log)
     also = []
     if not args.no_extra and args.workload == "classifier":
-        for eop in ("fwd", "fwd_bwd"):
-            also.append(time_workload(ce, "lmhead", eop, "mean", max(20, args.steps // 5),
+        for wl, eop in (("lmhead", "fwd"), ("lmhead", "fwd_bwd"), ("lmhead", "bwd"),
+                        ("lmhead", "softmax"), ("classifier", "bwd"), ("classifier", "softmax"),
+                        ("stress", "fwd"), ("stress", "fwd_bwd"), ("skinny", "fwd")):
+            also.append(time_workload(ce, wl, eop, "mean", max(20, args.steps // 5),
                                       max(3, args.warmup // 5), log))
     traffic = load_traffic(args.workload, op, red)
     cpu = None if args.no_cpu else cpu_baseline(args.workload, op, red, log)
 
     line = {
         "metric": "CE %s HBM GB/s (algorithmic bytes / kernel time), %s %dx%d %s"
-                  % ("fwd" if op == "fwd" else "fused fwd+bwd", args.workload, c["M"], c["V"],
-                     c["dtype"]),
+                  % ({"fwd": "fwd", "fwd_bwd": "fused fwd+bwd"}.get(op, op), args.workload,
+                     c["M"], c["V"], c["dtype"]),
         "value": round(head["alg_GBps"], 2),
         "unit": "GB/s",
         "n_gpus": 1,

@@ -37,18 +37,14 @@ struct Plan {
 
 KernelRef lookup(int dtype, int op, int kind, int a, int b, bool exact, int nbuf)
 {
-    const bool fwd = op == cek::EPI_NONE;
-    switch (dtype) {
-    case CE_F32:
-        return fwd ? cek::get_kernel_f32_fwd(op, kind, a, b, exact, nbuf)
-                   : cek::get_kernel_f32_epi(op, kind, a, b, exact, nbuf);
-    case CE_F16:
-        return fwd ? cek::get_kernel_f16_fwd(op, kind, a, b, exact, nbuf)
-                   : cek::get_kernel_f16_epi(op, kind, a, b, exact, nbuf);
-    default:
-        return fwd ? cek::get_kernel_bf16_fwd(op, kind, a, b, exact, nbuf)
-                   : cek::get_kernel_bf16_epi(op, kind, a, b, exact, nbuf);
-    }
+    using Fn = KernelRef (*)(int, int, int, int, bool, int);
+    static const Fn table[3][3] = {
+        {cek::get_kernel_f32_fwd, cek::get_kernel_f32_grad, cek::get_kernel_f32_aux},
+        {cek::get_kernel_f16_fwd, cek::get_kernel_f16_grad, cek::get_kernel_f16_aux},
+        {cek::get_kernel_bf16_fwd, cek::get_kernel_bf16_grad, cek::get_kernel_bf16_aux},
+    };
+    const int part = op == cek::EPI_NONE ? 0 : op == cek::EPI_GRAD ? 1 : 2;
+    return table[dtype][part](op, kind, a, b, exact, nbuf);
 }
 
 // Vectors one tile of a shape covers (0 for the stream kernels: any row).
@@ -188,43 +184,30 @@ int64_t window_vectors(int64_t V, int E, bool aligned)
     return aligned ? V / E : (V + 2 * E - 2) / E;
 }
 
-// The split backward streams each row once (chunks of G*4 vectors per G
-// lanes): a few lanes per row for short rows, a whole wave for long ones.
-void choose_lse_grad_shape(int64_t nvec, int *a, int *b)
-{
-    *a = nvec <= 16 ? 4 : nvec <= 64 ? 16 : 64;
-    *b = 4;
-}
-
 int make_plan(int64_t M, int64_t V, int dtype, int op, bool aligned, Plan *plan)
 {
     const int E = 16 / (int)elem_size(dtype);
     const int64_t nvec = window_vectors(V, E, aligned);
     int kind = 0, a = 0, b = 0, nbuf = 1;
-    if (op == cek::EPI_LSE_GRAD) {
-        kind = cek::KIND_ROWS;
-        choose_lse_grad_shape(nvec, &a, &b);
-    } else {
-        choose_shape(nvec, op != cek::EPI_NONE, &kind, &a, &b, &nbuf);
-        int fk, fa, fb;
-        if (forced_shape(&fk, &fa, &fb)) {
-            const int64_t tile = tile_vectors(fk, fa, fb);
-            if (lookup(dtype, op, fk, fa, fb, false, 1).fn &&
-                (fk == cek::KIND_STREAM || fk == cek::KIND_WSTREAM || tile >= nvec)) {
-                kind = fk;
-                a = fa;
-                b = fb;
-                nbuf = 1;
-            }
+    choose_shape(nvec, op != cek::EPI_NONE, &kind, &a, &b, &nbuf);
+    int fk, fa, fb;
+    if (forced_shape(&fk, &fa, &fb)) {
+        const int64_t tile = tile_vectors(fk, fa, fb);
+        if (lookup(dtype, op, fk, fa, fb, false, 1).fn &&
+            (fk == cek::KIND_STREAM || fk == cek::KIND_WSTREAM || tile >= nvec)) {
+            kind = fk;
+            a = fa;
+            b = fb;
+            nbuf = 1;
         }
     }
     plan->kind = kind;
     plan->a = a;
     plan->b = b;
-    plan->exact = op != cek::EPI_LSE_GRAD && aligned && tile_vectors(kind, a, b) == nvec;
+    plan->exact = aligned && tile_vectors(kind, a, b) == nvec;
     plan->nbuf = kind == cek::KIND_ROWS ? nbuf : 1;
     const char *nb = std::getenv("CE_FORCE_NBUF");
-    if (kind == cek::KIND_ROWS && op != cek::EPI_LSE_GRAD && nb &&
+    if (kind == cek::KIND_ROWS && nb &&
         (std::atoi(nb) == 1 || std::atoi(nb) == 2 || std::atoi(nb) == 17 || std::atoi(nb) == 18))
         plan->nbuf = std::atoi(nb);
     plan->k = lookup(dtype, op, kind, a, b, plan->exact, plan->nbuf);
@@ -249,12 +232,10 @@ int make_plan(int64_t M, int64_t V, int dtype, int op, bool aligned, Plan *plan)
     int64_t needed = (M + rows_per_wg - 1) / rows_per_wg;
     // Few deep waves beat many shallow ones here (measured): each wave keeps
     // a whole row of loads in flight, so the rows kernel runs 4 waves per CU
-    // and the workgroup kernels 16.  The split backward has only one chunk
-    // of loads in flight per lane and wants more waves.
+    // and the workgroup kernels 16.
     const int waves_per_wg = plan->k.block / 64;
     const char *tw = std::getenv("CE_WAVES_PER_CU");
     const int target_waves = (tw && std::atoi(tw) > 0) ? std::atoi(tw)
-                             : op == cek::EPI_LSE_GRAD ? 32
                              : kind == cek::KIND_ROWS  ? 4
                                                        : 16;
     int wg_per_cu = target_waves / waves_per_wg;
@@ -408,12 +389,17 @@ int run(const Call &c, void *stream)
     p.aligned = aligned ? 1 : 0;
     const char *map = std::getenv("CE_ROW_MAP");
     p.blocked = (map && !std::strcmp(map, "blocked")) ? 1 : 0;
-    // the split backward takes its reduction only for the gradient scale
-    p.reduction = c.op == cek::EPI_LSE_GRAD ? c.reduction : reduction;
+    // Only calls that compute losses reduce them (and have a workspace); the
+    // split backward uses its reduction for the gradient scale and the shape
+    // of dloss alone.
+    p.reduction = reduction;
+    if (reduction != CE_NONE && (!p.ticket || !p.partials))
+        return CE_ERR_WORKSPACE;
     const double scale = c.reduction == CE_MEAN ? 1.0 / (double)c.M : 1.0;
     p.c = (float)scale;
     p.out_scale = scale;
     p.dloss = c.dloss;
+    p.dloss_per_row = c.reduction == CE_NONE ? 1 : 0;
     p.lse_out = c.lse_out;
     p.lse_in = c.lse_in;
     void *args[] = {&p};

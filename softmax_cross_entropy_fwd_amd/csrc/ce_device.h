@@ -38,8 +38,10 @@ namespace cek {
 
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 enum : int { RED_NONE = 0, RED_MEAN = 1, RED_SUM = 2 };
-// What the kernels write over (or next to) the row once its log-sum-exp is known.
-enum : int { EPI_NONE = 0, EPI_GRAD = 1, EPI_SOFTMAX = 2, EPI_LOGSOFTMAX = 3 };
+// What the kernels write over (or next to) the row once its log-sum-exp is
+// known.  EPI_LSE_GRAD is the gradient from a log-sum-exp given per row (no
+// reduction pass).
+enum : int { EPI_NONE = 0, EPI_GRAD = 1, EPI_SOFTMAX = 2, EPI_LOGSOFTMAX = 3, EPI_LSE_GRAD = 4 };
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
@@ -64,7 +66,8 @@ struct Params {
     float c;                 // gradient scale (1/M for mean, 1 otherwise)
     double out_scale;        // 1/M (mean) or 1 (sum)
     Vec *y;                  // epilogue output, same 16-byte phase as x (== x in place)
-    const float *dloss;      // upstream gradient, [M] (none) or [1]; null means 1
+    const float *dloss;      // upstream gradient, [M] or [1] (see dloss_per_row); null means 1
+    int dloss_per_row;       // dloss holds one value per row
     float *lse_out;          // optional [M] row log-sum-exps
     const float *lse_in;     // [M] given log-sum-exps (backward from saved statistics)
 };
@@ -696,7 +699,7 @@ __device__ __forceinline__ float row_scale(const Params &p, int64_t row)
 {
     if (!p.dloss)
         return p.c;
-    return p.c * p.dloss[p.reduction == RED_NONE ? row : 0];
+    return p.c * p.dloss[p.dloss_per_row ? row : 0];
 }
 
 // Row state carried by the register pipeline: the row in raw[] was loaded
@@ -705,6 +708,8 @@ struct RowRef {
     int64_t row;     // the row held (clamped to a real row for idle lanes)
     bool active;     // this lane's row is a real row
     int64_t t;       // its target, -1 for idle lanes
+    float c;         // gradient scale of the row (gradient epilogues)
+    float lse;       // given log-sum-exp (EPI_LSE_GRAD)
     Window w;
 };
 
@@ -727,41 +732,48 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
     const float xt = tp.valid ? load_logit<DT>(p, cur.row, cur.t) : __builtin_nanf("");
     const bool masked = !EXACT && !p.aligned;
 
-    // One pass: each vector is folded into the lane's running (max, sum) as
-    // it arrives -- the sum is rescaled by 2^((m_old - m_new) log2 e) when the
-    // max grows -- and (forward) its registers are refilled at once with the
-    // next row's vector.
-    float m_run = -__builtin_inff();
-    float s_run = 0.0f;
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const int v = lidx + STRIDE * k;
-        Vec x = raw[k];
-        if (masked) {
-            if (k == 0 && lidx == 0 && w.head > 0)
-                mask_outside<DT>(x, w.head, E);
-            if (k + 1 >= kfull && v >= w.nvec - 1)
-                mask_outside<DT>(x, 0, (int)(w.head + p.V - (int64_t)(w.nvec - 1) * E));
-        }
-        if constexpr (BWD) {
-            if (masked)
-                raw[k] = x;
-        }
-        const bool valid = vec_valid<STRIDE, EXACT>(k, kfull, lidx, w.nvec);
-        const float mn = vec_max<DT>(x, m_run);
-        const float mnL = mn == -__builtin_inff() ? 0.0f : mn * kLog2e;
-        const float add = vec_sumexp<DT>(x, mnL);
-        const float s_new = __builtin_fmaf(rescale_to(s_run, m_run, mn), 1.0f, add);
-        s_run = valid ? s_new : s_run;
-        m_run = valid ? mn : m_run;
-        if constexpr (!BWD) {
-            raw[k] = ldv(&next.w.xrow[(EXACT || v < next.w.nvec) ? v : next.w.nvec - 1]);
-            // keep each load after the use of the register it refills
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
     float m, s;
-    red.combine(m_run, s_run, m, s);
+    if constexpr (OP == EPI_LSE_GRAD) {
+        // the row's statistics are given: exp(x - lse) = 2^((x - m) log2 e - log2 s)
+        // with m = lse and s = 1
+        m = cur.lse;
+        s = 1.0f;
+    } else {
+        // One pass: each vector is folded into the lane's running (max, sum)
+        // as it arrives -- the sum is rescaled by 2^((m_old - m_new) log2 e)
+        // when the max grows -- and (forward) its registers are refilled at
+        // once with the next row's vector.
+        float m_run = -__builtin_inff();
+        float s_run = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int v = lidx + STRIDE * k;
+            Vec x = raw[k];
+            if (masked) {
+                if (k == 0 && lidx == 0 && w.head > 0)
+                    mask_outside<DT>(x, w.head, E);
+                if (k + 1 >= kfull && v >= w.nvec - 1)
+                    mask_outside<DT>(x, 0, (int)(w.head + p.V - (int64_t)(w.nvec - 1) * E));
+            }
+            if constexpr (BWD) {
+                if (masked)
+                    raw[k] = x;
+            }
+            const bool valid = vec_valid<STRIDE, EXACT>(k, kfull, lidx, w.nvec);
+            const float mn = vec_max<DT>(x, m_run);
+            const float mnL = mn == -__builtin_inff() ? 0.0f : mn * kLog2e;
+            const float add = vec_sumexp<DT>(x, mnL);
+            const float s_new = __builtin_fmaf(rescale_to(s_run, m_run, mn), 1.0f, add);
+            s_run = valid ? s_new : s_run;
+            m_run = valid ? mn : m_run;
+            if constexpr (!BWD) {
+                raw[k] = ldv(&next.w.xrow[(EXACT || v < next.w.nvec) ? v : next.w.nvec - 1]);
+                // keep each load after the use of the register it refills
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        red.combine(m_run, s_run, m, s);
+    }
     const float mL = m * kLog2e;
 
     const float et = fast_exp2(__builtin_fmaf(xt, kLog2e, -mL));
@@ -770,21 +782,22 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
     if (accurate)
         s_excl = red.sum_excl(sum_without_target<DT>(p, w.xrow, lidx, STRIDE, w.nvec, w.head,
                                                      mL, tp.vt, tp.jt));
-    const float c = row_scale(p, cur.row);
+    const float c = cur.c;
     const RowResult rr = row_result(tp.valid, m, xt, et, s, s_excl, accurate, c);
-    const float log2s = __log2f(s);
-    if (p.lse_out && cur.active && lidx == 0)
+    const float log2s = OP == EPI_LSE_GRAD ? 0.0f : __log2f(s);
+    if (OP != EPI_LSE_GRAD && p.lse_out && cur.active && lidx == 0)
         p.lse_out[cur.row] = m + kLn2 * log2s;
 
     if constexpr (BWD) {
         opt_barrier<DT, K>(raw);
-        const EpiCoef<DT> ec = epi_coef<DT, OP>(m, mL, log2s, c);
-        const int kt = (OP == EPI_GRAD && tp.valid) ? tp.vt / STRIDE : -1;
+        constexpr int EOP = OP == EPI_LSE_GRAD ? EPI_GRAD : OP;
+        const EpiCoef<DT> ec = epi_coef<DT, EOP>(m, mL, log2s, c);
+        const int kt = (EOP == EPI_GRAD && tp.valid) ? tp.vt / STRIDE : -1;
         const bool is_owner = tp.valid && lidx == tp.vt % STRIDE;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int v = lidx + STRIDE * k;
-            Vec g = epi_vec<DT, OP>(raw[k], ec);
+            Vec g = epi_vec<DT, EOP>(raw[k], ec);
             if (k == kt) {
                 if (is_owner)
                     set_elem<DT>(g, tp.jt, rr.gt);
@@ -836,16 +849,18 @@ __device__ __forceinline__ void finish_reduction(const Params &p, double wg_sum)
 // ================================================================ kernels
 
 
-template <int DT>
+template <int DT, int OP>
 __device__ __forceinline__ RowRef row_ref(const Params &p, int64_t row)
 {
     RowRef r;
     r.active = row < p.M;
     r.row = r.active ? row : 0;   // idle lanes redo row 0, store nothing, drop the loss
-    // The target is read here, a step before it is used and before the row's
-    // own loads: vector loads retire in order, so a late target load would
-    // make the wave wait for every prefetch issued before it.
+    // The per-row scalars are read here, a step before they are used and
+    // before the row's own loads: vector loads retire in order, so a late
+    // load would make the wave wait for every prefetch issued before it.
     r.t = (r.active && p.targets) ? p.targets[r.row] : -1;
+    r.c = (OP == EPI_GRAD || OP == EPI_LSE_GRAD) ? row_scale(p, r.row) : 0.0f;
+    r.lse = OP == EPI_LSE_GRAD ? p.lse_in[r.row] : 0.0f;
     r.w = row_window<DT>(p, r.row);
     return r;
 }
@@ -894,11 +909,11 @@ __global__ void __launch_bounds__(NW * 64) rows_kernel(Params p)
     };
     // the group's row in the wave's row block `base`, or fallback past the end
     auto ref_at = [&](int64_t base, const RowRef &fallback) {
-        return base < row_end ? row_ref<DT>(p, base + lane / G) : fallback;
+        return base < row_end ? row_ref<DT, OP>(p, base + lane / G) : fallback;
     };
     GroupRed<G> red;
     if (rb < row_end) {
-        RowRef a = row_ref<DT>(p, rb + lane / G);
+        RowRef a = row_ref<DT, OP>(p, rb + lane / G);
         Vec ra[K];
         issue_loads<DT, K, G, EXACT>(ra, a.w.xrow, lig, a.w.nvec);
         if constexpr (NBUF == 1) {
@@ -968,12 +983,12 @@ __global__ void __launch_bounds__(W * 64) wg_kernel(Params p)
         row_end = p.M;
     }
     if (row < row_end) {
-        RowRef cur = row_ref<DT>(p, row);
+        RowRef cur = row_ref<DT, OP>(p, row);
         Vec raw[K];
         issue_loads<DT, K, NT, EXACT>(raw, cur.w.xrow, threadIdx.x, cur.w.nvec);
         for (; row < row_end; row += row_step) {
             const bool has_next = row + row_step < row_end;
-            const RowRef next = has_next ? row_ref<DT>(p, row + row_step) : cur;
+            const RowRef next = has_next ? row_ref<DT, OP>(p, row + row_step) : cur;
             const float loss =
                 pipeline_step<DT, K, NT, OP, EXACT>(p, red, raw, cur, next, threadIdx.x, kfull);
             if (threadIdx.x == 0) {
@@ -1077,67 +1092,6 @@ __global__ void __launch_bounds__(256) wstream_kernel(Params p)
     finish_reduction(p, wg_sum);
 }
 
-// ---- gradient from a saved log-sum-exp -------------------------------------
-// The split backward: lse comes from an earlier forward, so every row is a
-// single streaming pass (read, write) with no reduction, except the rare rows
-// whose target holds more than half of the mass: there 1 - p_t is summed from
-// the other terms (one extra read of the row) to keep its relative accuracy.
-// G lanes per row, chunks of G*K vectors.  The output may be the logits.
-template <int DT, int G, int K>
-__global__ void __launch_bounds__(256) lse_grad_kernel(Params p)
-{
-    constexpr int E = Traits<DT>::E;
-    constexpr int GPW = 64 / G;
-    constexpr int CH = G * K;
-    const int lane = threadIdx.x & 63;
-    const int lig = lane & (G - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nwaves = blockDim.x >> 6;
-    const int64_t row_step = (int64_t)gridDim.x * nwaves * GPW;
-    GroupRed<G> red;
-    for (int64_t rb = ((int64_t)blockIdx.x * nwaves + wave) * GPW; rb < p.M; rb += row_step) {
-        const int64_t row_l = rb + lane / G;
-        const bool active = row_l < p.M;
-        const int64_t row = active ? row_l : 0;
-        const Window w = row_window<DT>(p, row);
-        const int64_t t = active ? p.targets[row] : -1;
-        const TargetPos tp = target_pos<DT>(t, p.V, w.head);
-        const float lse = p.lse_in[row];
-        const float lseL = lse * kLog2e;
-        const float c = row_scale(p, row);
-        // 1 - p_t, accurately when the target dominates
-        const float xt = tp.valid ? load_logit<DT>(p, row, t) : 0.0f;
-        const float pt = fast_exp2(__builtin_fmaf(xt, kLog2e, -lseL));
-        const bool accurate = tp.valid && pt > 0.5f;
-        float gt = (pt - 1.0f) * c;
-        if (accurate) {
-            const float sx = red.sum_excl(
-                sum_without_target<DT>(p, w.xrow, lig, G, w.nvec, w.head, lseL, tp.vt, tp.jt));
-            gt = -sx * c;
-        }
-        // p = 2^(x log2e - lse log2e): the row max is replaced by lse (m = lse,
-        // log2 s = 0), which gives the same exponent
-        const EpiCoef<DT> ec = epi_coef<DT, EPI_GRAD>(lse, lseL, 0.0f, c);
-        for (int cb = 0; cb < w.nvec; cb += CH) {
-            Vec raw[K];
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int v = cb + lig + G * k;
-                raw[k] = ldv(&w.xrow[v < w.nvec ? v : w.nvec - 1]);
-            }
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int v = cb + lig + G * k;
-                Vec g = epi_vec<DT, EPI_GRAD>(raw[k], ec);
-                if (v == tp.vt)
-                    set_elem<DT>(g, tp.jt, gt);
-                if (active && v < w.nvec)
-                    store_grad<DT>(w.yrow, v, g, w.head, p.V, p.aligned);
-            }
-        }
-    }
-}
-
 // ---- one row per workgroup, streamed in chunks ---------------------------------
 template <int DT, int W, int K, int OP>
 __global__ void __launch_bounds__(W * 64) stream_kernel(Params p)
@@ -1157,62 +1111,71 @@ __global__ void __launch_bounds__(W * 64) stream_kernel(Params p)
         const int64_t t = p.targets ? p.targets[row] : -1;
         const TargetPos tp = target_pos<DT>(t, p.V, w.head);
 
-        // pass 1: online (max, sum) per lane, rescaled once per chunk
-        float m_run = -__builtin_inff();
-        float s_run = 0.0f;
-        for (int cb = 0; cb < w.nvec; cb += CH) {
-            Vec raw[K];
-            const int kfull = (w.nvec - cb) >= CH ? K : (w.nvec - cb) / NT;
-            // the chunk is a window of its own: the row's head lies in chunk 0,
-            // and its end is at element head + V - cb*E of the chunk
-            load_window<DT, K, NT>(raw, w.xrow + cb, tid, w.nvec - cb, kfull,
-                                   cb == 0 ? w.head : 0,
-                                   cb == 0 ? p.V : p.V + w.head - (int64_t)cb * E,
-                                   p.aligned != 0);
-            if (tp.valid && tp.vt >= cb && tp.vt < cb + CH) {
-                const int off = tp.vt - cb;
+        float m, s, xt;
+        if constexpr (OP == EPI_LSE_GRAD) {
+            // statistics given: m = lse, s = 1
+            m = p.lse_in[row];
+            s = 1.0f;
+            xt = tp.valid ? load_logit<DT>(p, row, t) : __builtin_nanf("");
+        } else {
+            // pass 1: online (max, sum) per lane, rescaled once per chunk
+            float m_run = -__builtin_inff();
+            float s_run = 0.0f;
+            for (int cb = 0; cb < w.nvec; cb += CH) {
+                Vec raw[K];
+                const int kfull = (w.nvec - cb) >= CH ? K : (w.nvec - cb) / NT;
+                // the chunk is a window of its own: the row's head lies in chunk 0,
+                // and its end is at element head + V - cb*E of the chunk
+                load_window<DT, K, NT>(raw, w.xrow + cb, tid, w.nvec - cb, kfull,
+                                       cb == 0 ? w.head : 0,
+                                       cb == 0 ? p.V : p.V + w.head - (int64_t)cb * E,
+                                       p.aligned != 0);
+                if (tp.valid && tp.vt >= cb && tp.vt < cb + CH) {
+                    const int off = tp.vt - cb;
+#pragma unroll
+                    for (int k = 0; k < K; ++k)
+                        if (off == tid + NT * k)
+                            s_xt = vec_elem_dyn<DT>(raw[k], tp.jt);
+                }
+                float cm = m_run;
 #pragma unroll
                 for (int k = 0; k < K; ++k)
-                    if (off == tid + NT * k)
-                        s_xt = vec_elem_dyn<DT>(raw[k], tp.jt);
-            }
-            float cm = m_run;
+                    cm = vec_max<DT>(raw[k], cm);
+                if (cm != -__builtin_inff()) {
+                    const float cmL = cm * kLog2e;
+                    float add = 0.0f;
 #pragma unroll
-            for (int k = 0; k < K; ++k)
-                cm = vec_max<DT>(raw[k], cm);
-            if (cm != -__builtin_inff()) {
-                const float cmL = cm * kLog2e;
-                float add = 0.0f;
-#pragma unroll
-                for (int k = 0; k < K; ++k) {
-                    const float e = vec_sumexp<DT>(raw[k], cmL);
-                    add += vec_valid<NT>(k, kfull, tid, w.nvec - cb) ? e : 0.0f;
+                    for (int k = 0; k < K; ++k) {
+                        const float e = vec_sumexp<DT>(raw[k], cmL);
+                        add += vec_valid<NT>(k, kfull, tid, w.nvec - cb) ? e : 0.0f;
+                    }
+                    // the old sum is scaled by 2^(m_old - m_new); m_old = -inf gives 0
+                    s_run = s_run * fast_exp2((m_run - cm) * kLog2e) + add;
+                    m_run = cm;
                 }
-                // the old sum is scaled by 2^(m_old - m_new); m_old = -inf gives 0
-                s_run = s_run * fast_exp2((m_run - cm) * kLog2e) + add;
-                m_run = cm;
             }
+            float wm = group_reduce<64>(m_run, OpMax());
+            if (lane == 0)
+                s_max[wave] = wm;
+            __syncthreads();
+            m = s_max[0];
+#pragma unroll
+            for (int i = 1; i < W; ++i)
+                m = fmaxf(m, s_max[i]);
+            const float mL = m * kLog2e;
+            xt = tp.valid ? s_xt : __builtin_nanf("");
+            // every lane's sum, moved to the row max
+            float ls = (m_run == -__builtin_inff()) ? 0.0f : s_run * fast_exp2(m_run * kLog2e - mL);
+            ls = group_reduce<64>(ls, OpSum());
+            if (lane == 0)
+                s_sum[wave] = ls;
+            __syncthreads();
+            s = s_sum[0];
+#pragma unroll
+            for (int i = 1; i < W; ++i)
+                s += s_sum[i];
         }
-        float wm = group_reduce<64>(m_run, OpMax());
-        if (lane == 0)
-            s_max[wave] = wm;
-        __syncthreads();
-        float m = s_max[0];
-#pragma unroll
-        for (int i = 1; i < W; ++i)
-            m = fmaxf(m, s_max[i]);
         const float mL = m * kLog2e;
-        const float xt = tp.valid ? s_xt : __builtin_nanf("");
-        // every lane's sum, moved to the row max
-        float ls = (m_run == -__builtin_inff()) ? 0.0f : s_run * fast_exp2(m_run * kLog2e - mL);
-        ls = group_reduce<64>(ls, OpSum());
-        if (lane == 0)
-            s_sum[wave] = ls;
-        __syncthreads();
-        float s = s_sum[0];
-#pragma unroll
-        for (int i = 1; i < W; ++i)
-            s += s_sum[i];
 
         const float et = fast_exp2(__builtin_fmaf(xt, kLog2e, -mL));
         const bool accurate = tp.valid && et > 0.5f * s;
@@ -1245,13 +1208,14 @@ __global__ void __launch_bounds__(W * 64) stream_kernel(Params p)
         }
         const float c = row_scale(p, row);
         const RowResult rr = row_result(tp.valid, m, xt, et, s, s_excl, accurate, c);
-        const float log2s = __log2f(s);
-        if (p.lse_out && tid == 0)
+        const float log2s = OP == EPI_LSE_GRAD ? 0.0f : __log2f(s);
+        if (OP != EPI_LSE_GRAD && p.lse_out && tid == 0)
             p.lse_out[row] = m + kLn2 * log2s;
 
         if constexpr (BWD) {
             // pass 2: re-read the row and write the epilogue
-            const EpiCoef<DT> ec = epi_coef<DT, OP>(m, mL, log2s, c);
+            constexpr int EOP = OP == EPI_LSE_GRAD ? EPI_GRAD : OP;
+            const EpiCoef<DT> ec = epi_coef<DT, EOP>(m, mL, log2s, c);
             for (int cb = 0; cb < w.nvec; cb += CH) {
                 Vec raw[K];
 #pragma unroll
@@ -1264,8 +1228,8 @@ __global__ void __launch_bounds__(W * 64) stream_kernel(Params p)
                 for (int k = 0; k < K; ++k) {
                     const int v = cb + tid + NT * k;
                     if (v < w.nvec) {
-                        Vec g = epi_vec<DT, OP>(raw[k], ec);
-                        if (OP == EPI_GRAD && v == tp.vt)
+                        Vec g = epi_vec<DT, EOP>(raw[k], ec);
+                        if (EOP == EPI_GRAD && v == tp.vt)
                             set_elem<DT>(g, tp.jt, rr.gt);
                         store_grad<DT>(w.yrow, v, g, w.head, p.V, p.aligned);
                     }

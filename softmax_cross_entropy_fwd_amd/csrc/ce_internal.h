@@ -5,30 +5,29 @@ namespace cek {
 
 enum Kind : int { KIND_ROWS = 0, KIND_WG = 1, KIND_STREAM = 2, KIND_WSTREAM = 3 };
 
-// Host-side operation codes: the epilogues of ce_device.h plus the backward
-// from a saved log-sum-exp (its own kernel).
-enum : int { EPI_LSE_GRAD = 16 };
-
 struct KernelRef {
     const void *fn;   // host stub of a __global__ instance, or nullptr
     int block;        // threads per workgroup it was compiled for
 };
 
 // op: EPI_NONE (forward), EPI_GRAD (fused in-place backward), EPI_SOFTMAX,
-// EPI_LOGSOFTMAX or EPI_LSE_GRAD (rows kind, a = lanes per row, b = 4).
+// EPI_LOGSOFTMAX or EPI_LSE_GRAD (backward from a given log-sum-exp).
 // (kind, a, b): rows (G lanes per row, K vectors per lane), wg (W waves, K
 // vectors per lane), stream (W waves, K vectors per lane per chunk) or
 // wstream (a = 1 wave per row, K vectors per lane per chunk; forward only).
 // exact: every row window is exactly the tile (aligned rows of G*K or
 // W*64*K vectors).  nbuf: row buffers per lane of the rows kernel (1 or 2;
-// 17 or 18 for 16-wave workgroups).  Forward units answer EPI_NONE only,
-// epilogue units everything else.
+// 17 or 18 for 16-wave workgroups).  Each unit answers its own operations:
+// _fwd EPI_NONE, _grad EPI_GRAD, _aux the rest; others get a null KernelRef.
 KernelRef get_kernel_f32_fwd(int op, int kind, int a, int b, bool exact, int nbuf);
-KernelRef get_kernel_f32_epi(int op, int kind, int a, int b, bool exact, int nbuf);
+KernelRef get_kernel_f32_grad(int op, int kind, int a, int b, bool exact, int nbuf);
+KernelRef get_kernel_f32_aux(int op, int kind, int a, int b, bool exact, int nbuf);
 KernelRef get_kernel_f16_fwd(int op, int kind, int a, int b, bool exact, int nbuf);
-KernelRef get_kernel_f16_epi(int op, int kind, int a, int b, bool exact, int nbuf);
+KernelRef get_kernel_f16_grad(int op, int kind, int a, int b, bool exact, int nbuf);
+KernelRef get_kernel_f16_aux(int op, int kind, int a, int b, bool exact, int nbuf);
 KernelRef get_kernel_bf16_fwd(int op, int kind, int a, int b, bool exact, int nbuf);
-KernelRef get_kernel_bf16_epi(int op, int kind, int a, int b, bool exact, int nbuf);
+KernelRef get_kernel_bf16_grad(int op, int kind, int a, int b, bool exact, int nbuf);
+KernelRef get_kernel_bf16_aux(int op, int kind, int a, int b, bool exact, int nbuf);
 
 const void *empty_reduce_fn();
 

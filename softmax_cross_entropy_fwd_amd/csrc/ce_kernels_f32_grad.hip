@@ -1,0 +1,5 @@
+// f32 kernel instances: fused forward + in-place backward.
+#define CE_DT DT_F32
+#define CE_PART 1
+#define CE_GET_KERNEL get_kernel_f32_grad
+#include "ce_kernels_inst.h"

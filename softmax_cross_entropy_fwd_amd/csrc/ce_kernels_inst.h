@@ -1,6 +1,7 @@
 // ce_kernels_inst.h -- instantiates the kernel shapes for one storage type and
-// one group of epilogues.  Included by the per-type units with CE_DT, CE_PART
-// (0: forward only, 1: epilogues) and CE_GET_KERNEL defined.
+// one group of operations.  Included by the per-type units with CE_DT, CE_PART
+// (0: forward, 1: fused backward, 2: softmax, log-softmax and the backward
+// from a given log-sum-exp) and CE_GET_KERNEL defined.
 #include "ce_device.h"
 #include "ce_internal.h"
 
@@ -49,7 +50,8 @@ KernelRef pick_all(int kind, int a, int b, int nbuf)
     return KernelRef{nullptr, 0};
 }
 
-// The shapes the plan table uses, for softmax and log-softmax.
+// The shapes the plan table uses, for softmax, log-softmax and the backward
+// from a given log-sum-exp.
 template <int DT, int OP, bool EXACT>
 KernelRef pick_table(int kind, int a, int b, int nbuf)
 {
@@ -80,21 +82,20 @@ KernelRef CE_GET_KERNEL(int op, int kind, int a, int b, bool exact, int nbuf)
     if (op == EPI_NONE)
         return exact ? pick_all<CE_DT, EPI_NONE, true>(kind, a, b, nbuf)
                      : pick_all<CE_DT, EPI_NONE, false>(kind, a, b, nbuf);
-#else
+#elif CE_PART == 1
     if (op == EPI_GRAD)
         return exact ? pick_all<CE_DT, EPI_GRAD, true>(kind, a, b, nbuf)
                      : pick_all<CE_DT, EPI_GRAD, false>(kind, a, b, nbuf);
+#else
     if (op == EPI_SOFTMAX)
         return exact ? pick_table<CE_DT, EPI_SOFTMAX, true>(kind, a, b, nbuf)
                      : pick_table<CE_DT, EPI_SOFTMAX, false>(kind, a, b, nbuf);
     if (op == EPI_LOGSOFTMAX)
         return exact ? pick_table<CE_DT, EPI_LOGSOFTMAX, true>(kind, a, b, nbuf)
                      : pick_table<CE_DT, EPI_LOGSOFTMAX, false>(kind, a, b, nbuf);
-    if (op == EPI_LSE_GRAD && kind == KIND_ROWS && b == 4) {
-        if (a == 4) return KernelRef{(const void *)&lse_grad_kernel<CE_DT, 4, 4>, 256};
-        if (a == 16) return KernelRef{(const void *)&lse_grad_kernel<CE_DT, 16, 4>, 256};
-        if (a == 64) return KernelRef{(const void *)&lse_grad_kernel<CE_DT, 64, 4>, 256};
-    }
+    if (op == EPI_LSE_GRAD)
+        return exact ? pick_table<CE_DT, EPI_LSE_GRAD, true>(kind, a, b, nbuf)
+                     : pick_table<CE_DT, EPI_LSE_GRAD, false>(kind, a, b, nbuf);
 #endif
     return KernelRef{nullptr, 0};
 }
