@@ -17,8 +17,9 @@
  *   in place over x, with c = 1/M for mean and c = 1 for sum and none (the
  *   gradient of the returned loss, or of the sum of the row losses).
  *
- * Numerics: every row is reduced in fp32 (online max, then sum of
- * exp2((x - max) * log2 e)); row losses are accumulated in fp64 and the
+ * Numerics: every row is reduced in fp32 in one pass (running max and a sum
+ * of exp2((x - max) * log2 e) rescaled when the max grows); row losses are
+ * accumulated in fp64 and the
  * mean/sum is formed in fp64 in a fixed order, so results are bitwise
  * reproducible for a given device and shape.  Gradients are rounded to the
  * storage type with round-to-nearest-even (subnormals kept).
@@ -70,14 +71,16 @@ enum {
 #define CE_MAX_V 2147483647LL
 
 /*
- * Bytes of device workspace ce_fwd / ce_fwd_lse / ce_fwd_bwd_inplace need for these
- * arguments: 0 for CE_NONE and for M == 0, otherwise a fixed 33 KiB
- * (a ticket word and up to 4096 fp64 partial sums).
+ * Bytes of device workspace ce_fwd / ce_fwd_lse / ce_fwd_bwd_inplace need
+ * for these arguments: 0 for CE_NONE and for M == 0, otherwise a fixed
+ * 128 KiB (up to 16384 fp64 partial sums, one per wavefront or workgroup of
+ * the launch).
  *
- * The workspace must be zero-filled before its first use; every call leaves
- * it zero-filled again, so one workspace can be reused by successive calls on
- * one stream.  Calls that may run concurrently need distinct workspaces.
- * Returns 0 for invalid arguments as well.
+ * Its contents need no initialization and are scratch after the call.  A
+ * mean or sum is two launches on `stream` (the row kernel, then a one-
+ * wavefront kernel that adds the partial sums in a fixed order), so calls on
+ * one stream may share a workspace; calls that may run concurrently need
+ * distinct workspaces.  Returns 0 for invalid arguments as well.
  */
 size_t ce_workspace_bytes(int64_t M, int64_t V, ce_dtype_t dtype,
                           ce_reduction_t reduction);

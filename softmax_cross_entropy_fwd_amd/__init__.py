@@ -103,7 +103,7 @@ def ce_plan_describe(M, V, dtype, reduction="mean", fwd_bwd=False, op=None):
 
 
 def workspace_for(device, stream, nbytes):
-    """A zero-filled workspace cached per (device, stream); calls leave it zeroed."""
+    """A workspace cached per (device, stream) (its contents need no initialization)."""
     import torch
     key = (device.index, int(stream.cuda_stream))
     ws = _workspaces.get(key)

@@ -20,8 +20,7 @@ namespace {
 
 using cek::KernelRef;
 
-constexpr size_t kTicketBytes = 256;
-constexpr size_t kWorkspaceBytes = kTicketBytes + sizeof(double) * cek::kMaxPartials;
+constexpr size_t kWorkspaceBytes = sizeof(double) * cek::kMaxPartials;
 
 size_t elem_size(int dtype) { return dtype == CE_F32 ? 4 : 2; }
 
@@ -31,6 +30,7 @@ struct Plan {
     int nbuf = 1;
     KernelRef k{nullptr, 0};
     int64_t grid = 0;
+    int units_per_wg = 1;   // partial sums each workgroup publishes
     int occupancy = 0;
     int cus = 0;
 };
@@ -247,8 +247,12 @@ int make_plan(int64_t M, int64_t V, int dtype, int op, bool aligned, Plan *plan)
     const char *g = std::getenv("CE_FORCE_GRID");
     if (g && *g && std::atoll(g) > 0)
         cap = std::atoll(g);
-    if (cap > cek::kMaxPartials)
-        cap = cek::kMaxPartials;
+    // one published partial per wavefront (rows kernels) or workgroup
+    const int64_t units_per_wg =
+        (kind == cek::KIND_ROWS || kind == cek::KIND_WSTREAM) ? plan->k.block / 64 : 1;
+    plan->units_per_wg = (int)units_per_wg;
+    if (cap * units_per_wg > cek::kMaxPartials)
+        cap = cek::kMaxPartials / units_per_wg;
     plan->grid = needed < cap ? needed : cap;
     if (plan->grid < 1)
         plan->grid = 1;
@@ -381,8 +385,7 @@ int run(const Call &c, void *stream)
     p.y = c.y ? (cek::Vec *)((uintptr_t)c.y - (uintptr_t)head0 * s) : nullptr;
     p.targets = c.targets;
     p.out = c.loss ? c.out : nullptr;
-    p.ticket = reduction == CE_NONE ? nullptr : (unsigned int *)c.ws;
-    p.partials = reduction == CE_NONE ? nullptr : (double *)((char *)c.ws + kTicketBytes);
+    p.partials = reduction == CE_NONE ? nullptr : (double *)c.ws;
     p.M = c.M;
     p.V = c.V;
     p.head0 = head0;
@@ -393,7 +396,7 @@ int run(const Call &c, void *stream)
     // split backward uses its reduction for the gradient scale and the shape
     // of dloss alone.
     p.reduction = reduction;
-    if (reduction != CE_NONE && (!p.ticket || !p.partials))
+    if (reduction != CE_NONE && !p.partials)
         return CE_ERR_WORKSPACE;
     const double scale = c.reduction == CE_MEAN ? 1.0 / (double)c.M : 1.0;
     p.c = (float)scale;
@@ -406,6 +409,13 @@ int run(const Call &c, void *stream)
     if (hipLaunchKernel(plan.k.fn, dim3((unsigned)plan.grid), dim3(plan.k.block), args, 0, st) !=
         hipSuccess)
         return CE_ERR_HIP;
+    if (reduction != CE_NONE) {
+        // the fixed-order sum of the units' partials (same stream, after the grid)
+        unsigned nunits = (unsigned)(plan.grid * plan.units_per_wg);
+        void *args2[] = {&p, &nunits};
+        if (hipLaunchKernel(cek::sum_partials_fn(), dim3(1), dim3(64), args2, 0, st) != hipSuccess)
+            return CE_ERR_HIP;
+    }
     return CE_OK;
 }
 

@@ -45,7 +45,7 @@ enum : int { EPI_NONE = 0, EPI_GRAD = 1, EPI_SOFTMAX = 2, EPI_LOGSOFTMAX = 3, EP
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
-constexpr int kMaxPartials = 4096;
+constexpr int kMaxPartials = 16384;   // units (wavefronts or workgroups) per grid
 
 struct alignas(16) Vec {
     uint32_t w[4];
@@ -55,8 +55,7 @@ struct Params {
     Vec *x;                  // 16-byte aligned address at or before logits[0]
     const int64_t *targets;  // [M]
     float *out;              // [M] (none) or [1]
-    double *partials;        // [gridDim.x] per-workgroup loss sums
-    unsigned int *ticket;    // zero between calls
+    double *partials;        // one loss sum per unit (wavefront or workgroup)
     int64_t M;
     int64_t V;
     int head0;               // elements between x and logits[0]
@@ -813,37 +812,40 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
 }
 
 // --------------------------------------------- end of kernel: mean / sum
-// Each workgroup publishes its fp64 loss sum; the last one to finish (integer
-// ticket) adds all of them in index order and writes the result, then clears
-// the ticket.  The order of every addition is fixed by the launch shape.
+// Every unit (a wavefront of the rows kernels, a workgroup of the row-per-
+// workgroup kernels) stores its fp64 loss sum in its own slot; a second,
+// one-wavefront kernel on the same stream adds the slots in index order and
+// writes the result.  No atomics, fences or barriers: a unit leaves as soon
+// as its rows are done, and the order of every addition is fixed by the
+// launch shape.  (Measured on MI355X, the kernel boundary costs less than a
+// ticket taken by the last unit of the grid.)
 
-__device__ __forceinline__ void finish_reduction(const Params &p, double wg_sum)
+// Sum over the 64 lanes in a fixed butterfly order; every lane gets the sum.
+__device__ __forceinline__ double wave_sum_f64(double v)
 {
-    __shared__ int s_last;
-    __shared__ double s_red[1024];
-    if (threadIdx.x == 0) {
-        __hip_atomic_store(&p.partials[blockIdx.x], wg_sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        unsigned prev = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == gridDim.x - 1);
-    }
-    __syncthreads();
-    if (!s_last)
-        return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Adds nunits partial sums in a fixed order with one wavefront (all lanes
+// get the total).
+__device__ __forceinline__ double sum_partials(const double *partials, unsigned nunits, int lane)
+{
     double acc = 0.0;
-    for (unsigned i = threadIdx.x; i < gridDim.x; i += blockDim.x)
-        acc += __hip_atomic_load(&p.partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_red[threadIdx.x] = acc;
-    __syncthreads();
-    for (unsigned w = blockDim.x / 2; w > 0; w >>= 1) {
-        if (threadIdx.x < w)
-            s_red[threadIdx.x] += s_red[threadIdx.x + w];
-        __syncthreads();
+    for (unsigned base = 0; base < nunits; base += 64 * 8) {
+        double v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const unsigned i = base + (unsigned)lane + 64u * j;
+            v[j] = i < nunits ? partials[i] : 0.0;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            acc += v[j];
     }
-    if (threadIdx.x == 0) {
-        p.out[0] = (float)(s_red[0] * p.out_scale);
-        __hip_atomic_store(p.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    return wave_sum_f64(acc);
 }
 
 // ================================================================ kernels
@@ -941,16 +943,10 @@ __global__ void __launch_bounds__(NW * 64) rows_kernel(Params p)
 
     if (p.reduction == RED_NONE)
         return;
-    __shared__ double s_grp[NW * 64 / G];
-    if (lig == 0)
-        s_grp[threadIdx.x / G] = acc;
-    __syncthreads();
-    double wg_sum = 0.0;
-    if (threadIdx.x == 0) {
-        for (int i = 0; i < (int)(blockDim.x / G); ++i)
-            wg_sum += s_grp[i];
-    }
-    finish_reduction(p, wg_sum);
+    // lanes other than each group's first hold 0
+    const double wave_total = wave_sum_f64(acc);
+    if (lane == 0)
+        p.partials[blockIdx.x * nwaves + wave] = wave_total;
 }
 
 // ---- one row per workgroup, row in registers --------------------------------
@@ -1002,8 +998,9 @@ __global__ void __launch_bounds__(W * 64) wg_kernel(Params p)
             cur = next;
         }
     }
-    if (p.reduction != RED_NONE)
-        finish_reduction(p, acc);
+    // thread 0 holds the workgroup's sum
+    if (p.reduction != RED_NONE && threadIdx.x == 0)
+        p.partials[blockIdx.x] = acc;
 }
 
 // ---- one row per wavefront, streamed in chunks ------------------------------
@@ -1081,15 +1078,9 @@ __global__ void __launch_bounds__(256) wstream_kernel(Params p)
     }
     if (p.reduction == RED_NONE)
         return;
-    __shared__ double s_wave[4];
+    // lane 0 holds the wavefront's sum
     if (lane == 0)
-        s_wave[wave] = acc;
-    __syncthreads();
-    double wg_sum = 0.0;
-    if (threadIdx.x == 0)
-        for (int i = 0; i < nwaves; ++i)
-            wg_sum += s_wave[i];
-    finish_reduction(p, wg_sum);
+        p.partials[blockIdx.x * nwaves + wave] = acc;
 }
 
 // ---- one row per workgroup, streamed in chunks ---------------------------------
@@ -1246,8 +1237,8 @@ __global__ void __launch_bounds__(W * 64) stream_kernel(Params p)
         }
         __syncthreads();   // s_xt and the LDS partials are reused by the next row
     }
-    if (p.reduction != RED_NONE)
-        finish_reduction(p, acc);
+    if (p.reduction != RED_NONE && tid == 0)
+        p.partials[blockIdx.x] = acc;
 }
 
 }  // namespace cek

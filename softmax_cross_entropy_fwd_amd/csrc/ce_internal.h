@@ -30,5 +30,6 @@ KernelRef get_kernel_bf16_grad(int op, int kind, int a, int b, bool exact, int n
 KernelRef get_kernel_bf16_aux(int op, int kind, int a, int b, bool exact, int nbuf);
 
 const void *empty_reduce_fn();
+const void *sum_partials_fn();
 
 }  // namespace cek

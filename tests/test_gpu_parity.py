@@ -271,3 +271,25 @@ def test_workspace_reuse_and_streams(ce):
             r = ce.ce_fwd(x, t, "mean")
         s.synchronize()
         check_scalar(r.item(), want)
+
+
+def test_workspace_needs_no_initialization(ce):
+    import torch
+    # the partial-sum slots are written before they are read: garbage in the
+    # workspace (NaN bit patterns) changes nothing
+    for name, M in (("classifier", 3000), ("stress", 64), ("skinny", 9000)):
+        c = inputs.CONFIGS[name]
+        x, t = inputs.make(c["dtype"], M, c["V"], c["sigma"], c["seed"], c["structure"],
+                           device="cuda:0")
+        nbytes = ce.ce_workspace_bytes(M, c["V"], {"f32": 0, "f16": 1, "bf16": 2}[c["dtype"]],
+                                       "mean")
+        ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda:0")
+        want = oracle.reduce(oracle.loss_rows(inputs.host_bits(x), t.cpu().numpy(),
+                                              dtype=c["dtype"]), "mean")
+        for _ in range(2):
+            got = ce.ce_fwd(x, t, "mean", workspace=ws)
+            check_scalar(got.item(), want)
+        y = x.clone()
+        got = ce.ce_fwd_bwd_inplace(y, t, "sum", workspace=ws)
+        check_scalar(got.item(), oracle.reduce(oracle.loss_rows(
+            inputs.host_bits(x), t.cpu().numpy(), dtype=c["dtype"]), "sum"))
