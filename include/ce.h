@@ -60,7 +60,8 @@ enum {
     CE_ERR_SHAPE = -2,       /* M < 0, V < 1, V > CE_MAX_V, or M*V*size overflows */
     CE_ERR_DTYPE = -3,       /* dtype is not a ce_dtype_t */
     CE_ERR_REDUCTION = -4,   /* reduction is not a ce_reduction_t */
-    CE_ERR_WORKSPACE = -5,   /* workspace NULL, too small or not 8-byte aligned */
+    CE_ERR_WORKSPACE = -5,   /* workspace NULL or too small for a mean / sum, or
+                                not 8-byte aligned */
     CE_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed */
     CE_ERR_ALIGNMENT = -7,   /* a pointer not aligned to its element size, or an
                                 output not at the logits' address modulo 16 */
@@ -71,16 +72,20 @@ enum {
 #define CE_MAX_V 2147483647LL
 
 /*
- * Bytes of device workspace ce_fwd / ce_fwd_lse / ce_fwd_bwd_inplace need
- * for these arguments: 0 for CE_NONE and for M == 0, otherwise a fixed
- * 128 KiB (up to 16384 fp64 partial sums, one per wavefront or workgroup of
- * the launch).
+ * Bytes of device workspace a call with these arguments can use:
+ *  - the mean or sum of ce_fwd / ce_fwd_lse / ce_fwd_bwd_inplace needs
+ *    128 KiB (up to 16384 fp64 partial sums, one per wavefront or workgroup
+ *    of the launch; a one-wavefront kernel adds them in a fixed order);
+ *  - few long rows (M <= 128 and rows of at least 256 KiB) are split over
+ *    several workgroups when the call gets a workspace of the size returned
+ *    here (128 KiB plus up to M * 772 bytes), for every entry point and
+ *    every reduction; with less (or NULL, where allowed) each row stays in
+ *    one workgroup, with the same results to rounding.
+ * Returns 0 when no workspace is used (and for invalid arguments).
  *
  * Its contents need no initialization and are scratch after the call.  A
- * mean or sum is two launches on `stream` (the row kernel, then a one-
- * wavefront kernel that adds the partial sums in a fixed order), so calls on
- * one stream may share a workspace; calls that may run concurrently need
- * distinct workspaces.  Returns 0 for invalid arguments as well.
+ * call may be several launches on `stream`, so calls on one stream may share
+ * a workspace; calls that may run concurrently need distinct workspaces.
  */
 size_t ce_workspace_bytes(int64_t M, int64_t V, ce_dtype_t dtype,
                           ce_reduction_t reduction);
@@ -141,6 +146,7 @@ int ce_fwd_bwd_inplace(void *logits, const int64_t *targets, int64_t M,
  *            16 bytes as logits (CE_ERR_ALIGNMENT).  grad == logits
  *            overwrites the logits; any other overlap with an argument is
  *            CE_ERR_ALIAS.
+ *   workspace, workspace_bytes: optional (NULL, 0); see ce_workspace_bytes.
  * A row whose target is outside [0, V) gets d_i c softmax(x_i), with no
  * one-hot term.  Where p_t > 1/2, 1 - p_t is summed from the other terms of
  * the row (one extra read of that row) so the target's gradient keeps its
@@ -148,7 +154,8 @@ int ce_fwd_bwd_inplace(void *logits, const int64_t *targets, int64_t M,
  */
 int ce_bwd(const void *logits, const int64_t *targets, const float *lse,
            const float *dloss, int64_t M, int64_t V, ce_dtype_t dtype,
-           ce_reduction_t reduction, void *grad, void *stream);
+           ce_reduction_t reduction, void *grad, void *workspace,
+           size_t workspace_bytes, void *stream);
 
 /*
  * Row softmax or log-softmax in one pass over the row: the fused softmax of
@@ -161,10 +168,12 @@ int ce_bwd(const void *logits, const int64_t *targets, const float *lse,
  * in the logits' dtype, rounded to nearest even.  out has the same
  * alignment rule and may be logits (in place), as grad of ce_bwd.
  *   lse      optional [M] fp32 row log-sum-exps (NULL: not written).
+ *   workspace, workspace_bytes: optional (NULL, 0); see ce_workspace_bytes.
  * A row that is entirely -inf gives NaN.
  */
 int ce_softmax(const void *logits, int64_t M, int64_t V, ce_dtype_t dtype,
-               int log_softmax, void *out, float *lse, void *stream);
+               int log_softmax, void *out, float *lse, void *workspace,
+               size_t workspace_bytes, void *stream);
 
 /* A static, human-readable name for a status code. */
 const char *ce_status_string(int status);

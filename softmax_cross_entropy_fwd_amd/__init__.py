@@ -58,9 +58,9 @@ def load_library(path=None):
         lib.ce_fwd_bwd_inplace.restype = i32
         lib.ce_fwd_lse.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, vp, sz, vp]
         lib.ce_fwd_lse.restype = i32
-        lib.ce_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, vp, vp]
+        lib.ce_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, vp, vp, sz, vp]
         lib.ce_bwd.restype = i32
-        lib.ce_softmax.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp]
+        lib.ce_softmax.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, sz, vp]
         lib.ce_softmax.restype = i32
         lib.ce_status_string.argtypes = [i32]
         lib.ce_status_string.restype = ctypes.c_char_p
@@ -190,7 +190,20 @@ def ce_fwd_lse(logits, targets, reduction="mean", out=None, lse=None, workspace=
     return _call("ce_fwd_lse", logits, targets, reduction, out, workspace, lse=lse), lse
 
 
-def ce_bwd(logits, targets, lse, reduction="mean", dloss=None, grad=None):
+def _workspace(lib, logits, red, workspace):
+    """(pointer, bytes) of the workspace a call can use, cached per stream
+    unless one is given; (None, 0) when the call uses none."""
+    import torch
+    M, V = logits.shape
+    nbytes = int(lib.ce_workspace_bytes(M, V, _dtype_code(logits), red))
+    if not nbytes:
+        return None, 0
+    if workspace is None:
+        workspace = workspace_for(logits.device, torch.cuda.current_stream(logits.device), nbytes)
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def ce_bwd(logits, targets, lse, reduction="mean", dloss=None, grad=None, workspace=None):
     """Gradient of the loss from saved row log-sum-exps, into grad (a new
     tensor by default; grad=logits overwrites the logits).  dloss: the
     upstream gradient, [M] for 'none', one element otherwise, or None for 1."""
@@ -207,17 +220,18 @@ def ce_bwd(logits, targets, lse, reduction="mean", dloss=None, grad=None):
         grad = torch.empty_like(logits)
     _check_like(grad, logits, "grad")
     stream = torch.cuda.current_stream(dev)
+    ws_ptr, ws_len = _workspace(lib, logits, red, workspace)
     with torch.cuda.device(dev):
         rc = lib.ce_bwd(logits.data_ptr(), targets.data_ptr(), lse.data_ptr() if M else None,
                         dloss.data_ptr() if dloss is not None else None, M, V,
                         _dtype_code(logits), red, grad.data_ptr() if M else None,
-                        stream.cuda_stream)
+                        ws_ptr, ws_len, stream.cuda_stream)
     if rc:
         raise CEError(rc, "ce_bwd")
     return grad
 
 
-def ce_softmax(logits, log_softmax=False, out=None, lse=None):
+def ce_softmax(logits, log_softmax=False, out=None, lse=None, workspace=None):
     """Row softmax (or log-softmax) of logits [M, V] in their dtype, into out
     (a new tensor by default; out=logits works in place).  lse: optional [M]
     fp32 tensor that receives the row log-sum-exps."""
@@ -232,11 +246,12 @@ def ce_softmax(logits, log_softmax=False, out=None, lse=None):
     if lse is not None:
         _check_rows(lse, M, dev, "lse")
     stream = torch.cuda.current_stream(dev)
+    ws_ptr, ws_len = _workspace(lib, logits, CE_NONE, workspace)
     with torch.cuda.device(dev):
         rc = lib.ce_softmax(logits.data_ptr(), M, V, _dtype_code(logits), int(bool(log_softmax)),
                             out.data_ptr() if M else None,
                             lse.data_ptr() if (lse is not None and M) else None,
-                            stream.cuda_stream)
+                            ws_ptr, ws_len, stream.cuda_stream)
     if rc:
         raise CEError(rc, "ce_softmax")
     return out

@@ -20,11 +20,17 @@ namespace {
 
 using cek::KernelRef;
 
-constexpr size_t kWorkspaceBytes = sizeof(double) * cek::kMaxPartials;
+constexpr size_t kPartialBytes = sizeof(double) * cek::kMaxPartials;
+constexpr int kMaxSplit = 64;            // slices per row
+constexpr int64_t kSplitMaxRows = 128;         // rows up to which splitting pays
+constexpr int64_t kSplitMaxRowsForced = 512;   // bound of the workspace's split scratch
+constexpr int64_t kSplitMinVecs = 16384;       // 256 KiB rows
+constexpr size_t kSplitBytesPerSlice = 12;   // (max, sum) + the target-fix sum, fp32
 
 size_t elem_size(int dtype) { return dtype == CE_F32 ? 4 : 2; }
 
 struct Plan {
+    int split = 0, slice_vecs = 0;   // slices per row (0: one workgroup or group per row)
     int kind = 0, a = 0, b = 0;
     bool exact = false;
     int nbuf = 1;
@@ -45,6 +51,13 @@ KernelRef lookup(int dtype, int op, int kind, int a, int b, bool exact, int nbuf
     };
     const int part = op == cek::EPI_NONE ? 0 : op == cek::EPI_GRAD ? 1 : 2;
     return table[dtype][part](op, kind, a, b, exact, nbuf);
+}
+
+cek::SplitKernels split_kernels(int dtype)
+{
+    return dtype == CE_F32 ? cek::split_kernels_f32()
+           : dtype == CE_F16 ? cek::split_kernels_f16()
+                             : cek::split_kernels_bf16();
 }
 
 // Vectors one tile of a shape covers (0 for the stream kernels: any row).
@@ -184,6 +197,51 @@ int64_t window_vectors(int64_t V, int E, bool aligned)
     return aligned ? V / E : (V + 2 * E - 2) / E;
 }
 
+// Slices per row when the rows are long and too few to fill the device one
+// workgroup per row (0: no split): about 1024 workgroups in all, slices of
+// whole chunks.  Measured on MI355X: splitting pays for at most 128 rows of
+// at least 256 KiB (a 2 MiB bf16 row: 112 -> 23 us for the fused backward),
+// and loses to the one-row kernels from about 256 rows on.
+// CE_FORCE_SPLIT=S forces S slices for up to 512 rows of 32 KiB and more
+// (0 disables splitting); CE_FORCE_PLAN disables it unless CE_FORCE_SPLIT is
+// set.  Both are for tuning and tests.
+int split_slices(int64_t M, int64_t nvec, int *slice_vecs)
+{
+    const char *f = std::getenv("CE_FORCE_SPLIT");
+    const int forced = (f && *f) ? std::atoi(f) : -1;
+    const char *fp = std::getenv("CE_FORCE_PLAN");
+    if (forced == 0 || (forced < 0 && fp && *fp))
+        return 0;
+    const int64_t max_rows = forced > 0 ? kSplitMaxRowsForced : kSplitMaxRows;
+    const int64_t min_vecs = forced > 0 ? 2 * cek::kSplitChunk : kSplitMinVecs;
+    if (M < 1 || M > max_rows || nvec < min_vecs)
+        return 0;
+    int64_t S = forced > 0 ? forced : (1024 + M - 1) / M;
+    const int64_t by_len = nvec / cek::kSplitChunk;
+    if (S > by_len)
+        S = by_len;
+    if (S > kMaxSplit)
+        S = kMaxSplit;
+    if (S < 2)
+        return 0;
+    int64_t sv = (nvec + S - 1) / S;
+    sv = (sv + cek::kSplitChunk - 1) / cek::kSplitChunk * cek::kSplitChunk;
+    S = (nvec + sv - 1) / sv;
+    if (S < 2)
+        return 0;
+    *slice_vecs = (int)sv;
+    return (int)S;
+}
+
+// Workspace bytes a call uses: the partial-sum slots when it reduces losses,
+// then the split scratch when its rows are split.
+size_t used_workspace(int64_t M, bool reduced, int S)
+{
+    if (S > 0)
+        return kPartialBytes + (size_t)M * ((size_t)S * kSplitBytesPerSlice + 4);
+    return reduced ? kPartialBytes : 0;
+}
+
 int make_plan(int64_t M, int64_t V, int dtype, int op, bool aligned, Plan *plan)
 {
     const int E = 16 / (int)elem_size(dtype);
@@ -291,6 +349,25 @@ struct Region {
     size_t n;
 };
 
+// Slices per row this call uses: split rows need the workspace's scratch.
+int call_split(const Call &c, int *slice_vecs)
+{
+    if (c.M < 1 || !c.ws)
+        return 0;
+    const size_t s = elem_size(c.dtype);
+    const int E = 16 / (int)s;
+    const int head0 = (int)(((uintptr_t)c.logits % 16) / s);
+    const bool aligned = head0 == 0 && c.V % E == 0;
+    int sv = 0;
+    const int S = split_slices(c.M, window_vectors(c.V, E, aligned), &sv);
+    const bool reduced = c.loss && c.reduction != CE_NONE;
+    if (S < 2 || c.ws_bytes < used_workspace(c.M, reduced, S))
+        return 0;
+    if (slice_vecs)
+        *slice_vecs = sv;
+    return S;
+}
+
 int check_args(const Call &c)
 {
     if (c.dtype != CE_F32 && c.dtype != CE_F16 && c.dtype != CE_BF16)
@@ -320,9 +397,11 @@ int check_args(const Call &c)
     if (has_y && (uintptr_t)c.y % 16 != (uintptr_t)c.logits % 16)
         return CE_ERR_ALIGNMENT;
     if (reduced) {
-        if (!c.ws || c.ws_bytes < kWorkspaceBytes || (uintptr_t)c.ws % 8)
+        if (!c.ws || c.ws_bytes < kPartialBytes || (uintptr_t)c.ws % 8)
             return CE_ERR_WORKSPACE;
     }
+    if (c.ws && (uintptr_t)c.ws % 8)
+        return CE_ERR_WORKSPACE;
     // Outputs may not overlap one another or any input; the epilogue output
     // may be the logits themselves (exactly, in place).
     const size_t xb = (size_t)c.M * (size_t)c.V * s;
@@ -333,7 +412,7 @@ int check_args(const Call &c)
         {c.lse_out, per_row},
         {c.y == c.logits ? nullptr : c.y, has_y ? xb : 0},
         {c.y == c.logits ? c.y : nullptr, has_y ? xb : 0},
-        {c.ws, reduced ? kWorkspaceBytes : 0},
+        {c.ws, used_workspace(c.M, reduced, call_split(c, nullptr))},
     };
     const Region ins[] = {
         {c.y == c.logits ? nullptr : c.logits, xb},
@@ -375,9 +454,13 @@ int run(const Call &c, void *stream)
     const int head0 = (int)((base % 16) / s);
     const bool aligned = head0 == 0 && c.V % E == 0;
     Plan plan;
-    rc = make_plan(c.M, c.V, c.dtype, c.op, aligned, &plan);
-    if (rc)
-        return rc;
+    int slice_vecs = 0;
+    const int S = call_split(c, &slice_vecs);
+    if (S == 0) {
+        rc = make_plan(c.M, c.V, c.dtype, c.op, aligned, &plan);
+        if (rc)
+            return rc;
+    }
 
     const int reduction = c.loss ? c.reduction : CE_NONE;
     cek::Params p;
@@ -405,13 +488,38 @@ int run(const Call &c, void *stream)
     p.dloss_per_row = c.reduction == CE_NONE ? 1 : 0;
     p.lse_out = c.lse_out;
     p.lse_in = c.lse_in;
+    p.S = S;
+    p.slice_vecs = slice_vecs;
+    p.stats = S ? (float *)((char *)c.ws + kPartialBytes) : nullptr;
+    p.fix = S ? p.stats + 2 * (size_t)c.M * (size_t)S : nullptr;
+    p.rowx = S ? p.fix + (size_t)c.M * (size_t)S : nullptr;
     void *args[] = {&p};
-    if (hipLaunchKernel(plan.k.fn, dim3((unsigned)plan.grid), dim3(plan.k.block), args, 0, st) !=
-        hipSuccess)
-        return CE_ERR_HIP;
+    unsigned nunits = 0;
+    if (S) {
+        // split rows: slice statistics, then the per-row finish or the
+        // epilogue over every slice, then (backward from lse) the target fix
+        const cek::SplitKernels sk = split_kernels(c.dtype);
+        const unsigned wgs = (unsigned)(c.M * S);
+        if (c.op != cek::EPI_LSE_GRAD &&
+            hipLaunchKernel(sk.stats, dim3(wgs), dim3(256), args, 0, st) != hipSuccess)
+            return CE_ERR_HIP;
+        const bool fwd = c.op == cek::EPI_NONE;
+        if (hipLaunchKernel(fwd ? sk.finish : sk.epi[c.op], dim3(fwd ? (unsigned)c.M : wgs),
+                            dim3(fwd ? 64 : 256), args, 0, st) != hipSuccess)
+            return CE_ERR_HIP;
+        if (c.op == cek::EPI_LSE_GRAD &&
+            hipLaunchKernel(sk.fix, dim3((unsigned)((c.M + 3) / 4)), dim3(256), args, 0, st) !=
+                hipSuccess)
+            return CE_ERR_HIP;
+        nunits = (unsigned)c.M;   // one partial per row
+    } else {
+        if (hipLaunchKernel(plan.k.fn, dim3((unsigned)plan.grid), dim3(plan.k.block), args, 0,
+                            st) != hipSuccess)
+            return CE_ERR_HIP;
+        nunits = (unsigned)(plan.grid * plan.units_per_wg);
+    }
     if (reduction != CE_NONE) {
         // the fixed-order sum of the units' partials (same stream, after the grid)
-        unsigned nunits = (unsigned)(plan.grid * plan.units_per_wg);
         void *args2[] = {&p, &nunits};
         if (hipLaunchKernel(cek::sum_partials_fn(), dim3(1), dim3(64), args2, 0, st) != hipSuccess)
             return CE_ERR_HIP;
@@ -427,11 +535,17 @@ size_t ce_workspace_bytes(int64_t M, int64_t V, ce_dtype_t dtype, ce_reduction_t
 {
     if (dtype != CE_F32 && dtype != CE_F16 && dtype != CE_BF16)
         return 0;
-    if (reduction != CE_MEAN && reduction != CE_SUM)
+    if (reduction != CE_NONE && reduction != CE_MEAN && reduction != CE_SUM)
         return 0;
     if (M <= 0 || V < 1 || V > CE_MAX_V)
         return 0;
-    return kWorkspaceBytes;
+    // the worst-case window (a misaligned base) bounds the slices
+    const int E = 16 / (int)elem_size(dtype);
+    int sv = 0;
+    const int S = split_slices(M, window_vectors(V, E, false), &sv);
+    if (S > 0)
+        return kPartialBytes + (size_t)M * (kMaxSplit * kSplitBytesPerSlice + 4);
+    return reduction == CE_NONE ? 0 : kPartialBytes;
 }
 
 int ce_fwd(const void *logits, const int64_t *targets, int64_t M, int64_t V, ce_dtype_t dtype,
@@ -492,7 +606,7 @@ int ce_fwd_bwd_inplace(void *logits, const int64_t *targets, int64_t M, int64_t 
 
 int ce_bwd(const void *logits, const int64_t *targets, const float *lse, const float *dloss,
            int64_t M, int64_t V, ce_dtype_t dtype, ce_reduction_t reduction, void *grad,
-           void *stream)
+           void *workspace, size_t workspace_bytes, void *stream)
 {
     Call c;
     c.op = cek::EPI_LSE_GRAD;
@@ -506,11 +620,13 @@ int ce_bwd(const void *logits, const int64_t *targets, const float *lse, const f
     c.dtype = (int)dtype;
     c.reduction = (int)reduction;
     c.y = grad;
+    c.ws = workspace;
+    c.ws_bytes = workspace ? workspace_bytes : 0;
     return run(c, stream);
 }
 
 int ce_softmax(const void *logits, int64_t M, int64_t V, ce_dtype_t dtype, int log_softmax,
-               void *out, float *lse, void *stream)
+               void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream)
 {
     Call c;
     c.op = log_softmax ? cek::EPI_LOGSOFTMAX : cek::EPI_SOFTMAX;
@@ -521,6 +637,8 @@ int ce_softmax(const void *logits, int64_t M, int64_t V, ce_dtype_t dtype, int l
     c.dtype = (int)dtype;
     c.y = out;
     c.lse_out = lse;
+    c.ws = workspace;
+    c.ws_bytes = workspace ? workspace_bytes : 0;
     return run(c, stream);
 }
 
@@ -559,6 +677,13 @@ int ce_plan_describe(int64_t M, int64_t V, ce_dtype_t dtype, ce_reduction_t redu
         return CE_ERR_SHAPE;
     const int E = 16 / (int)elem_size(dtype);
     const bool aligned = V % E == 0;   // for a 16-byte aligned base
+    int sv = 0;
+    const int S = split_slices(M, window_vectors(V, E, aligned), &sv);
+    if (S > 0) {
+        std::snprintf(buf, buf_len, "split:%d slice=%d block=256 grid=%lld (with workspace)", S,
+                      sv, (long long)M * S);
+        return CE_OK;
+    }
     Plan plan;
     int rc = make_plan(M, V, (int)dtype, ops[op], aligned, &plan);
     if (rc)

@@ -69,6 +69,12 @@ struct Params {
     int dloss_per_row;       // dloss holds one value per row
     float *lse_out;          // optional [M] row log-sum-exps
     const float *lse_in;     // [M] given log-sum-exps (backward from saved statistics)
+    // split rows: S workgroups per row, each over slice_vecs window vectors
+    int S;
+    int slice_vecs;
+    float *stats;            // [M * S][2] slice (max, sum) with the target left out
+    float *fix;              // [M * S] slice sums of p_j, j != t (backward from lse)
+    float *rowx;             // [M] target logits, saved before any slice is overwritten
 };
 
 // ------------------------------------------------------------ storage types
@@ -1239,6 +1245,262 @@ __global__ void __launch_bounds__(W * 64) stream_kernel(Params p)
     }
     if (p.reduction != RED_NONE && tid == 0)
         p.partials[blockIdx.x] = acc;
+}
+
+
+// ---- split rows: several workgroups per row ---------------------------------
+// For few long rows: workgroup b takes slice b % S of row b / S (slice_vecs
+// window vectors).  A first kernel leaves each slice's (max, sum of
+// exp(x - max)) with the target element left out; the epilogue kernel
+// combines a row's S pairs in a fixed order (every workgroup of the row
+// computes the same combine) and writes its slice.  Leaving the target out
+// gives the sum of the other terms exactly, so the dominant-target form of
+// the loss and of the target's gradient needs no second read.
+
+template <int DT, int W, int K>
+__global__ void __launch_bounds__(W * 64) split_stats_kernel(Params p)
+{
+    constexpr int E = Traits<DT>::E;
+    constexpr int NT = W * 64;
+    constexpr int CH = NT * K;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    __shared__ float s_m[W], s_s[W];
+    const int64_t row = blockIdx.x / p.S;
+    const int slice = blockIdx.x % p.S;
+    const Window w = row_window<DT>(p, row);
+    const int64_t t = p.targets ? p.targets[row] : -1;
+    const TargetPos tp = target_pos<DT>(t, p.V, w.head);
+    const int v0 = slice * p.slice_vecs;
+    const int v1 = v0 + p.slice_vecs < w.nvec ? v0 + p.slice_vecs : w.nvec;
+    const int tail_n = (int)(w.head + p.V - (int64_t)(w.nvec - 1) * E);
+    // the slice holding the target saves its logit for the later kernels
+    if (tid == 0 && tp.vt >= v0 && tp.vt < v1)
+        p.rowx[row] = load_logit<DT>(p, row, t);
+    float m_run = -__builtin_inff();
+    float s_run = 0.0f;
+    for (int cb = v0; cb < v1; cb += CH) {
+        Vec raw[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int v = cb + tid + NT * k;
+            raw[k] = ldv(&w.xrow[v < v1 ? v : v1 - 1]);
+        }
+        float cm = m_run;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int v = cb + tid + NT * k;
+            if (v == 0 && w.head > 0)
+                mask_outside<DT>(raw[k], w.head, E);
+            if (v == w.nvec - 1)
+                mask_outside<DT>(raw[k], 0, tail_n);
+            if (v == tp.vt)
+                set_elem<DT>(raw[k], tp.jt, -__builtin_inff());
+            cm = v < v1 ? vec_max<DT>(raw[k], cm) : cm;
+        }
+        if (cm != -__builtin_inff()) {
+            const float cmL = cm * kLog2e;
+            float add = 0.0f;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const float e = vec_sumexp<DT>(raw[k], cmL);
+                add += (cb + tid + NT * k) < v1 ? e : 0.0f;
+            }
+            s_run = rescale_to(s_run, m_run, cm) + add;
+            m_run = cm;
+        }
+    }
+    const float wm = group_reduce<64>(m_run, OpMax());
+    const float ws = group_reduce<64>(rescale_to(s_run, m_run, wm), OpSum());
+    if (lane == 0) {
+        s_m[wave] = wm;
+        s_s[wave] = ws;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float m = s_m[0];
+#pragma unroll
+        for (int i = 1; i < W; ++i)
+            m = fmaxf(m, s_m[i]);
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < W; ++i)
+            s += rescale_to(s_s[i], s_m[i], m);
+        p.stats[2 * blockIdx.x] = m;
+        p.stats[2 * blockIdx.x + 1] = s;
+    }
+}
+
+// The row's statistics from its S slice pairs, in a fixed order, by one
+// wavefront (every lane gets them): max and sum over all terms but the target.
+__device__ __forceinline__ void combine_slices(const Params &p, int64_t row, int lane,
+                                               float &m_ex, float &s_ex)
+{
+    const float *st = p.stats + 2 * row * p.S;
+    const float mi = lane < p.S ? st[2 * lane] : -__builtin_inff();
+    const float si = lane < p.S ? st[2 * lane + 1] : 0.0f;
+    m_ex = group_reduce<64>(mi, OpMax());
+    s_ex = group_reduce<64>(rescale_to(si, mi, m_ex), OpSum());
+}
+
+// OP == EPI_NONE: one 64-thread workgroup per row (b = row) finishing the
+// forward; otherwise workgroup b writes the epilogue over slice b % S of row
+// b / S.  The loss, lse and partial sums are written by slice 0.
+template <int DT, int W, int K, int OP>
+__global__ void __launch_bounds__(W * 64) split_epi_kernel(Params p)
+{
+    constexpr int E = Traits<DT>::E;
+    constexpr int NT = W * 64;
+    constexpr int CH = NT * K;
+    constexpr int EOP = OP == EPI_LSE_GRAD ? EPI_GRAD : OP;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    __shared__ float s_row[3];
+    const int64_t row = OP == EPI_NONE ? (int64_t)blockIdx.x : (int64_t)(blockIdx.x / p.S);
+    const int slice = OP == EPI_NONE ? 0 : (int)(blockIdx.x % p.S);
+    const Window w = row_window<DT>(p, row);
+    const int64_t t = p.targets ? p.targets[row] : -1;
+    const TargetPos tp = target_pos<DT>(t, p.V, w.head);
+    const float c = (EOP == EPI_GRAD) ? row_scale(p, row) : 0.0f;
+    const int v0 = slice * p.slice_vecs;
+    const int v1 = v0 + p.slice_vecs < w.nvec ? v0 + p.slice_vecs : w.nvec;
+    const bool owner = tp.vt >= v0 && tp.vt < v1;   // this slice holds the target
+    if (wave == 0) {
+        // The target logit: saved by the statistics kernel; for the backward
+        // from a given lse only the owner needs it (it reads it before any
+        // store of its own, and saves it for the fix).  Other slices of an
+        // in-place call may already have overwritten it.
+        float xt = __builtin_nanf("");
+        if constexpr (OP == EPI_LSE_GRAD) {
+            if (owner) {
+                xt = load_logit<DT>(p, row, t);
+                if (lane == 0)
+                    p.rowx[row] = xt;
+            }
+        } else if (tp.valid) {
+            xt = p.rowx[row];
+        }
+        float m, s, s_excl;
+        if constexpr (OP == EPI_LSE_GRAD) {
+            m = p.lse_in[row];
+            s = 1.0f;
+            s_excl = 0.0f;   // unused: the target's gradient is (p_t - 1) c, refined later
+        } else {
+            float m_ex, s_ex;
+            combine_slices(p, row, lane, m_ex, s_ex);
+            m = tp.valid ? fmaxf(m_ex, xt) : m_ex;
+            s_excl = rescale_to(s_ex, m_ex, m);
+            s = s_excl;
+        }
+        const float mL = m * kLog2e;
+        const float et = tp.valid ? fast_exp2(__builtin_fmaf(xt, kLog2e, -mL)) : 0.0f;
+        if constexpr (OP != EPI_LSE_GRAD)
+            s += et;
+        else
+            s_excl = s - et;
+        const bool accurate = OP != EPI_LSE_GRAD && tp.valid && et > 0.5f * s;
+        const RowResult rr = row_result(tp.valid, m, xt, et, s, s_excl, accurate, c);
+        const float log2s = OP == EPI_LSE_GRAD ? 0.0f : __log2f(s);
+        if (lane == 0) {
+            s_row[0] = m;
+            s_row[1] = log2s;
+            s_row[2] = rr.gt;
+            if (slice == 0 && OP != EPI_LSE_GRAD) {
+                if (p.lse_out)
+                    p.lse_out[row] = m + kLn2 * log2s;
+                if (p.reduction == RED_NONE) {
+                    if (p.out)
+                        p.out[row] = rr.loss;
+                } else {
+                    p.partials[row] = (double)rr.loss;
+                }
+            }
+        }
+    }
+    if constexpr (OP == EPI_NONE) {
+        return;
+    } else {
+        __syncthreads();
+        const float m = s_row[0];
+        const float log2s = s_row[1];
+        const float gt = s_row[2];
+        const float mL = m * kLog2e;
+        const EpiCoef<DT> ec = epi_coef<DT, EOP>(m, mL, log2s, c);
+        const int tail_n = (int)(w.head + p.V - (int64_t)(w.nvec - 1) * E);
+        float fx = 0.0f;   // sum of p_j over j != t in this slice (EPI_LSE_GRAD)
+        for (int cb = v0; cb < v1; cb += CH) {
+            Vec raw[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int v = cb + tid + NT * k;
+                raw[k] = ldv(&w.xrow[v < v1 ? v : v1 - 1]);
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int v = cb + tid + NT * k;
+                if (v < v1) {
+                    Vec g = epi_vec<DT, EOP>(raw[k], ec);
+                    if (EOP == EPI_GRAD && owner && v == tp.vt)
+                        set_elem<DT>(g, tp.jt, gt);
+                    store_grad<DT>(w.yrow, v, g, w.head, p.V, p.aligned);
+                    if constexpr (OP == EPI_LSE_GRAD) {
+                        Vec x = raw[k];
+                        if (v == 0 && w.head > 0)
+                            mask_outside<DT>(x, w.head, E);
+                        if (v == w.nvec - 1)
+                            mask_outside<DT>(x, 0, tail_n);
+                        if (v == tp.vt)
+                            set_elem<DT>(x, tp.jt, -__builtin_inff());
+                        fx += vec_sumexp<DT>(x, mL);
+                    }
+                }
+            }
+        }
+        if constexpr (OP == EPI_LSE_GRAD) {
+            __shared__ float s_fx[W];
+            const float wf = group_reduce<64>(fx, OpSum());
+            if (lane == 0)
+                s_fx[wave] = wf;
+            __syncthreads();
+            if (tid == 0) {
+                float f = 0.0f;
+#pragma unroll
+                for (int i = 0; i < W; ++i)
+                    f += s_fx[i];
+                p.fix[blockIdx.x] = f;
+            }
+        }
+    }
+}
+
+// Backward from a given lse over split rows: where p_t > 1/2, the target's
+// gradient is rewritten as -(sum of the other p_j) c from the slices' sums,
+// which keeps its relative accuracy.  One wavefront per row.
+template <int DT>
+__global__ void __launch_bounds__(256) split_fix_kernel(Params p)
+{
+    constexpr int E = Traits<DT>::E;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (row >= p.M)
+        return;
+    const int64_t t = p.targets[row];
+    const Window w = row_window<DT>(p, row);
+    const TargetPos tp = target_pos<DT>(t, p.V, w.head);
+    if (!tp.valid)
+        return;
+    const float lseL = p.lse_in[row] * kLog2e;
+    const float pt = fast_exp2(__builtin_fmaf(p.rowx[row], kLog2e, -lseL));
+    if (!(pt > 0.5f))
+        return;
+    const float f = group_reduce<64>(lane < p.S ? p.fix[row * p.S + lane] : 0.0f, OpSum());
+    if (lane == 0) {
+        Vec g = {};
+        set_elem<DT>(g, tp.jt, -f * row_scale(p, row));
+        store_partial<DT>(w.yrow + tp.vt, g, tp.jt, tp.jt + 1);
+    }
 }
 
 }  // namespace cek

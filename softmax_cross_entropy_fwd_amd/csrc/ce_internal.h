@@ -29,6 +29,21 @@ KernelRef get_kernel_bf16_fwd(int op, int kind, int a, int b, bool exact, int nb
 KernelRef get_kernel_bf16_grad(int op, int kind, int a, int b, bool exact, int nbuf);
 KernelRef get_kernel_bf16_aux(int op, int kind, int a, int b, bool exact, int nbuf);
 
+// Split rows (several workgroups per row): slice statistics, the forward's
+// per-row finish (64 threads), the epilogue per operation (indexed by EPI_*,
+// null for EPI_NONE), the target fix of the backward from a given lse.
+// Slices are streamed in chunks of kSplitChunk window vectors by 256 threads.
+constexpr int kSplitChunk = 1024;
+struct SplitKernels {
+    const void *stats;
+    const void *finish;
+    const void *epi[5];
+    const void *fix;
+};
+SplitKernels split_kernels_f32();
+SplitKernels split_kernels_f16();
+SplitKernels split_kernels_bf16();
+
 const void *empty_reduce_fn();
 const void *sum_partials_fn();
 

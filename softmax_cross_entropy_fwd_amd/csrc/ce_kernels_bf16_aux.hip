@@ -1,5 +1,6 @@
-// bf16 kernel instances: softmax, log-softmax, backward from a given log-sum-exp.
+// bf16 kernel instances: softmax, log-softmax, backward from a given log-sum-exp; the split-row kernels.
 #define CE_DT DT_BF16
 #define CE_PART 2
 #define CE_GET_KERNEL get_kernel_bf16_aux
+#define CE_SPLIT_KERNELS split_kernels_bf16
 #include "ce_kernels_inst.h"

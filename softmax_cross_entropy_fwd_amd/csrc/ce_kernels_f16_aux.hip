@@ -1,5 +1,6 @@
-// f16 kernel instances: softmax, log-softmax, backward from a given log-sum-exp.
+// f16 kernel instances: softmax, log-softmax, backward from a given log-sum-exp; the split-row kernels.
 #define CE_DT DT_F16
 #define CE_PART 2
 #define CE_GET_KERNEL get_kernel_f16_aux
+#define CE_SPLIT_KERNELS split_kernels_f16
 #include "ce_kernels_inst.h"

@@ -100,4 +100,21 @@ KernelRef CE_GET_KERNEL(int op, int kind, int a, int b, bool exact, int nbuf)
     return KernelRef{nullptr, 0};
 }
 
+#if CE_PART == 2
+SplitKernels CE_SPLIT_KERNELS()
+{
+    static_assert(kSplitChunk == 4 * 64 * 4, "chunk = W x 64 x K of the split kernels");
+    SplitKernels s;
+    s.stats = (const void *)&split_stats_kernel<CE_DT, 4, 4>;
+    s.finish = (const void *)&split_epi_kernel<CE_DT, 1, 1, EPI_NONE>;
+    s.epi[EPI_NONE] = nullptr;
+    s.epi[EPI_GRAD] = (const void *)&split_epi_kernel<CE_DT, 4, 4, EPI_GRAD>;
+    s.epi[EPI_SOFTMAX] = (const void *)&split_epi_kernel<CE_DT, 4, 4, EPI_SOFTMAX>;
+    s.epi[EPI_LOGSOFTMAX] = (const void *)&split_epi_kernel<CE_DT, 4, 4, EPI_LOGSOFTMAX>;
+    s.epi[EPI_LSE_GRAD] = (const void *)&split_epi_kernel<CE_DT, 4, 4, EPI_LSE_GRAD>;
+    s.fix = (const void *)&split_fix_kernel<CE_DT>;
+    return s;
+}
+#endif
+
 }  // namespace cek

@@ -135,10 +135,10 @@ def test_fwd_lse_argument_errors(lib):
 
 
 def call_bwd(lib, logits=FAKE, targets=FAKE + 2048, lse=FAKE + 3072, dloss=None, M=4, V=8,
-             dtype=0, red=1, grad=FAKE + 65536):
+             dtype=0, red=1, grad=FAKE + 65536, ws=None, ws_bytes=0):
     return lib.ce_bwd(VP(logits) if logits else None, VP(targets) if targets else None,
                       VP(lse) if lse else None, VP(dloss) if dloss else None, M, V, dtype, red,
-                      VP(grad) if grad else None, None)
+                      VP(grad) if grad else None, VP(ws) if ws else None, ws_bytes, None)
 
 
 def test_bwd_argument_errors(lib):
@@ -166,9 +166,11 @@ def test_bwd_argument_errors(lib):
     assert call_bwd(lib, M=0, logits=0, targets=0, lse=0, grad=0) == ce.CE_OK
 
 
-def call_softmax(lib, logits=FAKE, M=4, V=8, dtype=0, log=0, out=FAKE + 65536, lse=None):
+def call_softmax(lib, logits=FAKE, M=4, V=8, dtype=0, log=0, out=FAKE + 65536, lse=None,
+                 ws=None, ws_bytes=0):
     return lib.ce_softmax(VP(logits) if logits else None, M, V, dtype, log,
-                          VP(out) if out else None, VP(lse) if lse else None, None)
+                          VP(out) if out else None, VP(lse) if lse else None,
+                          VP(ws) if ws else None, ws_bytes, None)
 
 
 def test_softmax_argument_errors(lib):
@@ -190,6 +192,25 @@ def test_plan_describe_rejects_unknown_op(lib):
     buf = ctypes.create_string_buffer(64)
     assert lib.ce_plan_describe(4, 8, 0, 1, 5, buf, 64) == ce.CE_ERR_SHAPE
     assert lib.ce_plan_describe(4, 8, 0, 1, -1, buf, 64) == ce.CE_ERR_SHAPE
+
+
+def test_split_workspace_checks(lib):
+    import softmax_cross_entropy_fwd_amd as ce
+    # few long rows: the workspace also holds the split scratch, for every
+    # reduction; a misaligned workspace is refused, an overlapping one too
+    M, V = 8, 1 << 17
+    n = lib.ce_workspace_bytes(M, V, 2, 0)
+    assert n >= (128 << 10) + M * 64 * 12
+    assert lib.ce_workspace_bytes(M, V, 2, 1) == n
+    assert lib.ce_workspace_bytes(4096, V, 2, 0) == 0            # many rows: no split
+    assert lib.ce_workspace_bytes(8, 1000, 0, 0) == 0            # short rows: no split
+    big = 1 << 40
+    assert call_softmax(lib, M=M, V=V, dtype=2, out=FAKE + big, ws=FAKE + 2 * big + 4,
+                        ws_bytes=n) == ce.CE_ERR_WORKSPACE
+    assert call_softmax(lib, M=M, V=V, dtype=2, out=FAKE + big, ws=FAKE + big + 64,
+                        ws_bytes=n) == ce.CE_ERR_ALIAS
+    assert call_bwd(lib, M=M, V=V, dtype=2, lse=FAKE + 3 * big, targets=FAKE + 3 * big + 4096,
+                    grad=FAKE + big, ws=FAKE + 64, ws_bytes=n) == ce.CE_ERR_ALIAS
 
 
 def test_workspace_bytes(lib):
