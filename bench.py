@@ -63,10 +63,12 @@ OPS = ["fwd", "fwd_lse", "fwd_bwd", "bwd", "softmax", "log_softmax"]
 
 
 def kernel_source_hash():
+    """Hash of the sources the cross-entropy kernels are built from (the
+    csrc/ce_* units and headers and the public header)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "softmax_cross_entropy_fwd_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
+        if name.startswith("ce_") and name.endswith((".hip", ".h")):
             h.update(name.encode())
             h.update(open(os.path.join(csrc, name), "rb").read())
     h.update(open(os.path.join(ROOT, "include", "ce.h"), "rb").read())
