@@ -14,7 +14,9 @@ of the pages it follows, is documented in ``ce_oracle.c``:
 * mean / sum over rows (same trace: mean reduction of ``F.cross_entropy``);
 * gradient (softmax - onehot) * c written in the storage type ("9 Triton
   kernels in 9 weeks", week 7), optionally times a per-row upstream gradient;
-* row softmax and log-softmax (same page, week 1; the trace's log_softmax).
+* row softmax and log-softmax (same page, week 1; the trace's log_softmax);
+* linear + cross-entropy: logits H W^T of bf16 H, W, then the loss, and the
+  gradients of H and W (same page, week 8).
 
 Storage types are passed as raw bits: float32 arrays for fp32, uint16 arrays of
 the bit patterns for fp16 and bf16.
@@ -71,6 +73,9 @@ def _load():
     lib.oracle_ce_grad_rows.restype = i32
     lib.oracle_softmax_rows.argtypes = [vp, i32, i64, i64, i64, i64, i32, i32, vp, _dp, _dp]
     lib.oracle_softmax_rows.restype = i32
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    lib.oracle_linear_ce.argtypes = [u16p, u16p, _i64p, i64, i64, i64, i32, _dp, _dp, _dp, _dp, _dp]
+    lib.oracle_linear_ce.restype = i32
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i32
     _lib = lib
@@ -199,6 +204,42 @@ def softmax_rows(x, dtype="f32", log=False, row0=0, nrows=None, out_dtype=None,
     if with_lse:
         res += (lse,)
     return res[0] if len(res) == 1 else res
+
+
+def linear_ce(h_bits, w_bits, targets, reduction="mean", grads=False):
+    """Linear + cross-entropy on bf16 bit patterns H [M, D], W [V, D].
+
+    Returns (loss, lse) -- loss as fp64 [M] for 'none', else a float -- and,
+    with grads, also (G, dH, dW) in fp64: the logits' gradient [M, V] and the
+    gradients of the hidden states [M, D] and the weight [V, D].
+    """
+    lib = _load()
+    h = np.ascontiguousarray(h_bits, dtype=np.uint16)
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    if h.ndim != 2 or w.ndim != 2 or h.shape[1] != w.shape[1]:
+        raise ValueError("H must be [M, D] and W [V, D]")
+    M, D = h.shape
+    V = w.shape[0]
+    t = _targets(targets, M)
+    red = _RED_CODE[reduction]
+    out = np.empty(max(M, 1) if red == NONE else 1, dtype=np.float64)
+    lse = np.empty(max(M, 1), dtype=np.float64)
+    G = np.empty((M, V), dtype=np.float64) if grads else None
+    dH = np.empty((M, D), dtype=np.float64) if grads else None
+    dW = np.empty((V, D), dtype=np.float64) if grads else None
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    rc = lib.oracle_linear_ce(h.ctypes.data_as(u16p), w.ctypes.data_as(u16p),
+                              t.ctypes.data_as(_i64p), M, D, V, red, out.ctypes.data_as(_dp),
+                              lse.ctypes.data_as(_dp),
+                              G.ctypes.data_as(_dp) if grads else None,
+                              dH.ctypes.data_as(_dp) if grads else None,
+                              dW.ctypes.data_as(_dp) if grads else None)
+    if rc:
+        raise ValueError("oracle_linear_ce: bad arguments")
+    loss = out[:M] if red == NONE else float(out[0])
+    if grads:
+        return loss, lse[:M], G, dH, dW
+    return loss, lse[:M]
 
 
 def widen(bits, dtype):

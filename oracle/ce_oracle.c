@@ -25,6 +25,12 @@
  *  - Row softmax exp(x_ij - lse_i) and log-softmax x_ij - lse_i: same page,
  *    week 1 (fused softmax), and the log_softmax step of the trace's problem
  *    statement.
+ *  - Linear + cross-entropy: the logits are the lm_head projection z = H W^T
+ *    of bf16 hidden states H [M, D] and weight W [V, D], and the loss is the
+ *    cross-entropy above on z; gradients dH = G W and dW = G^T H with G the
+ *    logits' gradient: same page, week 8 (the lm_head projection folded into
+ *    the loss, chunk by chunk).  Products of two bf16 values are exact in
+ *    fp64; their sums are plain fp64 sums.
  *
  * Readings taken where the pages are silent (each is listed in the design
  * notes of the repository):
@@ -47,9 +53,10 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2 };
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_F64 = 3 /* internal: fp64 rows */ };
 enum { OR_NONE = 0, OR_MEAN = 1, OR_SUM = 2 };
 
 /* ---------------------------------------------------------------- storage */
@@ -154,6 +161,8 @@ float oracle_round_f32(double v)
 static double elem(const void *x, int dtype, int64_t k)
 {
     switch (dtype) {
+    case OR_F64:
+        return ((const double *)x)[k];
     case OR_F32:
         return (double)((const float *)x)[k];
     case OR_F16:
@@ -377,6 +386,83 @@ int oracle_softmax_rows(const void *x, int dtype, int64_t M, int64_t V,
             if (out)
                 store_rounded(out, out_dtype, o, v);
         }
+    }
+    return 0;
+}
+
+/*
+ * Linear + cross-entropy on bf16 H [M, D] and W [V, D] (bit patterns):
+ * z_i = H_i W^T in fp64, then row_loss on z_i.  out: per-row losses (none)
+ * or the reduced loss in out[0]; lse_out [M] (may be NULL).  When G is not
+ * NULL it receives the logits' gradient [M, V] with scale c (1/M for mean,
+ * else 1); dH [M, D] = G W and dW [V, D] = G^T H (each may be NULL; both
+ * need G).  Returns 0, or -1 on bad arguments or no memory.
+ */
+int oracle_linear_ce(const uint16_t *H, const uint16_t *W, const int64_t *targets,
+                     int64_t M, int64_t D, int64_t V, int reduction,
+                     double *out, double *lse_out, double *G, double *dH,
+                     double *dW)
+{
+    if (!H || !W || !targets || !out || M < 0 || D < 1 || V < 1 ||
+        reduction < OR_NONE || reduction > OR_SUM || ((dH || dW) && !G))
+        return -1;
+    double *losses = (double *)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+    if (!losses)
+        return -1;
+    const double c = reduction == OR_MEAN ? 1.0 / (double)M : 1.0;
+    int fail = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i) {
+        double *z = (double *)malloc(sizeof(double) * (size_t)V);
+        if (!z) {
+            fail = 1;
+            continue;
+        }
+        for (int64_t j = 0; j < V; ++j) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < D; ++k)
+                acc += oracle_widen_bf16(H[i * D + k]) * oracle_widen_bf16(W[j * D + k]);
+            z[j] = acc;
+        }
+        const int64_t t = targets[i];
+        double lse;
+        const double loss = row_loss(z, OR_F64, V, t, &lse);
+        losses[i] = loss;
+        if (lse_out)
+            lse_out[i] = lse;
+        if (G)
+            for (int64_t j = 0; j < V; ++j)
+                G[i * V + j] = (j == t ? expm1(-loss) : exp(z[j] - lse)) * c;
+        free(z);
+    }
+    if (fail) {
+        free(losses);
+        return -1;
+    }
+    if (reduction == OR_NONE)
+        memcpy(out, losses, sizeof(double) * (size_t)M);
+    else
+        out[0] = oracle_ce_reduce(losses, M, reduction);
+    free(losses);
+    if (dH) {
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < M; ++i)
+            for (int64_t k = 0; k < D; ++k) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < V; ++j)
+                    acc += G[i * V + j] * oracle_widen_bf16(W[j * D + k]);
+                dH[i * D + k] = acc;
+            }
+    }
+    if (dW) {
+#pragma omp parallel for schedule(static)
+        for (int64_t j = 0; j < V; ++j)
+            for (int64_t k = 0; k < D; ++k) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < M; ++i)
+                    acc += G[i * V + j] * oracle_widen_bf16(H[i * D + k]);
+                dW[j * D + k] = acc;
+            }
     }
     return 0;
 }
