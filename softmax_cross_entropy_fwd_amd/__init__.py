@@ -11,6 +11,8 @@ in the library's HIP kernels; if the library is missing, every call raises.
     loss, lse = ce_fwd_lse(logits, targets, reduction="mean")
     grad = ce_bwd(logits, targets, lse, reduction="mean", dloss=None)
     probs = ce_softmax(logits)                    # or log_softmax=True
+    loss, lse = ce_linear_fwd(hidden, weight, targets)            # logits = hidden @ weight.T
+    loss, dhidden, dweight = ce_linear_fwd_bwd(hidden, weight, targets)
 """
 import ctypes
 import os
@@ -62,6 +64,15 @@ def load_library(path=None):
         lib.ce_bwd.restype = i32
         lib.ce_softmax.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, sz, vp]
         lib.ce_softmax.restype = i32
+        lib.ce_linear_chunk.argtypes = [i64, i64, i64, i64]
+        lib.ce_linear_chunk.restype = i64
+        lib.ce_linear_workspace_bytes.argtypes = [i64, i64, i64, i64]
+        lib.ce_linear_workspace_bytes.restype = sz
+        lib.ce_linear_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, vp, i64, vp, sz, vp]
+        lib.ce_linear_fwd.restype = i32
+        lib.ce_linear_fwd_bwd.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, vp, vp, vp, i64, vp,
+                                          sz, vp]
+        lib.ce_linear_fwd_bwd.restype = i32
         lib.ce_status_string.argtypes = [i32]
         lib.ce_status_string.restype = ctypes.c_char_p
         lib.ce_plan_describe.argtypes = [i64, i64, i32, i32, i32, ctypes.c_char_p, sz]
@@ -257,6 +268,58 @@ def ce_softmax(logits, log_softmax=False, out=None, lse=None, workspace=None):
     return out
 
 
+def _linear(fn_name, hidden, weight, targets, reduction, chunk, workspace, bwd):
+    import torch
+    lib = load_library()
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise TypeError("hidden and weight must be bfloat16")
+    for t, name in ((hidden, "hidden"), (weight, "weight")):
+        if not t.is_cuda or t.dim() != 2 or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous 2-D device tensor" % name)
+    M, D = hidden.shape
+    V = weight.shape[0]
+    if weight.shape[1] != D or weight.device != hidden.device:
+        raise ValueError("weight must be [V, D] on the hidden states' device")
+    if (targets.dtype != torch.int64 or targets.dim() != 1 or not targets.is_contiguous()
+            or targets.numel() != M or targets.device != hidden.device):
+        raise ValueError("targets must be a contiguous int64 [M] tensor on the same device")
+    red = REDUCTIONS[reduction]
+    dev = hidden.device
+    out = torch.empty((M,) if red == CE_NONE else (), dtype=torch.float32, device=dev)
+    lse = torch.empty(M, dtype=torch.float32, device=dev)
+    nbytes = int(lib.ce_linear_workspace_bytes(M, D, V, int(chunk)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    ws_len = workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(dev)
+    args = [hidden.data_ptr(), weight.data_ptr(), targets.data_ptr(), M, D, V, red,
+            out.data_ptr() if out.numel() else None, lse.data_ptr() if M else None]
+    if bwd:
+        dh = torch.empty((M, D), dtype=torch.float32, device=dev)
+        dw = torch.empty((V, D), dtype=torch.float32, device=dev)
+        args += [dh.data_ptr() if M else None, dw.data_ptr()]
+    with torch.cuda.device(dev):
+        rc = getattr(lib, fn_name)(*args, int(chunk), workspace.data_ptr(), ws_len,
+                                   stream.cuda_stream)
+    if rc:
+        raise CEError(rc, fn_name)
+    return (out, lse, dh, dw) if bwd else (out, lse)
+
+
+def ce_linear_fwd(hidden, weight, targets, reduction="mean", chunk=0, workspace=None):
+    """Cross-entropy of the logits hidden @ weight.T (bf16 [M, D] and [V, D]),
+    taken over vocabulary chunks; returns (loss, lse)."""
+    return _linear("ce_linear_fwd", hidden, weight, targets, reduction, chunk, workspace, False)
+
+
+def ce_linear_fwd_bwd(hidden, weight, targets, reduction="mean", chunk=0, workspace=None):
+    """Loss as ce_linear_fwd and its gradients; returns (loss, lse, dhidden,
+    dweight), the gradients in fp32."""
+    return _linear("ce_linear_fwd_bwd", hidden, weight, targets, reduction, chunk, workspace,
+                   True)
+
+
 __all__ = ["ce_fwd", "ce_fwd_lse", "ce_fwd_bwd_inplace", "ce_bwd", "ce_softmax",
+           "ce_linear_fwd", "ce_linear_fwd_bwd",
            "ce_workspace_bytes", "ce_status_string", "ce_plan_describe", "load_library",
            "CEError", "LIB_PATH"]

@@ -3,7 +3,8 @@
     python -m softmax_cross_entropy_fwd_amd.build [-v]
 
 Each csrc/*.hip unit is compiled to an object in parallel, then linked into
-softmax_cross_entropy_fwd_amd/libce.so; probe/bw_probe.hip (HBM bandwidth
+softmax_cross_entropy_fwd_amd/libce.so (with rocBLAS, for the GEMMs of the
+linear + cross-entropy path); probe/bw_probe.hip (HBM bandwidth
 probes for the bench) goes into libce_probe.so.  Packed-fp32 VALU forms are disabled
 for device code; no fast-math, so fp32 rounding and denormals follow IEEE.
 """
@@ -21,6 +22,7 @@ LIB = os.path.join(PKG, "libce.so")
 PROBE_SRC = os.path.join(PKG, "probe", "bw_probe.hip")
 PROBE_LIB = os.path.join(PKG, "libce_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ROCM_LIB = "/opt/rocm/lib"
 ARCH = "gfx950"
 
 CFLAGS = [
@@ -57,7 +59,9 @@ def build(verbose=False, jobs=None, defines=(), out=None):
         objs = list(ex.map(lambda s: _compile(s, verbose, defines, build_dir), srcs))
     lib = out or LIB
     tmp = lib + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp]
+    # rocBLAS serves the plain GEMMs of the linear + cross-entropy path
+    cmd = ([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs +
+           ["-L" + ROCM_LIB, "-lrocblas", "-o", tmp])
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

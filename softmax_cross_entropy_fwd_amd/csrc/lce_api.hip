@@ -1,0 +1,282 @@
+// lce_api.hip -- the C ABI of linear + cross-entropy: argument checks, the
+// chunk loop, the library GEMMs (rocBLAS) and the launches of the row
+// kernels between them.
+#include <hip/hip_runtime.h>
+#include <rocblas/rocblas.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+#include <unordered_map>
+
+#include "ce.h"
+#include "ce_device.h"
+#include "ce_internal.h"
+#include "ce_linear.h"
+#include "lce_internal.h"
+
+namespace {
+
+constexpr int64_t kChunkAlign = 256;         // columns
+constexpr int64_t kChunkBytes = 1LL << 30;   // default budget of the two chunk buffers
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+int64_t chunk_for(int64_t M, int64_t V, int64_t chunk)
+{
+    const int64_t vmax = (V + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+    int64_t C;
+    if (chunk > 0) {
+        C = (chunk + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+    } else {
+        const int64_t per_col = 6 * (M > 0 ? M : 1);   // fp32 logits + bf16 gradient
+        C = kChunkBytes / per_col / kChunkAlign * kChunkAlign;
+        if (C < kChunkAlign)
+            C = kChunkAlign;
+    }
+    return C < vmax ? C : vmax;
+}
+
+// Workspace layout (offsets in bytes, each 256-aligned).
+struct Layout {
+    size_t L, G, stats, rowx, lse, gt, partials, total;
+};
+
+Layout layout(int64_t M, int64_t C, int64_t nch)
+{
+    Layout l;
+    size_t o = 0;
+    l.L = o;
+    o += align256((size_t)M * C * 4);
+    l.G = o;
+    o += align256((size_t)M * C * 2);
+    l.stats = o;
+    o += align256((size_t)M * nch * 8);
+    l.rowx = o;
+    o += align256((size_t)M * 4);
+    l.lse = o;
+    o += align256((size_t)M * 4);
+    l.gt = o;
+    o += align256((size_t)M * 4);
+    l.partials = o;
+    o += align256((size_t)M * 8);
+    l.total = o;
+    return l;
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb)
+{
+    if (!a || !b || !na || !nb)
+        return false;
+    uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+std::mutex g_mu;
+std::unordered_map<int, rocblas_handle> g_handles;
+
+// C[m x n] (row-major, ldc) = op(A) op(B) + beta C with bf16 A, B and fp32
+// C, through rocBLAS's column-major interface (C^T = op(B)^T op(A)^T).
+bool gemm_rm(rocblas_handle h, bool ta, bool tb, int m, int n, int k, const void *A, int lda,
+             const void *B, int ldb, float beta, float *C, int ldc)
+{
+    const float alpha = 1.0f;
+    return rocblas_gemm_ex(h, tb ? rocblas_operation_transpose : rocblas_operation_none,
+                           ta ? rocblas_operation_transpose : rocblas_operation_none, n, m, k,
+                           &alpha, B, rocblas_datatype_bf16_r, ldb, A, rocblas_datatype_bf16_r, lda,
+                           &beta, C, rocblas_datatype_f32_r, ldc, C, rocblas_datatype_f32_r, ldc,
+                           rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0,
+                           rocblas_gemm_flags_none) == rocblas_status_success;
+}
+
+bool launch(const void *fn, unsigned grid, unsigned block, void **args, hipStream_t st)
+{
+    return hipLaunchKernel(fn, dim3(grid), dim3(block), args, 0, st) == hipSuccess;
+}
+
+int run(const void *H, const void *W, const int64_t *targets, int64_t M, int64_t D, int64_t V,
+        int reduction, float *out, float *lse, float *dH, float *dW, int64_t chunk, void *ws,
+        size_t ws_bytes, void *stream, bool bwd)
+{
+    if (reduction != CE_NONE && reduction != CE_MEAN && reduction != CE_SUM)
+        return CE_ERR_REDUCTION;
+    if (M < 0 || D < 1 || V < 1 || M > INT_MAX || D > INT_MAX || V > INT_MAX || chunk < 0)
+        return CE_ERR_SHAPE;
+    const int64_t C = chunk_for(M, V, chunk);
+    const int64_t nch = (V + C - 1) / C;
+    const Layout lay = layout(M, C, nch);
+    hipStream_t st = (hipStream_t)stream;
+    const bool reduced = reduction != CE_NONE;
+    if (M == 0) {
+        if (reduced && !out)
+            return CE_ERR_NULL;
+        if (bwd && !dW)
+            return CE_ERR_NULL;
+    } else {
+        if (!H || !W || !targets || !out || (bwd && (!dH || !dW)))
+            return CE_ERR_NULL;
+        if ((uintptr_t)H % 2 || (uintptr_t)W % 2 || (uintptr_t)targets % 8 || (uintptr_t)out % 4 ||
+            (uintptr_t)lse % 4 || (uintptr_t)dH % 4 || (uintptr_t)dW % 4)
+            return CE_ERR_ALIGNMENT;
+        if (!ws || ws_bytes < lay.total || (uintptr_t)ws % 16)
+            return CE_ERR_WORKSPACE;
+        const size_t hb = (size_t)M * D * 2, wb = (size_t)V * D * 2;
+        const struct {
+            const void *p;
+            size_t n;
+        } outs[] = {{out, reduced ? 4 : (size_t)M * 4}, {lse, (size_t)M * 4},
+                    {dH, bwd ? (size_t)M * D * 4 : 0}, {dW, bwd ? (size_t)V * D * 4 : 0},
+                    {ws, lay.total}},
+          ins[] = {{H, hb}, {W, wb}, {targets, (size_t)M * 8}};
+        for (int i = 0; i < 5; ++i) {
+            for (int j = i + 1; j < 5; ++j)
+                if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+                    return CE_ERR_ALIAS;
+            for (int j = 0; j < 3; ++j)
+                if (overlaps(outs[i].p, outs[i].n, ins[j].p, ins[j].n))
+                    return CE_ERR_ALIAS;
+        }
+    }
+
+    if (M == 0) {
+        if (bwd) {
+            int64_t n = V * D;
+            void *za[] = {&dW, &n};
+            if (!launch(lce::zero_kernel_fn(), 1024, 256, za, st))
+                return CE_ERR_HIP;
+        }
+        if (reduced) {
+            float value = reduction == CE_MEAN ? __builtin_nanf("") : 0.0f;
+            void *args[] = {&out, &value};
+            if (!launch(cek::empty_reduce_fn(), 1, 64, args, st))
+                return CE_ERR_HIP;
+        }
+        return CE_OK;
+    }
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return CE_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_mu);   // the handle serves one call at a time
+    rocblas_handle h;
+    auto it = g_handles.find(dev);
+    if (it == g_handles.end()) {
+        if (rocblas_create_handle(&h) != rocblas_status_success)
+            return CE_ERR_HIP;
+        g_handles[dev] = h;
+    } else {
+        h = it->second;
+    }
+    if (rocblas_set_stream(h, st) != rocblas_status_success)
+        return CE_ERR_HIP;
+
+    char *base = (char *)ws;
+    lce::LceParams q;
+    q.L = (const float *)(base + lay.L);
+    q.G = (uint16_t *)(base + lay.G);
+    q.targets = targets;
+    q.M = M;
+    q.V = V;
+    q.ldc = (int)C;
+    q.nchunks = (int)nch;
+    q.stats = (float *)(base + lay.stats);
+    q.rowx = (float *)(base + lay.rowx);
+    q.lse = (float *)(base + lay.lse);
+    q.gt = (float *)(base + lay.gt);
+    q.lse_out = lse;
+    q.out = reduced ? nullptr : out;
+    q.partials = reduced ? (double *)(base + lay.partials) : nullptr;
+    q.c = reduction == CE_MEAN ? (float)(1.0 / (double)M) : 1.0f;
+    const unsigned row_grid = (unsigned)((M + 3) / 4);
+    const int m = (int)M, d = (int)D;
+    float *Lw = (float *)(base + lay.L);
+
+    // forward: each chunk's logits, then its statistics
+    for (int64_t ci = 0; ci < nch; ++ci) {
+        q.v0 = ci * C;
+        q.vn = (int)(V - q.v0 < C ? V - q.v0 : C);
+        q.chunk_index = (int)ci;
+        const void *Wc = (const char *)W + (size_t)q.v0 * D * 2;
+        if (!gemm_rm(h, false, true, m, q.vn, d, H, d, Wc, d, 0.0f, Lw, (int)C))
+            return CE_ERR_HIP;
+        void *args[] = {&q};
+        if (!launch(lce::stats_kernel_fn(), row_grid, 256, args, st))
+            return CE_ERR_HIP;
+    }
+    {
+        void *args[] = {&q};
+        if (!launch(lce::finish_kernel_fn(), row_grid, 256, args, st))
+            return CE_ERR_HIP;
+    }
+    if (reduced) {
+        cek::Params p{};
+        p.partials = q.partials;
+        p.out = out;
+        p.out_scale = reduction == CE_MEAN ? 1.0 / (double)M : 1.0;
+        unsigned nunits = (unsigned)M;
+        void *args[] = {&p, &nunits};
+        if (!launch(cek::sum_partials_fn(), 1, 64, args, st))
+            return CE_ERR_HIP;
+    }
+    if (!bwd)
+        return CE_OK;
+
+    // backward: recompute each chunk's logits, write its bf16 gradient, then
+    // dH (+)= G W_c and dW_c = G^T H
+    for (int64_t ci = 0; ci < nch; ++ci) {
+        q.v0 = ci * C;
+        q.vn = (int)(V - q.v0 < C ? V - q.v0 : C);
+        q.chunk_index = (int)ci;
+        const void *Wc = (const char *)W + (size_t)q.v0 * D * 2;
+        if (!gemm_rm(h, false, true, m, q.vn, d, H, d, Wc, d, 0.0f, Lw, (int)C))
+            return CE_ERR_HIP;
+        void *args[] = {&q};
+        if (!launch(lce::grad_kernel_fn(), row_grid, 256, args, st))
+            return CE_ERR_HIP;
+        if (!gemm_rm(h, false, false, m, d, q.vn, q.G, (int)C, Wc, d, ci == 0 ? 0.0f : 1.0f, dH, d))
+            return CE_ERR_HIP;
+        if (!gemm_rm(h, true, false, q.vn, d, m, q.G, (int)C, H, d, 0.0f,
+                     dW + (size_t)q.v0 * D, d))
+            return CE_ERR_HIP;
+    }
+    return CE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t ce_linear_chunk(int64_t M, int64_t D, int64_t V, int64_t chunk)
+{
+    if (M < 0 || D < 1 || V < 1 || chunk < 0)
+        return 0;
+    return chunk_for(M, V, chunk);
+}
+
+size_t ce_linear_workspace_bytes(int64_t M, int64_t D, int64_t V, int64_t chunk)
+{
+    if (M < 0 || D < 1 || V < 1 || M > INT_MAX || D > INT_MAX || V > INT_MAX || chunk < 0)
+        return 0;
+    const int64_t C = chunk_for(M, V, chunk);
+    return layout(M, C, (V + C - 1) / C).total;
+}
+
+int ce_linear_fwd(const void *hidden, const void *weight, const int64_t *targets, int64_t M,
+                  int64_t D, int64_t V, ce_reduction_t reduction, float *out, float *lse,
+                  int64_t chunk, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return run(hidden, weight, targets, M, D, V, (int)reduction, out, lse, nullptr, nullptr,
+               chunk, workspace, workspace_bytes, stream, false);
+}
+
+int ce_linear_fwd_bwd(const void *hidden, const void *weight, const int64_t *targets, int64_t M,
+                      int64_t D, int64_t V, ce_reduction_t reduction, float *out, float *lse,
+                      float *dhidden, float *dweight, int64_t chunk, void *workspace,
+                      size_t workspace_bytes, void *stream)
+{
+    return run(hidden, weight, targets, M, D, V, (int)reduction, out, lse, dhidden, dweight,
+               chunk, workspace, workspace_bytes, stream, true);
+}
+
+}  // extern "C"

@@ -121,3 +121,31 @@ def dtype_name(t):
         if t.dtype == v:
             return k
     raise TypeError("unsupported logits dtype %s" % t.dtype)
+
+
+# The linear + cross-entropy workload: an LM head with the LM-head workload's
+# vocabulary (V = 131072) and logit spread (sigma = 2), hidden size 4096 and
+# 4096 tokens, in bf16.  The sizes other than V are this library's choice.
+LINEAR_CONFIGS = {
+    "lmhead_linear": dict(M=4096, D=4096, V=131072, sigma=2.0, seed=106),
+}
+
+
+def make_linear(M=64, D=256, V=1000, sigma=2.0, seed=0, device="cpu"):
+    """Return (hidden [M, D] bf16, weight [V, D] bf16, targets [M] int64):
+    hidden ~ N(0, 1) and weight ~ N(0, sigma^2 / D), so the logits hidden @
+    weight.T have standard deviation close to sigma; drawn in fp32 and rounded
+    to nearest even."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(int(seed))
+    targets = torch.randint(0, V, (M,), generator=gen, device=dev, dtype=torch.int64)
+    hidden = torch.randn((M, D), generator=gen, device=dev, dtype=torch.float32)
+    hidden = hidden.to(torch.bfloat16)
+    weight = torch.empty((V, D), dtype=torch.bfloat16, device=dev)
+    scale = sigma / float(D) ** 0.5
+    for r0 in range(0, V, 8192):
+        r1 = min(V, r0 + 8192)
+        w = torch.randn((r1 - r0, D), generator=gen, device=dev, dtype=torch.float32)
+        weight[r0:r1].copy_(w.mul_(scale))
+    return hidden, weight, targets

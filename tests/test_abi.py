@@ -9,7 +9,7 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "ce.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("ce.h", "ce_linear.h")]
 
 
 @pytest.fixture(scope="module")
@@ -22,15 +22,18 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ce_[a-z_]+)\s*\(", text)))
+    names = set()
+    for header in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+        names.update(re.findall(r"\b(ce_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("ce_fwd", "ce_fwd_lse", "ce_fwd_bwd_inplace", "ce_bwd", "ce_softmax",
-              "ce_workspace_bytes", "ce_status_string", "ce_plan_describe"):
+              "ce_workspace_bytes", "ce_status_string", "ce_plan_describe", "ce_linear_chunk",
+              "ce_linear_workspace_bytes", "ce_linear_fwd", "ce_linear_fwd_bwd"):
         assert n in names
 
 
@@ -242,3 +245,49 @@ def test_binding_rejects_host_tensors():
     t = torch.zeros(2, dtype=torch.int64)
     with pytest.raises(ValueError):
         ce.ce_fwd(x, t)
+
+
+def call_linear(lib, fn="ce_linear_fwd_bwd", H=FAKE, W=FAKE + (1 << 30), t=FAKE + (2 << 30),
+                M=4, D=8, V=300, red=1, out=FAKE + (3 << 30), lse=None, dH=FAKE + (4 << 30),
+                dW=FAKE + (5 << 30), chunk=0, ws=FAKE + (6 << 30), ws_bytes=1 << 30):
+    vp = lambda a: VP(a) if a else None
+    args = [vp(H), vp(W), vp(t), M, D, V, red, vp(out), vp(lse)]
+    if fn == "ce_linear_fwd_bwd":
+        args += [vp(dH), vp(dW)]
+    return getattr(lib, fn)(*args, chunk, vp(ws), ws_bytes, None)
+
+
+def test_linear_chunk_and_workspace(lib):
+    assert lib.ce_linear_chunk(4096, 4096, 131072, 0) == (1 << 30) // (6 * 4096) // 256 * 256
+    assert lib.ce_linear_chunk(4, 8, 300, 0) == 512            # the whole vocabulary, rounded
+    assert lib.ce_linear_chunk(4, 8, 3000, 100) == 256         # rounded up to 256 columns
+    assert lib.ce_linear_chunk(-1, 8, 300, 0) == 0
+    n = lib.ce_linear_workspace_bytes(64, 128, 5000, 1024)
+    assert n >= 64 * 1024 * 6 + 64 * 5 * 8
+    assert lib.ce_linear_workspace_bytes(64, 0, 5000, 0) == 0
+
+
+@pytest.mark.parametrize("fn", ["ce_linear_fwd", "ce_linear_fwd_bwd"])
+def test_linear_argument_errors(lib, fn):
+    import softmax_cross_entropy_fwd_amd as ce
+    assert call_linear(lib, fn, red=5) == ce.CE_ERR_REDUCTION
+    assert call_linear(lib, fn, M=-1) == ce.CE_ERR_SHAPE
+    assert call_linear(lib, fn, D=0) == ce.CE_ERR_SHAPE
+    assert call_linear(lib, fn, V=1 << 31) == ce.CE_ERR_SHAPE
+    assert call_linear(lib, fn, H=0) == ce.CE_ERR_NULL
+    assert call_linear(lib, fn, W=0) == ce.CE_ERR_NULL
+    assert call_linear(lib, fn, t=0) == ce.CE_ERR_NULL
+    assert call_linear(lib, fn, out=0) == ce.CE_ERR_NULL
+    assert call_linear(lib, fn, H=FAKE + 1) == ce.CE_ERR_ALIGNMENT
+    assert call_linear(lib, fn, t=FAKE + (2 << 30) + 4) == ce.CE_ERR_ALIGNMENT
+    assert call_linear(lib, fn, ws=0) == ce.CE_ERR_WORKSPACE
+    assert call_linear(lib, fn, ws_bytes=1000) == ce.CE_ERR_WORKSPACE
+    assert call_linear(lib, fn, ws=FAKE + (6 << 30) + 8) == ce.CE_ERR_WORKSPACE
+    assert call_linear(lib, fn, out=FAKE + 8) == ce.CE_ERR_ALIAS          # inside H
+    assert call_linear(lib, fn, lse=FAKE + (2 << 30)) == ce.CE_ERR_ALIAS  # on the targets
+    assert call_linear(lib, fn, ws=FAKE + (3 << 30) - 256) == ce.CE_ERR_ALIAS
+    if fn == "ce_linear_fwd_bwd":
+        assert call_linear(lib, fn, dH=0) == ce.CE_ERR_NULL
+        assert call_linear(lib, fn, dW=0) == ce.CE_ERR_NULL
+        assert call_linear(lib, fn, dW=FAKE + (1 << 30) + 64) == ce.CE_ERR_ALIAS   # on W
+        assert call_linear(lib, fn, dH=FAKE + (5 << 30)) == ce.CE_ERR_ALIAS        # on dW
