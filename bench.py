@@ -21,7 +21,10 @@ GB/s = bytes the method must move / kernel time.  The same line carries:
                 log-sum-exp and row softmax; the classifier's split backward
                 and softmax; the stress (fp16 [8192, 50257], misaligned rows)
                 forward and fused backward; the skinny (fp32 [1048576, 128])
-                forward; each timed the same way.
+                forward; each timed the same way; and linear + cross-entropy
+                (logits = hidden @ weight.T, bf16 [4096, 4096] x [131072, 4096],
+                taken in vocabulary chunks) forward and forward + backward in
+                TFLOP/s against the bf16 MFMA peak.
 
 Inputs rotate over enough buffers (>= 1 GiB in total) that no launch finds its
 rows in the 256 MB last-level cache; the in-place backward restores its logits
@@ -237,6 +240,61 @@ def time_workload(ce, workload, op, reduction, steps, warmup, log):
     return res
 
 
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def time_linear(ce, op, steps, warmup, log, chunk=0):
+    """Linear + cross-entropy on the LM-head linear workload: TFLOP/s of the
+    algorithmic GEMM work (forward 2MVD; forward + backward 6MVD -- the
+    backward's recomputation of the logits is not counted) over the call's
+    HIP-event time, against the bf16 MFMA peak; and, for context, one plain
+    bf16 GEMM of the logits (torch.matmul, the same library) timed alike."""
+    import torch
+    from softmax_cross_entropy_fwd_amd import inputs
+    c = inputs.LINEAR_CONFIGS["lmhead_linear"]
+    M, D, V = c["M"], c["D"], c["V"]
+    dev = torch.device("cuda:0")
+    h, w, t = inputs.make_linear(M, D, V, c["sigma"], c["seed"], device=dev)
+    nbytes = int(ce.load_library().ce_linear_workspace_bytes(M, D, V, chunk))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    fn = {"fwd": lambda: ce.ce_linear_fwd(h, w, t, "mean", chunk=chunk, workspace=ws),
+          "fwd_bwd": lambda: ce.ce_linear_fwd_bwd(h, w, t, "mean", chunk=chunk, workspace=ws)}[op]
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(f, n, nw):
+        for _ in range(nw):
+            f()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for a, b in ev:
+            a.record(stream)
+            f()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / n
+
+    ms = timed(fn, steps, warmup)
+    flops = (2 if op == "fwd" else 6) * M * V * D
+    gemm_ms = timed(lambda: torch.matmul(h, w.t()), max(3, steps // 2), 2)
+    chunk_cols = int(ce.load_library().ce_linear_chunk(M, D, V, chunk))
+    res = {
+        "workload": "lmhead_linear", "op": "linear_" + op, "M": M, "D": D, "V": V,
+        "storage": "bf16", "chunk": chunk_cols, "workspace_MB": round(nbytes / 1e6, 1),
+        "full_logits_MB": round(M * V * 2 / 1e6, 1),
+        "kernel_ms_avg": ms, "alg_TFLOPs": flops / (ms * 1e-3) / 1e12,
+        "logits_gemm_ms": gemm_ms, "logits_gemm_TFLOPs": 2 * M * V * D / (gemm_ms * 1e-3) / 1e12,
+    }
+    res["frac_of_peak"] = res["alg_TFLOPs"] / PEAK_BF16_TFLOPS
+    log("linear %s: %.3f ms/call, %.1f TFLOP/s = %.1f%% of bf16 peak; one logits GEMM %.3f ms "
+        "(%.1f TFLOP/s); chunk %d columns, workspace %.0f MB vs %.0f MB of bf16 logits" % (
+            op, ms, res["alg_TFLOPs"], 100 * res["frac_of_peak"], gemm_ms,
+            res["logits_gemm_TFLOPs"], chunk_cols, nbytes / 1e6, M * V * 2 / 1e6))
+    del h, w, t, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(workload, op, reduction, log, budget_s=20.0):
     """The fp64 oracle over the whole workload, repeated until ~3 s have passed
     (each pass is bounded by the budget), on every host core OpenMP gives it."""
@@ -271,13 +329,61 @@ def cpu_baseline(workload, op, reduction, log, budget_s=20.0):
                       % (workload, rows, V, dtype, op, reduction, reps, el, rows * reps / el)}
 
 
+def linear_cpu_baseline(log, rows=2):
+    """The oracle's linear + cross-entropy forward on a bounded sample of the
+    LM-head linear workload (a few rows: each is V x D = 537M products)."""
+    import torch
+    import oracle
+    from softmax_cross_entropy_fwd_amd import inputs
+    c = inputs.LINEAR_CONFIGS["lmhead_linear"]
+    M, D, V = c["M"], c["D"], c["V"]
+    h, w, t = inputs.make_linear(M, D, V, c["sigma"], c["seed"])
+    hb, wb = inputs.host_bits(h[:rows]), inputs.host_bits(w)
+    t0 = time.perf_counter()
+    oracle.linear_ce(hb, wb, t[:rows].numpy(), "none")
+    el = time.perf_counter() - t0
+    val = 2.0 * rows * V * D / el / 1e12
+    log("cpu oracle (linear): %d rows in %.2f s = %.4f TFLOP/s" % (rows, el, val))
+    return {"value": val, "unit": "TFLOP/s", "cores": min(rows, oracle.num_threads()),
+            "kind": "oracle",
+            "sample": "forward of %d rows of the lmhead_linear workload (%d x %d x %d bf16), %.1f s"
+                      % (rows, M, D, V, el)}
+
+
+def linear_main(ce, args, log):
+    op = args.op or "fwd_bwd"
+    if op not in ("fwd", "fwd_bwd"):
+        print("lmhead_linear takes --op fwd or fwd_bwd", file=sys.stderr)
+        sys.exit(2)
+    steps = max(1, args.steps // 20) if args.steps == 200 else args.steps
+    r = time_linear(ce, op, steps, max(1, min(args.warmup, 3)), log)
+    cpu = None if args.no_cpu else linear_cpu_baseline(log)
+    line = {
+        "metric": "linear + CE %s TFLOP/s (algorithmic GEMM flops / call time), lmhead_linear "
+                  "%dx%dx%d bf16" % (op, r["M"], r["D"], r["V"]),
+        "value": round(r["alg_TFLOPs"], 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": max(1, min(args.warmup, 3)), "ms_per_step": round(r["kernel_ms_avg"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0, 1) hidden states, N(0, 4/D) weight, uniform targets)",
+        "config": {"workload": "lmhead_linear", "M": r["M"], "D": r["D"], "V": r["V"],
+                   "op": op, "reduction": "mean", "chunk": r["chunk"]},
+        "roofline": {"bound": "mfma", "achieved": round(r["alg_TFLOPs"], 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(r["frac_of_peak"], 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "also": [{k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()}],
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="classifier")
-    ap.add_argument("--op", default=None, choices=[None] + OPS)
+    ap.add_argument("--op", default=None, choices=[None] + OPS,
+                    help="for --workload lmhead_linear: fwd or fwd_bwd")
     ap.add_argument("--reduction", default=None, choices=[None, "mean", "none", "sum"])
     ap.add_argument("--no-extra", action="store_true", help="skip the extra lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -316,6 +422,9 @@ def main():
         sys.exit(1)
     ce.load_library()
     from softmax_cross_entropy_fwd_amd import inputs
+    if args.workload in inputs.LINEAR_CONFIGS:
+        linear_main(ce, args, log)
+        return
     c = inputs.CONFIGS[args.workload]
     op = args.op or c["ops"][0]
     red = args.reduction or c["reductions"][0]
@@ -332,6 +441,8 @@ def main():
                         ("stress", "fwd"), ("stress", "fwd_bwd"), ("skinny", "fwd")):
             also.append(time_workload(ce, wl, eop, "mean", max(20, args.steps // 5),
                                       max(3, args.warmup // 5), log))
+        for lop in ("fwd", "fwd_bwd"):
+            also.append(time_linear(ce, lop, max(5, args.steps // 20), 2, log))
     traffic = load_traffic(args.workload, op, red)
     cpu = None if args.no_cpu else cpu_baseline(args.workload, op, red, log)
 

@@ -47,8 +47,9 @@ extern "C" {
 
 /*
  * The vocabulary chunk (columns per chunk) the calls use for these sizes
- * when given chunk == 0: whole multiples of 256, the chunk buffers of about
- * 1 GiB at most.  A given chunk is rounded up to a multiple of 256.
+ * when given chunk == 0: a multiple of 256, at least 1024, with the fp32
+ * logits chunk (M * C * 4 bytes) near 128 MiB.  A given chunk is rounded up
+ * to a multiple of 256; no chunk exceeds V rounded up to 256.
  */
 int64_t ce_linear_chunk(int64_t M, int64_t D, int64_t V, int64_t chunk);
 

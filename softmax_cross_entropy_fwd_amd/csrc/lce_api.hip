@@ -19,7 +19,12 @@
 namespace {
 
 constexpr int64_t kChunkAlign = 256;         // columns
-constexpr int64_t kChunkBytes = 1LL << 30;   // default budget of the two chunk buffers
+// Default chunk: its fp32 logits take about 128 MiB, half the last-level
+// cache, so the statistics and gradient passes mostly read what the GEMM just
+// wrote (measured on the 4096 x 4096 x 131072 workload: 8192 columns, forward
+// 3.79 ms and forward + backward 15.5 ms, against 4.26 / 16.4 ms with 43520).
+constexpr int64_t kChunkBytes = 128LL << 20;
+constexpr int64_t kMinChunk = 1024;
 
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
@@ -30,10 +35,10 @@ int64_t chunk_for(int64_t M, int64_t V, int64_t chunk)
     if (chunk > 0) {
         C = (chunk + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
     } else {
-        const int64_t per_col = 6 * (M > 0 ? M : 1);   // fp32 logits + bf16 gradient
+        const int64_t per_col = 4 * (M > 0 ? M : 1);   // fp32 logits
         C = kChunkBytes / per_col / kChunkAlign * kChunkAlign;
-        if (C < kChunkAlign)
-            C = kChunkAlign;
+        if (C < kMinChunk)
+            C = kMinChunk;
     }
     return C < vmax ? C : vmax;
 }

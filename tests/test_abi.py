@@ -258,7 +258,8 @@ def call_linear(lib, fn="ce_linear_fwd_bwd", H=FAKE, W=FAKE + (1 << 30), t=FAKE 
 
 
 def test_linear_chunk_and_workspace(lib):
-    assert lib.ce_linear_chunk(4096, 4096, 131072, 0) == (1 << 30) // (6 * 4096) // 256 * 256
+    assert lib.ce_linear_chunk(4096, 4096, 131072, 0) == 8192
+    assert lib.ce_linear_chunk(1 << 20, 64, 131072, 0) == 1024   # at least 1024 columns
     assert lib.ce_linear_chunk(4, 8, 300, 0) == 512            # the whole vocabulary, rounded
     assert lib.ce_linear_chunk(4, 8, 3000, 100) == 256         # rounded up to 256 columns
     assert lib.ce_linear_chunk(-1, 8, 300, 0) == 0
