@@ -81,7 +81,8 @@ int pow2ceil(int64_t n)
 // Mapping and tile for a row of nvec 16-byte vectors (worst case over rows),
 // from measurements on MI355X:
 //  - rows up to 16 KB sit in the registers of 1..64 lanes (rows kernel);
-//  - longer rows are streamed by a 16- or 8-wave workgroup for the forward;
+//  - longer rows are streamed for the forward: by one wavefront per row just
+//    past 16 KB, then by 4-, 8- or 16-wave workgroups as the rows grow;
 //  - the fused backward keeps rows up to 256 KB in the registers of a
 //    16-wave workgroup (one HBM read per element), longer ones re-read.
 void choose_shape(int64_t nvec, bool bwd, int *kind, int *a, int *b, int *nbuf)
@@ -120,9 +121,18 @@ void choose_shape(int64_t nvec, bool bwd, int *kind, int *a, int *b, int *nbuf)
         *kind = cek::KIND_WG;
         *a = 16;
         *b = nvec <= 4096 ? 4 : nvec <= 8192 ? 8 : nvec <= 12288 ? 12 : 16;
+    } else if (!bwd && nvec <= 1536) {
+        // just past the register rows: one row per wavefront wastes least
+        *kind = cek::KIND_WSTREAM;
+        *a = 1;
+        *b = 4;
     } else {
+        // chunks of W*64*4 vectors; more, smaller workgroups per CU until the
+        // rows are long enough to keep a wide one busy (measured: 6283
+        // vectors 5.2 TB/s with W=4 against 4.7 with W=8; 15000 vectors 5.6
+        // with W=16 against 5.4 with W=8)
         *kind = cek::KIND_STREAM;
-        *a = nvec >= 16384 ? 16 : 8;
+        *a = nvec >= 14336 ? 16 : (!bwd && nvec < 8192) ? 4 : 8;
         *b = 4;
     }
 }
