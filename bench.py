@@ -169,13 +169,15 @@ def summarize_pmc(fetch_csv, write_csv, workload, op, reduction, kernel_prefix, 
     return "\n".join(lines) + "\n"
 
 
-def time_workload(ce, workload, op, reduction, steps, warmup, log):
+def time_workload(ce, workload, op, reduction, steps, warmup, log, M=None, V=None):
+    """One operation on one workload (M and V may override its sizes, e.g. a
+    shard's shape), timed per launch with HIP events on the launch stream."""
     import torch
     from softmax_cross_entropy_fwd_amd import inputs
     c = inputs.CONFIGS[workload]
-    M, V, dtype = c["M"], c["V"], c["dtype"]
+    M, V, dtype = M or c["M"], V or c["V"], c["dtype"]
     dev = torch.device("cuda:0")
-    x0, t = inputs.make_config(workload, device=dev)
+    x0, t = inputs.make_config(workload, device=dev, M=M, V=V)
     nbytes = x0.numel() * x0.element_size()
     # read-only ops rotate over >= 1 GiB of inputs; the others write a buffer
     # as large as the logits, which already exceeds the last-level cache
@@ -220,12 +222,14 @@ def time_workload(ce, workload, op, reduction, steps, warmup, log):
     wall = time.perf_counter() - w0
     ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_ms = sum(ms) / len(ms)
+    med_ms = sorted(ms)[len(ms) // 2]
     ab = alg_bytes(M, V, dtype, op, reduction)
     has_loss = op in ("fwd", "fwd_lse", "fwd_bwd") and reduction != "none"
     res = {
-        "workload": workload, "op": op, "reduction": reduction, "M": M, "V": V,
+        "workload": workload if (M, V) == (c["M"], c["V"]) else "%s_%dx%d" % (workload, M, V),
+        "op": op, "reduction": reduction, "M": M, "V": V,
         "storage": dtype, "plan": plan,
-        "kernel_ms_avg": avg_ms, "kernel_ms_min": min(ms),
+        "kernel_ms_avg": avg_ms, "kernel_ms_median": med_ms, "kernel_ms_min": min(ms),
         "wall_ms_per_step": 1e3 * wall / steps,
         "alg_bytes_per_launch": ab,
         "alg_GBps": ab / (avg_ms * 1e-3) / 1e9,
@@ -295,6 +299,75 @@ def time_linear(ce, op, steps, warmup, log, chunk=0):
     return res
 
 
+def measure_ceilings(log):
+    """What plain kernels reach on this machine (the probe library): a read-only
+    stream and a copy over 4 GiB, best of a few launch shapes, in GB/s."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "softmax_cross_entropy_fwd_amd", "libce_probe.so"))
+    lib.probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                               ctypes.c_int, ctypes.c_void_p]
+    nb = 4 << 30
+    buf = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+    buf.fill_(1)
+    out = torch.empty(1 << 16, dtype=torch.float32, device="cuda:0")
+    st = torch.cuda.current_stream()
+
+    def best(fn, n=5):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            fn()
+            b.record(st)
+            torch.cuda.synchronize()
+            t.append(a.elapsed_time(b))
+        return min(t)
+
+    read = max(nb / best(lambda: lib.probe_read(buf.data_ptr(), nb, g, u, blk, out.data_ptr(),
+                                                st.cuda_stream)) / 1e6
+               for g, u, blk in ((1024, 8, 256), (512, 4, 1024), (2048, 8, 256)))
+    half = nb // 2
+    copy = max(2 * half / best(lambda: lib.probe_copy(buf.data_ptr() + half, buf.data_ptr(), half,
+                                                       g, u, st.cuda_stream)) / 1e6
+               for g, u in ((4096, 104), (2048, 8), (4096, 4)))
+    del buf, out
+    torch.cuda.empty_cache()
+    log("measured ceilings: read %.0f GB/s, copy %.0f GB/s (read + write)" % (read, copy))
+    return {"read_GBps": round(read, 1), "copy_GBps": round(copy, 1),
+            "how": "probe/bw_probe.hip over 4 GiB (copy: 2 GiB each way), best launch shape"}
+
+
+def time_tiny(ce, log, calls=1000):
+    """The tiny workload is launch-bound: 1000 back-to-back calls timed as a
+    whole, in microseconds per call."""
+    import torch
+    from softmax_cross_entropy_fwd_amd import inputs
+    x, t = inputs.make_config("tiny", device="cuda:0")
+    out = torch.empty((), dtype=torch.float32, device="cuda:0")
+    for _ in range(100):
+        ce.ce_fwd(x, t, "mean", out=out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    a.record()
+    for _ in range(calls):
+        ce.ce_fwd(x, t, "mean", out=out)
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    us = a.elapsed_time(b) * 1e3 / calls
+    log("tiny fwd mean: %.2f us per call over %d back-to-back calls (wall %.2f us)" % (
+        us, calls, wall * 1e6 / calls))
+    return {"workload": "tiny", "op": "fwd", "reduction": "mean", "M": 64, "V": 1000,
+            "us_per_call": us, "wall_us_per_call": wall * 1e6 / calls, "calls": calls,
+            "note": "launch-bound; no roofline claim"}
+
+
 def cpu_baseline(workload, op, reduction, log, budget_s=20.0):
     """The fp64 oracle over the whole workload, repeated until ~3 s have passed
     (each pass is bounded by the budget), on every host core OpenMP gives it."""
@@ -322,11 +395,25 @@ def cpu_baseline(workload, op, reduction, log, budget_s=20.0):
             break
     ab = alg_bytes(rows, V, dtype, op, reduction)
     val = ab * reps / el / 1e9
+    threads = oracle.num_threads()
     log("cpu oracle: %d pass(es) over %d rows in %.2f s = %.3f GB/s on %d threads" % (
-        reps, rows, el, val, oracle.num_threads()))
-    return {"value": val, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+        reps, rows, el, val, threads))
+    # the same on one thread, over a tenth of the rows
+    oracle.set_num_threads(1)
+    r1 = max(1, rows // 10)
+    t0 = time.perf_counter()
+    if op == "fwd":
+        oracle.fwd(xb[:r1], tn[:r1], dtype=dtype, reduction=reduction)
+    else:
+        oracle.grad_rows(xb[:r1], tn[:r1], dtype=dtype, c=1.0 / r1)
+    el1 = time.perf_counter() - t0
+    oracle.set_num_threads(threads)
+    val1 = alg_bytes(r1, V, dtype, op, reduction) / el1 / 1e9
+    log("cpu oracle, one thread: %d rows in %.2f s = %.3f GB/s" % (r1, el1, val1))
+    return {"value": val, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": "the whole %s workload (%d x %d %s, %s %s), %d pass(es), %.1f s; %.3g rows/s"
-                      % (workload, rows, V, dtype, op, reduction, reps, el, rows * reps / el)}
+                      % (workload, rows, V, dtype, op, reduction, reps, el, rows * reps / el),
+            "single_thread": {"value": val1, "unit": "GB/s", "rows": r1, "seconds": el1}}
 
 
 def linear_cpu_baseline(log, rows=2):
@@ -441,8 +528,15 @@ def main():
                         ("stress", "fwd"), ("stress", "fwd_bwd"), ("skinny", "fwd")):
             also.append(time_workload(ce, wl, eop, "mean", max(20, args.steps // 5),
                                       max(3, args.warmup // 5), log))
+        # one GPU's share of a sharded LM head: rows (M / 8) and vocabulary (V / 8)
+        also.append(time_workload(ce, "lmhead", "fwd", "mean", 50, 5, log, M=2048))
+        also.append(time_workload(ce, "lmhead", "fwd_bwd", "mean", 50, 5, log, M=2048))
+        also.append(time_workload(ce, "lmhead", "fwd_lse", "none", 50, 5, log, V=16384))
+        also.append(time_tiny(ce, log))
         for lop in ("fwd", "fwd_bwd"):
             also.append(time_linear(ce, lop, max(5, args.steps // 20), 2, log))
+    # after the timed lines, so the 4 GiB probe buffers do not precede them
+    ceilings = None if args.no_extra else measure_ceilings(log)
     traffic = load_traffic(args.workload, op, red)
     cpu = None if args.no_cpu else cpu_baseline(args.workload, op, red, log)
 
@@ -468,6 +562,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(head["alg_GBps"], 2), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(head["frac_of_peak"], 4),
                      "traffic": traffic},
+        "ms_per_step_median": round(head["kernel_ms_median"], 5),
+        "ms_per_step_min": round(head["kernel_ms_min"], 5),
+        "measured_ceiling": None if ceilings is None else dict(
+            ceilings, frac_of_read=round(head["alg_GBps"] / ceilings["read_GBps"], 4)),
         "cpu_baseline": cpu,
         "also": [{k: (round(v, 5) if isinstance(v, float) else v) for k, v in a.items()}
                  for a in also],

@@ -76,6 +76,8 @@ def _load():
     u16p = ctypes.POINTER(ctypes.c_uint16)
     lib.oracle_linear_ce.argtypes = [u16p, u16p, _i64p, i64, i64, i64, i32, _dp, _dp, _dp, _dp, _dp]
     lib.oracle_linear_ce.restype = i32
+    lib.oracle_set_num_threads.argtypes = [i32]
+    lib.oracle_set_num_threads.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i32
     _lib = lib
@@ -263,3 +265,8 @@ def round_to(values, dtype):
 
 def num_threads():
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n):
+    """Threads of the oracle's row loops from now on (for timing)."""
+    _load().oracle_set_num_threads(int(n))

@@ -467,6 +467,18 @@ int oracle_linear_ce(const uint16_t *H, const uint16_t *W, const int64_t *target
     return 0;
 }
 
+/* Sets the number of OpenMP threads later parallel regions use (n >= 1). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Number of OpenMP threads a parallel region uses (for reporting). */
 int oracle_num_threads(void)
 {
