@@ -64,7 +64,7 @@ KernelRef pick_table(int kind, int a, int b, int nbuf)
     } else if (kind == KIND_WG) {
         CE_WG(16, 4) CE_WG(16, 8) CE_WG(16, 12) CE_WG(16, 16)
     } else if (kind == KIND_STREAM && !EXACT) {
-        CE_STREAM(8, 4) CE_STREAM(16, 4)
+        CE_STREAM(4, 4) CE_STREAM(8, 4) CE_STREAM(16, 4)
     }
     return KernelRef{nullptr, 0};
 }
