@@ -24,7 +24,9 @@ GB/s = bytes the method must move / kernel time.  The same line carries:
                 forward; each timed the same way; and linear + cross-entropy
                 (logits = hidden @ weight.T, bf16 [4096, 4096] x [131072, 4096],
                 taken in vocabulary chunks) forward and forward + backward in
-                TFLOP/s against the bf16 MFMA peak.
+                TFLOP/s against the bf16 MFMA peak; with --extra-shapes, one
+                GPU's share of a row- and a vocabulary-sharded LM head and the
+                tiny workload's microseconds per call.
 
 Inputs rotate over enough buffers (>= 1 GiB in total) that no launch finds its
 rows in the 256 MB last-level cache; the in-place backward restores its logits
@@ -165,6 +167,30 @@ def summarize_pmc(fetch_csv, write_csv, workload, op, reduction, kernel_prefix, 
         "fetch_scale = %.4f" % f_scale,
         "write_scale = %.4f" % w_scale,
         "hbm_bytes_per_launch = %.0f" % hbm,
+    ]
+    return "\n".join(lines) + "\n"
+
+
+def summarize_util(csv_path, workload, op, reduction, kernel_prefix, command):
+    """One rocprofv3 --pmc pass of VALUBusy, TCC_HIT_sum and TCC_MISS_sum
+    (counter_collection.csv) as a short summary for the kernel."""
+    import csv
+    import statistics
+    vals = {}
+    for r in csv.DictReader(open(csv_path)):
+        if kernel_prefix in r["Kernel_Name"]:
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    med = {k: statistics.median(v) for k, v in vals.items()}
+    hit, miss = med.get("TCC_HIT_sum", 0.0), med.get("TCC_MISS_sum", 0.0)
+    lines = [
+        "# VALU busy and L2 hit rate of the %s %s (%s) kernel, from rocprofv3 counters"
+        % (workload, op, reduction),
+        "# command: %s" % command,
+        "kernel = %s" % kernel_prefix,
+        "kernel_source_sha = %s" % kernel_source_hash(),
+        "dispatches = %d" % len(vals.get("VALUBusy", [])),
+        "valu_busy_percent = %.1f" % med.get("VALUBusy", float("nan")),
+        "l2_hit_percent = %.1f" % (100.0 * hit / (hit + miss) if hit + miss else float("nan")),
     ]
     return "\n".join(lines) + "\n"
 
@@ -473,6 +499,10 @@ def main():
                     help="for --workload lmhead_linear: fwd or fwd_bwd")
     ap.add_argument("--reduction", default=None, choices=[None, "mean", "none", "sum"])
     ap.add_argument("--no-extra", action="store_true", help="skip the extra lines")
+    ap.add_argument("--extra-shapes", action="store_true",
+                    help="also time one GPU's share of a row- and a vocabulary-sharded LM head "
+                         "and the tiny workload's per-call time (these share kernels with the "
+                         "other lines, so they are off in profiled runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -480,6 +510,8 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL"),
                     help="write the traffic summary from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--pmc-command", default="", help="the profiled command, for the summary")
+    ap.add_argument("--summarize-util", nargs=2, metavar=("CSV", "KERNEL"),
+                    help="write the VALU-busy / L2-hit summary from one rocprofv3 --pmc run and exit")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -490,6 +522,18 @@ def main():
         text = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, op,
                              red, args.summarize_pmc[2], args.pmc_command)
         open(traffic_path(args.workload, op, red), "w").write(text)
+        print(text)
+        return
+
+    if args.summarize_util:
+        from softmax_cross_entropy_fwd_amd import inputs as _inp
+        c = _inp.CONFIGS[args.workload]
+        op = args.op or c["ops"][0]
+        red = args.reduction or c["reductions"][0]
+        text = summarize_util(args.summarize_util[0], args.workload, op, red,
+                              args.summarize_util[1], args.pmc_command)
+        path = os.path.join(ROOT, "profiles", "util_%s_%s_%s.txt" % (args.workload, op, red))
+        open(path, "w").write(text)
         print(text)
         return
 
@@ -528,11 +572,13 @@ def main():
                         ("stress", "fwd"), ("stress", "fwd_bwd"), ("skinny", "fwd")):
             also.append(time_workload(ce, wl, eop, "mean", max(20, args.steps // 5),
                                       max(3, args.warmup // 5), log))
-        # one GPU's share of a sharded LM head: rows (M / 8) and vocabulary (V / 8)
-        also.append(time_workload(ce, "lmhead", "fwd", "mean", 50, 5, log, M=2048))
-        also.append(time_workload(ce, "lmhead", "fwd_bwd", "mean", 50, 5, log, M=2048))
-        also.append(time_workload(ce, "lmhead", "fwd_lse", "none", 50, 5, log, V=16384))
-        also.append(time_tiny(ce, log))
+        if args.extra_shapes:
+            # one GPU's share of a sharded LM head: rows (M / 8) and vocabulary
+            # (V / 8); the tiny workload's per-call time
+            also.append(time_workload(ce, "lmhead", "fwd", "mean", 50, 5, log, M=2048))
+            also.append(time_workload(ce, "lmhead", "fwd_bwd", "mean", 50, 5, log, M=2048))
+            also.append(time_workload(ce, "lmhead", "fwd_lse", "none", 50, 5, log, V=16384))
+            also.append(time_tiny(ce, log))
         for lop in ("fwd", "fwd_bwd"):
             also.append(time_linear(ce, lop, max(5, args.steps // 20), 2, log))
     # after the timed lines, so the 4 GiB probe buffers do not precede them
