@@ -195,7 +195,8 @@ def summarize_util(csv_path, workload, op, reduction, kernel_prefix, command):
     return "\n".join(lines) + "\n"
 
 
-def time_workload(ce, workload, op, reduction, steps, warmup, log, M=None, V=None):
+def time_workload(ce, workload, op, reduction, steps, warmup, log, M=None, V=None,
+                  cpu_sample=False):
     """One operation on one workload (M and V may override its sizes, e.g. a
     shard's shape), timed per launch with HIP events on the launch stream."""
     import torch
@@ -262,6 +263,8 @@ def time_workload(ce, workload, op, reduction, steps, warmup, log, M=None, V=Non
         "rows_per_s": M / (avg_ms * 1e-3),
         "loss": float(out.float().mean().item()) if has_loss else None,
     }
+    if cpu_sample:
+        res["cpu_oracle"] = oracle_sample(workload, op, reduction, M, V)
     res["frac_of_peak"] = res["alg_GBps"] / PEAK_GBS
     log("  %.4f ms/launch (min %.4f), %.1f GB/s = %.1f%% of 8 TB/s, %.3g rows/s" % (
         avg_ms, min(ms), res["alg_GBps"], 100 * res["frac_of_peak"], res["rows_per_s"]))
@@ -392,6 +395,35 @@ def time_tiny(ce, log, calls=1000):
     return {"workload": "tiny", "op": "fwd", "reduction": "mean", "M": 64, "V": 1000,
             "us_per_call": us, "wall_us_per_call": wall * 1e6 / calls, "calls": calls,
             "note": "launch-bound; no roofline claim"}
+
+
+def oracle_sample(workload, op, reduction, M=None, V=None, budget_s=1.0):
+    """The oracle for one line's operation on a bounded sample of its rows
+    (drawn by the same generator; rows doubled until about budget_s), on all
+    host threads: GB/s of the line's algorithmic bytes for those rows."""
+    import oracle
+    from softmax_cross_entropy_fwd_amd import inputs
+    c = inputs.CONFIGS[workload]
+    Mf, V, dtype = M or c["M"], V or c["V"], c["dtype"]
+    rows = max(1, min(Mf, 2 ** 20 // V))
+    while True:
+        x, t = inputs.make_config(workload, device="cpu", M=rows, V=V)
+        xb, tn = inputs.host_bits(x), t.numpy()
+        t0 = time.perf_counter()
+        if op in ("fwd", "fwd_lse"):
+            oracle.loss_rows(xb, tn, dtype=dtype)
+        elif op in ("fwd_bwd", "bwd"):
+            oracle.loss_rows(xb, tn, dtype=dtype)
+            oracle.grad_rows(xb, tn, dtype=dtype, c=1.0 / rows)
+        else:
+            oracle.softmax_rows(xb, dtype=dtype, log=op == "log_softmax")
+        el = time.perf_counter() - t0
+        if el >= budget_s / 4 or rows >= Mf:
+            break
+        rows = min(Mf, rows * 4)
+    return {"value": alg_bytes(rows, V, dtype, op, reduction) / el / 1e9, "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d rows of the line's workload, %.2f s" % (rows, el)}
 
 
 def cpu_baseline(workload, op, reduction, log, budget_s=20.0):
@@ -571,7 +603,7 @@ def main():
                         ("lmhead", "softmax"), ("classifier", "bwd"), ("classifier", "softmax"),
                         ("stress", "fwd"), ("stress", "fwd_bwd"), ("skinny", "fwd")):
             also.append(time_workload(ce, wl, eop, "mean", max(20, args.steps // 5),
-                                      max(3, args.warmup // 5), log))
+                                      max(3, args.warmup // 5), log, cpu_sample=not args.no_cpu))
         if args.extra_shapes:
             # one GPU's share of a sharded LM head: rows (M / 8) and vocabulary
             # (V / 8); the tiny workload's per-call time
@@ -579,8 +611,10 @@ def main():
             also.append(time_workload(ce, "lmhead", "fwd_bwd", "mean", 50, 5, log, M=2048))
             also.append(time_workload(ce, "lmhead", "fwd_lse", "none", 50, 5, log, V=16384))
             also.append(time_tiny(ce, log))
+        lin_cpu = None if args.no_cpu else linear_cpu_baseline(log, rows=1)
         for lop in ("fwd", "fwd_bwd"):
             also.append(time_linear(ce, lop, max(5, args.steps // 20), 2, log))
+            also[-1]["cpu_oracle"] = lin_cpu
     # after the timed lines, so the 4 GiB probe buffers do not precede them
     ceilings = None if args.no_extra else measure_ceilings(log)
     traffic = load_traffic(args.workload, op, red)
