@@ -153,6 +153,15 @@ def _check(logits, targets):
         raise ValueError("targets must be on the logits' device with M entries")
 
 
+def _invoke(fn, dev, args):
+    """Calls a library entry point with dev current (switching only if needed)."""
+    import torch
+    if torch.cuda.current_device() == dev.index:
+        return fn(*args)
+    with torch.cuda.device(dev):
+        return fn(*args)
+
+
 def _call(fn_name, logits, targets, reduction, out, workspace, lse=None):
     import torch
     lib = load_library()
@@ -162,19 +171,21 @@ def _call(fn_name, logits, targets, reduction, out, workspace, lse=None):
     dev = logits.device
     if out is None:
         out = torch.empty((M,) if red == CE_NONE else (), dtype=torch.float32, device=dev)
+    else:
+        _check_rows(out, M if red == CE_NONE else 1, dev, "out")
     stream = torch.cuda.current_stream(dev)
-    nbytes = int(lib.ce_workspace_bytes(M, V, _dtype_code(logits), red))
+    code = _dtype_code(logits)
+    nbytes = int(lib.ce_workspace_bytes(M, V, code, red))
     if nbytes and workspace is None:
         workspace = workspace_for(dev, stream, nbytes)
     ws_ptr = workspace.data_ptr() if nbytes else None
     ws_len = workspace.numel() * workspace.element_size() if nbytes else 0
-    args = [logits.data_ptr(), targets.data_ptr(), M, V, _dtype_code(logits), red,
+    args = [logits.data_ptr(), targets.data_ptr(), M, V, code, red,
             out.data_ptr() if out.numel() else None]
     if fn_name == "ce_fwd_lse":
         _check_rows(lse, M, dev, "lse")
         args.append(lse.data_ptr() if M else None)
-    with torch.cuda.device(dev):
-        rc = getattr(lib, fn_name)(*args, ws_ptr, ws_len, stream.cuda_stream)
+    rc = _invoke(getattr(lib, fn_name), dev, args + [ws_ptr, ws_len, stream.cuda_stream])
     if rc:
         raise CEError(rc, fn_name)
     return out
@@ -232,11 +243,10 @@ def ce_bwd(logits, targets, lse, reduction="mean", dloss=None, grad=None, worksp
     _check_like(grad, logits, "grad")
     stream = torch.cuda.current_stream(dev)
     ws_ptr, ws_len = _workspace(lib, logits, red, workspace)
-    with torch.cuda.device(dev):
-        rc = lib.ce_bwd(logits.data_ptr(), targets.data_ptr(), lse.data_ptr() if M else None,
-                        dloss.data_ptr() if dloss is not None else None, M, V,
-                        _dtype_code(logits), red, grad.data_ptr() if M else None,
-                        ws_ptr, ws_len, stream.cuda_stream)
+    rc = _invoke(lib.ce_bwd, dev,
+                 [logits.data_ptr(), targets.data_ptr(), lse.data_ptr() if M else None,
+                  dloss.data_ptr() if dloss is not None else None, M, V, _dtype_code(logits),
+                  red, grad.data_ptr() if M else None, ws_ptr, ws_len, stream.cuda_stream])
     if rc:
         raise CEError(rc, "ce_bwd")
     return grad
@@ -258,11 +268,11 @@ def ce_softmax(logits, log_softmax=False, out=None, lse=None, workspace=None):
         _check_rows(lse, M, dev, "lse")
     stream = torch.cuda.current_stream(dev)
     ws_ptr, ws_len = _workspace(lib, logits, CE_NONE, workspace)
-    with torch.cuda.device(dev):
-        rc = lib.ce_softmax(logits.data_ptr(), M, V, _dtype_code(logits), int(bool(log_softmax)),
-                            out.data_ptr() if M else None,
-                            lse.data_ptr() if (lse is not None and M) else None,
-                            ws_ptr, ws_len, stream.cuda_stream)
+    rc = _invoke(lib.ce_softmax, dev,
+                 [logits.data_ptr(), M, V, _dtype_code(logits), int(bool(log_softmax)),
+                  out.data_ptr() if M else None,
+                  lse.data_ptr() if (lse is not None and M) else None,
+                  ws_ptr, ws_len, stream.cuda_stream])
     if rc:
         raise CEError(rc, "ce_softmax")
     return out
@@ -298,9 +308,8 @@ def _linear(fn_name, hidden, weight, targets, reduction, chunk, workspace, bwd):
         dh = torch.empty((M, D), dtype=torch.float32, device=dev)
         dw = torch.empty((V, D), dtype=torch.float32, device=dev)
         args += [dh.data_ptr() if M else None, dw.data_ptr()]
-    with torch.cuda.device(dev):
-        rc = getattr(lib, fn_name)(*args, int(chunk), workspace.data_ptr(), ws_len,
-                                   stream.cuda_stream)
+    rc = _invoke(getattr(lib, fn_name), dev,
+                 args + [int(chunk), workspace.data_ptr(), ws_len, stream.cuda_stream])
     if rc:
         raise CEError(rc, fn_name)
     return (out, lse, dh, dw) if bwd else (out, lse)

@@ -519,3 +519,6 @@ def test_grad_with_upstream_gradient_matches_autograd(reduction):
     c = 1.0 / M if reduction == "mean" else 1.0
     _, g = oracle.grad_rows(x, t, c=c, d=dd, want64=True)
     np.testing.assert_allclose(g, w.grad.numpy(), rtol=1e-12, atol=1e-16)
+    # a block of rows further down takes the upstream gradients of those rows
+    _, gb = oracle.grad_rows(x, t, c=c, d=dd, row0=3, nrows=4, want64=True)
+    np.testing.assert_allclose(gb, w.grad.numpy()[3:7], rtol=1e-12, atol=1e-16)
