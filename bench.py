@@ -390,11 +390,32 @@ def time_tiny(ce, log, calls=1000):
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     us = a.elapsed_time(b) * 1e3 / calls
-    log("tiny fwd mean: %.2f us per call over %d back-to-back calls (wall %.2f us)" % (
-        us, calls, wall * 1e6 / calls))
+    # the same call captured in a HIP graph (the launch-bound case graphs are for)
+    ws = torch.empty(ce.ce_workspace_bytes(64, 1000, 0, "mean"), dtype=torch.uint8, device="cuda:0")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ce.ce_fwd(x, t, "mean", out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(10):
+            ce.ce_fwd(x, t, "mean", out=out, workspace=ws)
+    for _ in range(10):
+        graph.replay()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(calls // 10):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    gus = a.elapsed_time(b) * 1e3 / calls
+    log("tiny fwd mean: %.2f us per call over %d back-to-back calls (wall %.2f us); "
+        "%.2f us per call replayed from a HIP graph of 10 calls" % (
+            us, calls, wall * 1e6 / calls, gus))
     return {"workload": "tiny", "op": "fwd", "reduction": "mean", "M": 64, "V": 1000,
             "us_per_call": us, "wall_us_per_call": wall * 1e6 / calls, "calls": calls,
-            "note": "launch-bound; no roofline claim"}
+            "graph_us_per_call": gus, "note": "launch-bound; no roofline claim"}
 
 
 def oracle_sample(workload, op, reduction, M=None, V=None, budget_s=1.0):
