@@ -371,7 +371,7 @@ def measure_ceilings(log):
             "how": "probe/bw_probe.hip over 4 GiB (copy: 2 GiB each way), best launch shape"}
 
 
-def time_tiny(ce, log, calls=1000):
+def time_tiny(ce, log, calls=1000, cpu_sample=False):
     """The tiny workload is launch-bound: 1000 back-to-back calls timed as a
     whole, in microseconds per call."""
     import torch
@@ -413,9 +413,26 @@ def time_tiny(ce, log, calls=1000):
     log("tiny fwd mean: %.2f us per call over %d back-to-back calls (wall %.2f us); "
         "%.2f us per call replayed from a HIP graph of 10 calls" % (
             us, calls, wall * 1e6 / calls, gus))
-    return {"workload": "tiny", "op": "fwd", "reduction": "mean", "M": 64, "V": 1000,
-            "us_per_call": us, "wall_us_per_call": wall * 1e6 / calls, "calls": calls,
-            "graph_us_per_call": gus, "note": "launch-bound; no roofline claim"}
+    res = {"workload": "tiny", "op": "fwd", "reduction": "mean", "M": 64, "V": 1000,
+           "us_per_call": us, "wall_us_per_call": wall * 1e6 / calls, "calls": calls,
+           "graph_us_per_call": gus, "note": "launch-bound; no roofline claim"}
+    if cpu_sample:
+        # the oracle on the same inputs, on one thread and on all of them
+        import oracle
+        xb, tn = inputs.host_bits(x), t.cpu().numpy()
+        threads = oracle.num_threads()
+        for n, key in ((1, "cpu_oracle_1_thread_us"), (threads, "cpu_oracle_all_threads_us")):
+            oracle.set_num_threads(n)
+            reps, t0 = 0, time.perf_counter()
+            while time.perf_counter() - t0 < 0.5:
+                oracle.fwd(xb, tn, dtype="f32", reduction="mean")
+                reps += 1
+            res[key] = (time.perf_counter() - t0) * 1e6 / reps
+        oracle.set_num_threads(threads)
+        res["cpu_oracle_threads"] = threads
+        log("tiny on the oracle: %.1f us per call on 1 thread, %.1f us on %d" % (
+            res["cpu_oracle_1_thread_us"], res["cpu_oracle_all_threads_us"], threads))
+    return res
 
 
 def oracle_sample(workload, op, reduction, M=None, V=None, budget_s=1.0):
@@ -631,7 +648,7 @@ def main():
             also.append(time_workload(ce, "lmhead", "fwd", "mean", 50, 5, log, M=2048))
             also.append(time_workload(ce, "lmhead", "fwd_bwd", "mean", 50, 5, log, M=2048))
             also.append(time_workload(ce, "lmhead", "fwd_lse", "none", 50, 5, log, V=16384))
-            also.append(time_tiny(ce, log))
+            also.append(time_tiny(ce, log, cpu_sample=not args.no_cpu))
         lin_cpu = None if args.no_cpu else linear_cpu_baseline(log, rows=1)
         for lop in ("fwd", "fwd_bwd"):
             also.append(time_linear(ce, lop, max(5, args.steps // 20), 2, log))
