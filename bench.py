@@ -465,7 +465,7 @@ def oracle_sample(workload, op, reduction, M=None, V=None, budget_s=1.0):
 
 
 def cpu_baseline(workload, op, reduction, log, budget_s=20.0):
-    """The fp64 oracle over the whole workload, repeated until ~3 s have passed
+    """The fp64 oracle over the whole workload, repeated until ~10 s have passed
     (each pass is bounded by the budget), on every host core OpenMP gives it."""
     import numpy as np
     import torch
@@ -485,7 +485,7 @@ def cpu_baseline(workload, op, reduction, log, budget_s=20.0):
             oracle.grad_rows(xb[:rows], tn[:rows], dtype=dtype, c=1.0 / rows)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= 3.0 or el > budget_s:
+        if el >= 10.0 or el > budget_s:
             break
         if reps == 1 and el > budget_s / 4:
             break
