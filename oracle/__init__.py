@@ -73,6 +73,9 @@ def _load():
     lib.oracle_ce_grad_rows.restype = i32
     lib.oracle_softmax_rows.argtypes = [vp, i32, i64, i64, i64, i64, i32, i32, vp, _dp, _dp]
     lib.oracle_softmax_rows.restype = i32
+    lib.oracle_at_elements.argtypes = [vp, i32, _i64p, i64, i64, _dp, i64, _i64p, _i64p, i32,
+                                       ctypes.c_double, _dp, i32, vp, _dp]
+    lib.oracle_at_elements.restype = i32
     u16p = ctypes.POINTER(ctypes.c_uint16)
     lib.oracle_linear_ce.argtypes = [u16p, u16p, _i64p, i64, i64, i64, i32, _dp, _dp, _dp, _dp, _dp]
     lib.oracle_linear_ce.restype = i32
@@ -206,6 +209,46 @@ def softmax_rows(x, dtype="f32", log=False, row0=0, nrows=None, out_dtype=None,
     if with_lse:
         res += (lse,)
     return res[0] if len(res) == 1 else res
+
+
+_AT_OPS = {"grad": 0, "softmax": 1, "log_softmax": 2}
+
+
+def at_elements(x, lse, rows, cols, op="grad", dtype="f32", targets=None, c=1.0, d=None,
+                out_dtype=None, want64=False):
+    """The gradient (op "grad", scaled by c and d[i] as in grad_rows),
+    softmax or log-softmax at elements (rows[k], cols[k]) of x, from the fp64
+    row log-sum-exps lse [M] (as loss_rows(..., with_lse=True) gives them).
+    Returns values rounded once to the storage type (and the fp64 values if
+    want64)."""
+    lib = _load()
+    x, code = _prep(x, dtype)
+    M, V = x.shape
+    lse = np.ascontiguousarray(lse, dtype=np.float64)
+    rows = np.ascontiguousarray(np.broadcast_to(rows, np.shape(cols)), dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if lse.shape != (M,) or rows.shape != cols.shape or cols.ndim != 1:
+        raise ValueError("lse must be [M]; rows and cols 1-D of one length")
+    t = _targets(targets, M) if targets is not None else None
+    if op == "grad" and t is None:
+        raise ValueError("the gradient needs the targets")
+    if d is not None:
+        d = np.ascontiguousarray(d, dtype=np.float64)
+        if d.shape != (M,):
+            raise ValueError("d must hold one upstream gradient per row")
+    ocode = code if out_dtype is None else dtype_code(out_dtype)
+    n = cols.size
+    y = np.empty(n, dtype=np.float32 if ocode == F32 else np.uint16)
+    y64 = np.empty(n, dtype=np.float64) if want64 else None
+    rc = lib.oracle_at_elements(x.ctypes.data, code,
+                                t.ctypes.data_as(_i64p) if t is not None else None, M, V,
+                                lse.ctypes.data_as(_dp), n, rows.ctypes.data_as(_i64p),
+                                cols.ctypes.data_as(_i64p), _AT_OPS[op], float(c),
+                                d.ctypes.data_as(_dp) if d is not None else None, ocode,
+                                y.ctypes.data, y64.ctypes.data_as(_dp) if want64 else None)
+    if rc:
+        raise ValueError("oracle_at_elements: bad arguments")
+    return (y, y64) if want64 else y
 
 
 def linear_ce(h_bits, w_bits, targets, reduction="mean", grads=False):

@@ -391,6 +391,50 @@ int oracle_softmax_rows(const void *x, int dtype, int64_t M, int64_t V,
 }
 
 /*
+ * The gradient, softmax or log-softmax of single elements, from the row's
+ * log-sum-exp as oracle_ce_loss_rows returns it (every one of these outputs
+ * depends only on its own logit once lse_i is known, so a sample of a very
+ * long row needs one pass over the row, not one per output).  For k < n,
+ * element (rows[k], cols[k]) of the [M, V] matrix x:
+ *   op 0:  g = (exp(x_ij - lse_i) - [j == t_i]) * c d_i, the target term as
+ *          expm1(x_it - lse_i) * c d_i (same page, week 7, and the chain rule
+ *          for d as in oracle_ce_grad_rows; d may be NULL);
+ *   op 1:  exp(x_ij - lse_i);   op 2:  x_ij - lse_i   (week 1, the trace).
+ * lse has one entry per row of x.  Results go to out64[k] (fp64, may be
+ * NULL) and out[k] in out_dtype rounded once (may be NULL).
+ */
+int oracle_at_elements(const void *x, int dtype, const int64_t *targets,
+                       int64_t M, int64_t V, const double *lse, int64_t n,
+                       const int64_t *rows, const int64_t *cols, int op,
+                       double c, const double *d, int out_dtype, void *out,
+                       double *out64)
+{
+    if (!x || !lse || !rows || !cols || n < 0 || V < 1 || op < 0 || op > 2 ||
+        (op == 0 && !targets) || dtype < OR_F32 || dtype > OR_BF16 ||
+        out_dtype < OR_F32 || out_dtype > OR_BF16)
+        return -1;
+    for (int64_t k = 0; k < n; ++k)
+        if (rows[k] < 0 || rows[k] >= M || cols[k] < 0 || cols[k] >= V)
+            return -1;
+    for (int64_t k = 0; k < n; ++k) {
+        int64_t i = rows[k], j = cols[k];
+        double u = elem(row_ptr(x, dtype, i, V), dtype, j) - lse[i];
+        double v;
+        if (op == 0) {
+            double ci = d ? c * d[i] : c;
+            v = (j == targets[i] ? expm1(u) : exp(u)) * ci;
+        } else {
+            v = op == 1 ? exp(u) : u;
+        }
+        if (out64)
+            out64[k] = v;
+        if (out)
+            store_rounded(out, out_dtype, (size_t)k, v);
+    }
+    return 0;
+}
+
+/*
  * Linear + cross-entropy on bf16 H [M, D] and W [V, D] (bit patterns):
  * z_i = H_i W^T in fp64, then row_loss on z_i.  out: per-row losses (none)
  * or the reduced loss in out[0]; lse_out [M] (may be NULL).  When G is not

@@ -50,7 +50,9 @@ def widen(xb, dtype):
     return u.view(np.float32).astype(np.float64)
 
 
-def check_row_losses(got, want, xb, targets, dtype, rtol=LOSS_RTOL):
+def check_row_losses(got, want, xb, targets, dtype, rtol=LOSS_RTOL, m=None, xt=None):
+    """m, xt: the rows' max and target logit when given (for inputs too large
+    to widen on the host); else taken from xb."""
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     assert got.shape == want.shape
@@ -59,10 +61,14 @@ def check_row_losses(got, want, xb, targets, dtype, rtol=LOSS_RTOL):
     ok = ~nan_w
     if not ok.any():
         return 0.0
-    w = widen(xb[ok], dtype)
-    m = np.max(w, axis=1)
-    t = np.asarray(targets)[ok]
-    xt = w[np.arange(w.shape[0]), t]
+    if m is None:
+        w = widen(xb[ok], dtype)
+        m = np.max(w, axis=1)
+        t = np.asarray(targets)[ok]
+        xt = w[np.arange(w.shape[0]), t]
+    else:
+        m = np.asarray(m, dtype=np.float64)[ok]
+        xt = np.asarray(xt, dtype=np.float64)[ok]
     inf = np.isinf(want[ok])
     np.testing.assert_array_equal(got[ok][inf], want[ok][inf])
     fin = ~inf
@@ -157,7 +163,9 @@ def storage_ulp(values, dtype):
     return 2.0 ** (e - 7)
 
 
-def check_log_softmax(got_bits, want64, xb, dtype):
+def check_log_softmax(got_bits, want64, xb, dtype, m=None):
+    """m: the rows' max ([rows, 1]) when xb holds only some of each row's
+    columns; else taken from xb."""
     g = widen(np.asarray(got_bits), dtype)
     w = np.asarray(want64, dtype=np.float64)
     x = widen(np.asarray(xb), dtype)
@@ -166,8 +174,9 @@ def check_log_softmax(got_bits, want64, xb, dtype):
     inf_w = np.isinf(w)
     np.testing.assert_array_equal(g[inf_w], w[inf_w])
     fin = ~nan_w & ~inf_w
-    with np.errstate(invalid="ignore"):
-        m = np.max(x, axis=1, keepdims=True)
+    if m is None:
+        with np.errstate(invalid="ignore"):
+            m = np.max(x, axis=1, keepdims=True)
     scale = np.maximum(np.abs(np.broadcast_to(m, x.shape)), np.abs(np.where(np.isfinite(x), x, 0)))
     bound = 1e-5 * np.abs(w) + 4 * ulp32(scale)
     if dtype != "f32":
@@ -179,7 +188,7 @@ def check_log_softmax(got_bits, want64, xb, dtype):
         np.argwhere(bad)[:5].tolist(), g[bad][:5], w[bad][:5])
 
 
-def check_lse(got, want, xb, dtype):
+def check_lse(got, want, xb, dtype, m=None):
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     nan_w = np.isnan(want)
@@ -188,8 +197,11 @@ def check_lse(got, want, xb, dtype):
     np.testing.assert_array_equal(got[~nan_w & ~ok], want[~nan_w & ~ok])
     if not ok.any():
         return
-    with np.errstate(invalid="ignore"):
-        m = np.max(widen(np.asarray(xb)[ok], dtype), axis=1)
+    if m is None:
+        with np.errstate(invalid="ignore"):
+            m = np.max(widen(np.asarray(xb)[ok], dtype), axis=1)
+    else:
+        m = np.asarray(m, dtype=np.float64)[ok]
     bound = 1e-5 * np.abs(want[ok] - m) + 4 * ulp32(np.maximum(np.abs(m), np.abs(want[ok])))
     err = np.abs(got[ok] - want[ok])
     bad = err > bound

@@ -522,3 +522,63 @@ def test_grad_with_upstream_gradient_matches_autograd(reduction):
     # a block of rows further down takes the upstream gradients of those rows
     _, gb = oracle.grad_rows(x, t, c=c, d=dd, row0=3, nrows=4, want64=True)
     np.testing.assert_allclose(gb, w.grad.numpy()[3:7], rtol=1e-12, atol=1e-16)
+
+
+# ------------------------------------------- outputs at sampled elements
+
+def test_at_elements_match_autograd_and_torch_softmax():
+    # the gradient with upstream gradients, softmax and log-softmax at sampled
+    # elements, from the oracle's own lse, against torch CPU float64
+    M, V = 7, 301
+    x = f32(RNG.normal(size=(M, V)) * 4)
+    t = RNG.integers(0, V, size=M)
+    d = RNG.uniform(-2, 2, size=M)
+    _, lse = oracle.loss_rows(x, t, with_lse=True)
+    rows = RNG.integers(0, M, size=400)
+    cols = RNG.integers(0, V, size=400)
+    rows[:M], cols[:M] = np.arange(M), t          # every target element too
+    w = torch.from_numpy(x.astype(np.float64)).requires_grad_(True)
+    F.cross_entropy(w, torch.from_numpy(t), reduction="none").backward(torch.from_numpy(d))
+    _, g = oracle.at_elements(x, lse, rows, cols, "grad", targets=t, d=d, want64=True)
+    np.testing.assert_allclose(g, w.grad.numpy()[rows, cols], rtol=1e-12, atol=1e-16)
+    xt = torch.from_numpy(x.astype(np.float64))
+    _, p = oracle.at_elements(x, lse, rows, cols, "softmax", want64=True)
+    np.testing.assert_allclose(p, torch.softmax(xt, 1).numpy()[rows, cols], rtol=1e-13)
+    _, lp = oracle.at_elements(x, lse, rows, cols, "log_softmax", want64=True)
+    np.testing.assert_allclose(lp, torch.log_softmax(xt, 1).numpy()[rows, cols], rtol=1e-13,
+                               atol=1e-13)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_at_elements_uniform_rows_closed_form(dtype):
+    # all-equal rows of length V: softmax 1/V, log-softmax -ln V, gradient
+    # (1/V - [j == t]) c; rounded outputs as the oracle's rounding of those
+    V, c = 1000, 0.25
+    x = _to_bits(np.full((3, V), -1.5), dtype)
+    t = np.array([0, 999, 5000])                  # the last one out of range
+    _, lse = oracle.loss_rows(x, t, dtype=dtype, with_lse=True)
+    rows = np.repeat(np.arange(3), 4)
+    cols = np.tile([0, 5, 998, 999], 3)
+    _, g = oracle.at_elements(x, lse, rows, cols, "grad", dtype=dtype, targets=t, c=c,
+                              want64=True)
+    want = (1.0 / V - (cols == t[rows])) * c
+    np.testing.assert_allclose(g, want, rtol=1e-14)
+    gb = oracle.at_elements(x, lse, rows, cols, "grad", dtype=dtype, targets=t, c=c)
+    np.testing.assert_array_equal(gb, oracle.round_to(want, dtype))
+    _, p = oracle.at_elements(x, lse, rows, cols, "softmax", dtype=dtype, want64=True)
+    np.testing.assert_allclose(p, 1.0 / V, rtol=1e-14)
+    _, lp = oracle.at_elements(x, lse, rows, cols, "log_softmax", dtype=dtype, want64=True)
+    np.testing.assert_allclose(lp, -math.log(V), rtol=1e-14)
+
+
+def test_at_elements_arguments():
+    x = f32(RNG.normal(size=(2, 5)))
+    lse = np.zeros(2)
+    with pytest.raises(ValueError):
+        oracle.at_elements(x, lse, [0], [5], "softmax")          # column out of range
+    with pytest.raises(ValueError):
+        oracle.at_elements(x, lse, [2], [0], "softmax")          # row out of range
+    with pytest.raises(ValueError):
+        oracle.at_elements(x, lse, [0], [0], "grad")             # no targets
+    with pytest.raises(ValueError):
+        oracle.at_elements(x, np.zeros(3), [0], [0], "softmax")  # lse not [M]
