@@ -263,6 +263,12 @@ def time_workload(ce, workload, op, reduction, steps, warmup, log, M=None, V=Non
         "rows_per_s": M / (avg_ms * 1e-3),
         "loss": float(out.float().mean().item()) if has_loss else None,
     }
+    if (M, V) == (c["M"], c["V"]):
+        # HBM bytes per launch from the committed counter summary (null once
+        # the kernels have changed since), and the rate they imply
+        res["traffic"] = load_traffic(workload, op, reduction)
+        res["counter_GBps"] = (None if res["traffic"] is None
+                               else res["traffic"] / (avg_ms * 1e-3) / 1e9)
     if cpu_sample:
         res["cpu_oracle"] = oracle_sample(workload, op, reduction, M, V)
     res["frac_of_peak"] = res["alg_GBps"] / PEAK_GBS
@@ -464,6 +470,28 @@ def oracle_sample(workload, op, reduction, M=None, V=None, budget_s=1.0):
             "sample": "%d rows of the line's workload, %.2f s" % (rows, el)}
 
 
+def host_env():
+    """Versions and the host the run used (the oracle timings depend on it)."""
+    import platform
+    import torch
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"device": torch.cuda.get_device_name(0), "torch": torch.__version__,
+            "hip": torch.version.hip, "python": platform.python_version(),
+            "cpu_model": model, "cpu_count": os.cpu_count(), "cpus_usable": usable,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
 def cpu_baseline(workload, op, reduction, log, budget_s=20.0):
     """The fp64 oracle over the whole workload, repeated until ~10 s have passed
     (each pass is bounded by the budget), on every host core OpenMP gives it."""
@@ -553,7 +581,9 @@ def linear_main(ce, args, log):
         "roofline": {"bound": "mfma", "achieved": round(r["alg_TFLOPs"], 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(r["frac_of_peak"], 4), "traffic": None},
+        "counter_GBps": head.get("counter_GBps"),
         "cpu_baseline": cpu,
+        "env": host_env(),
         "also": [{k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()}],
     }
     print(json.dumps(line), flush=True)
@@ -684,7 +714,9 @@ def main():
         "ms_per_step_min": round(head["kernel_ms_min"], 5),
         "measured_ceiling": None if ceilings is None else dict(
             ceilings, frac_of_read=round(head["alg_GBps"] / ceilings["read_GBps"], 4)),
+        "counter_GBps": head.get("counter_GBps"),
         "cpu_baseline": cpu,
+        "env": host_env(),
         "also": [{k: (round(v, 5) if isinstance(v, float) else v) for k, v in a.items()}
                  for a in also],
     }
