@@ -24,9 +24,10 @@ GB/s = bytes the method must move / kernel time.  The same line carries:
                 forward; each timed the same way; and linear + cross-entropy
                 (logits = hidden @ weight.T, bf16 [4096, 4096] x [131072, 4096],
                 taken in vocabulary chunks) forward and forward + backward in
-                TFLOP/s against the bf16 MFMA peak; with --extra-shapes, one
-                GPU's share of a row- and a vocabulary-sharded LM head and the
-                tiny workload's microseconds per call.
+                TFLOP/s against the bf16 MFMA peak; the tiny workload's
+                microseconds per call (eager and from a HIP graph); with
+                --extra-shapes, one GPU's share of a row- and a
+                vocabulary-sharded LM head.
 
 Inputs rotate over enough buffers (>= 1 GiB in total) that no launch finds its
 rows in the 256 MB last-level cache; the in-place backward restores its logits
@@ -601,8 +602,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the extra lines")
     ap.add_argument("--extra-shapes", action="store_true",
                     help="also time one GPU's share of a row- and a vocabulary-sharded LM head "
-                         "and the tiny workload's per-call time (these share kernels with the "
-                         "other lines, so they are off in profiled runs)")
+                         "(these share kernels with the other lines, so they are off in "
+                         "profiled runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -672,13 +673,14 @@ def main():
                         ("stress", "fwd"), ("stress", "fwd_bwd"), ("skinny", "fwd")):
             also.append(time_workload(ce, wl, eop, "mean", max(20, args.steps // 5),
                                       max(3, args.warmup // 5), log, cpu_sample=not args.no_cpu))
+        # the tiny workload: launch-bound, microseconds per call
+        also.append(time_tiny(ce, log, cpu_sample=not args.no_cpu))
         if args.extra_shapes:
             # one GPU's share of a sharded LM head: rows (M / 8) and vocabulary
-            # (V / 8); the tiny workload's per-call time
+            # (V / 8)
             also.append(time_workload(ce, "lmhead", "fwd", "mean", 50, 5, log, M=2048))
             also.append(time_workload(ce, "lmhead", "fwd_bwd", "mean", 50, 5, log, M=2048))
             also.append(time_workload(ce, "lmhead", "fwd_lse", "none", 50, 5, log, V=16384))
-            also.append(time_tiny(ce, log, cpu_sample=not args.no_cpu))
         lin_cpu = None if args.no_cpu else linear_cpu_baseline(log, rows=1)
         for lop in ("fwd", "fwd_bwd"):
             also.append(time_linear(ce, lop, max(5, args.steps // 20), 2, log))
