@@ -83,11 +83,21 @@ int pow2ceil(int64_t n)
 //  - rows up to 16 KB sit in the registers of 1..64 lanes (rows kernel);
 //  - longer rows are streamed for the forward: by one wavefront per row just
 //    past 16 KB, then by 4-, 8- or 16-wave workgroups as the rows grow;
-//  - the fused backward keeps rows up to 256 KB in the registers of a
-//    16-wave workgroup (one HBM read per element), longer ones re-read.
-void choose_shape(int64_t nvec, bool bwd, int *kind, int *a, int *b, int *nbuf)
+//  - the epilogues (fused backward, softmax, ...) past 16 KB: rows whose
+//    re-read stays in L2 while the CU's other rows stream are streamed
+//    twice (up to 48 KB by 8-wave workgroups, 32 waves per CU; up to 128 KB
+//    by one 16-wave workgroup per CU), unless they fill a 16-wave register
+//    tile exactly; rows of 128-256 KB sit in the registers of a 16-wave
+//    workgroup (one HBM read per element), longer ones are streamed again.
+//    A register tile that the row leaves partly empty costs nearly as much
+//    as a full one: the workgroup waits out each row's loads, so the tile,
+//    not the data, sets the time.
+// *waves: waves per CU the grid is sized for (0: the mapping's default).
+void choose_shape(int64_t nvec, bool bwd, bool aligned, int *kind, int *a, int *b, int *nbuf,
+                  int *waves)
 {
     *nbuf = 1;
+    *waves = 0;
     *kind = cek::KIND_ROWS;
     if (nvec <= 4) {
         *a = 1;
@@ -117,10 +127,30 @@ void choose_shape(int64_t nvec, bool bwd, int *kind, int *a, int *b, int *nbuf)
     } else if (nvec <= 1024) {
         *a = 64;
         *b = 16;
+    } else if (bwd && nvec <= 8192 && aligned && nvec % 1024 == 0 && nvec > 3072) {
+        // an exact 16-wave register tile
+        *kind = cek::KIND_WG;
+        *a = 16;
+        *b = (int)(nvec / 1024);
+    } else if (bwd && nvec <= 3072) {
+        // measured (fused fwd+bwd, 1 GiB of logits): 1500 vectors 464 us
+        // against 1036 with a 4096-vector register tile; 3072: 452 against 490
+        // in an exact 3072 tile
+        *kind = cek::KIND_STREAM;
+        *a = 8;
+        *b = 4;
+        *waves = 32;
+    } else if (bwd && nvec <= 8192) {
+        // measured: the stress rows (6283 vectors, fp16) 358 us against 394
+        // in an 8192 tile and 371 in a 7168 one; fp32 6000 vectors 484
+        // against 662 (8192) and 643 (6144)
+        *kind = cek::KIND_STREAM;
+        *a = 16;
+        *b = 4;
     } else if (bwd && nvec <= 16384) {
         *kind = cek::KIND_WG;
         *a = 16;
-        *b = nvec <= 4096 ? 4 : nvec <= 8192 ? 8 : nvec <= 12288 ? 12 : 16;
+        *b = nvec <= 12288 ? 12 : 16;
     } else if (!bwd && nvec <= 1536) {
         // just past the register rows: one row per wavefront wastes least
         *kind = cek::KIND_WSTREAM;
@@ -256,8 +286,8 @@ int make_plan(int64_t M, int64_t V, int dtype, int op, bool aligned, Plan *plan)
 {
     const int E = 16 / (int)elem_size(dtype);
     const int64_t nvec = window_vectors(V, E, aligned);
-    int kind = 0, a = 0, b = 0, nbuf = 1;
-    choose_shape(nvec, op != cek::EPI_NONE, &kind, &a, &b, &nbuf);
+    int kind = 0, a = 0, b = 0, nbuf = 1, waves = 0;
+    choose_shape(nvec, op != cek::EPI_NONE, aligned, &kind, &a, &b, &nbuf, &waves);
     // The backward from a given lse needs no row in registers: for long
     // 16-bit rows, 8-wave streaming workgroups, as many as fit, beat the
     // register-resident workgroup (measured: LM head 5.24 against 4.98 TB/s,
@@ -268,6 +298,7 @@ int make_plan(int64_t M, int64_t V, int dtype, int op, bool aligned, Plan *plan)
         a = 8;
         b = 4;
         nbuf = 1;
+        waves = 32;
     }
     int fk, fa, fb;
     if (forced_shape(&fk, &fa, &fb)) {
@@ -278,6 +309,7 @@ int make_plan(int64_t M, int64_t V, int dtype, int op, bool aligned, Plan *plan)
             a = fa;
             b = fb;
             nbuf = 1;
+            waves = 0;
         }
     }
     plan->kind = kind;
@@ -315,9 +347,9 @@ int make_plan(int64_t M, int64_t V, int dtype, int op, bool aligned, Plan *plan)
     const int waves_per_wg = plan->k.block / 64;
     const char *tw = std::getenv("CE_WAVES_PER_CU");
     const int target_waves = (tw && std::atoi(tw) > 0) ? std::atoi(tw)
-                             : kind == cek::KIND_ROWS  ? 4
-                             : lse_stream && kind == cek::KIND_STREAM ? 32
-                                                       : 16;
+                             : kind == cek::KIND_ROWS ? 4
+                             : waves > 0              ? waves
+                                                      : 16;
     int wg_per_cu = target_waves / waves_per_wg;
     if (wg_per_cu < 1)
         wg_per_cu = 1;

@@ -37,7 +37,7 @@ KernelRef pick_all(int kind, int a, int b, int nbuf)
         CE_ROWS(32, 32) CE_ROWS(2, 16)
     } else if (kind == KIND_WG) {
         CE_WG(4, 8) CE_WG(8, 8) CE_WG(8, 12) CE_WG(8, 16) CE_WG(16, 8) CE_WG(16, 12) CE_WG(16, 16)
-        CE_WG(4, 16) CE_WG(16, 4)
+        CE_WG(4, 16) CE_WG(16, 4) CE_WG(16, 2) CE_WG(16, 3) CE_WG(16, 5) CE_WG(16, 6) CE_WG(16, 7)
     } else if (kind == KIND_WSTREAM && !EXACT && OP == EPI_NONE) {
         if (a == 1 && b == 4) return KernelRef{(const void *)&wstream_kernel<DT, 4>, 256};
         if (a == 1 && b == 2) return KernelRef{(const void *)&wstream_kernel<DT, 2>, 256};
@@ -62,7 +62,8 @@ KernelRef pick_table(int kind, int a, int b, int nbuf)
         CE_ROWS1(1, 1) CE_ROWS1(1, 2) CE_ROWS1(1, 4) CE_ROWS1(2, 4) CE_ROWS1(4, 4)
         CE_ROWS1(16, 4) CE_ROWS1(32, 4) CE_ROWS1(64, 4) CE_ROWS1(64, 8) CE_ROWS1(64, 16)
     } else if (kind == KIND_WG) {
-        CE_WG(16, 4) CE_WG(16, 8) CE_WG(16, 12) CE_WG(16, 16)
+        CE_WG(16, 2) CE_WG(16, 3) CE_WG(16, 4) CE_WG(16, 5) CE_WG(16, 6) CE_WG(16, 7)
+        CE_WG(16, 8) CE_WG(16, 12) CE_WG(16, 16)
     } else if (kind == KIND_STREAM && !EXACT) {
         CE_STREAM(4, 4) CE_STREAM(8, 4) CE_STREAM(16, 4)
     }

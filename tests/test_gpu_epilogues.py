@@ -282,7 +282,9 @@ def test_every_softmax_and_grad_shape(ce, monkeypatch):
     for shape, cap in (("rows:1:1", 1), ("rows:1:2", 2), ("rows:1:4", 4), ("rows:2:4", 8),
                        ("rows:4:4", 16), ("rows:4:8", 32), ("rows:16:4", 64),
                        ("rows:32:4", 128), ("rows:64:4", 256), ("rows:64:8", 512),
-                       ("rows:64:16", 1024), ("wg:16:4", 4096), ("wg:16:8", 8192),
+                       ("rows:64:16", 1024), ("wg:16:2", 2048), ("wg:16:3", 3072),
+                       ("wg:16:4", 4096), ("wg:16:5", 5120), ("wg:16:6", 6144),
+                       ("wg:16:7", 7168), ("wg:16:8", 8192),
                        ("wg:16:12", 12288), ("wg:16:16", 16384), ("stream:8:4", 1 << 30),
                        ("stream:16:4", 1 << 30)):
         monkeypatch.setenv("CE_FORCE_PLAN", shape)

@@ -138,7 +138,8 @@ SHAPES = ["rows:1:1", "rows:1:2", "rows:1:4", "rows:2:4", "rows:4:4", "rows:8:4"
           "rows:32:4", "rows:64:4", "rows:64:8", "rows:64:16", "rows:4:8", "rows:8:2",
           "rows:16:2", "rows:32:1", "rows:32:8", "rows:32:16", "rows:32:32", "rows:2:16",
           "wg:4:8", "wg:8:8", "wg:8:12", "wg:8:16", "wg:16:8", "wg:16:12", "wg:16:16",
-          "wg:4:16", "wg:16:4", "stream:4:8", "stream:8:4", "stream:8:8", "stream:16:4",
+          "wg:4:16", "wg:16:4", "wg:16:2", "wg:16:3", "wg:16:5", "wg:16:6", "wg:16:7",
+          "stream:4:8", "stream:8:4", "stream:8:8", "stream:16:4",
           "stream:4:16", "stream:1:4", "stream:2:4", "stream:4:4", "stream:1:8", "stream:2:8",
           "stream:1:16", "stream:16:2", "stream:16:1", "stream:8:2",
           "wstream:1:2", "wstream:1:4", "wstream:1:8"]
@@ -172,6 +173,31 @@ def _check_shape(ce, shape, kind, cap):
             run_and_check(ce, dtype, M, V, 4.0, seed=V + 5, reduction="mean", op="fwd_bwd",
                           offset=(V // 2) % 2)
             run_and_check(ce, dtype, M, V, 4.0, seed=V + 9, reduction="sum", offset=0)
+
+
+# The fused backward's mapping for rows past 16 KB, one case per branch of the
+# plan table (window vectors: 16 bytes each): streamed twice by 8-wave
+# workgroups up to 3072 vectors, by 16-wave ones up to 8192 unless the row
+# fills a register tile exactly, register tiles of 12 or 16 x 1024 vectors up
+# to 16384.
+EPI_TABLE = [(1500, 0, "stream:8:4"), (3072, 0, "stream:8:4"), (4096, 0, "wg:16:4"),
+             (5120, 0, "wg:16:5"), (6283, 1, "stream:16:4"), (7168, 0, "wg:16:7"),
+             (8192, 0, "wg:16:8"), (8000, 0, "stream:16:4"), (10240, 0, "wg:16:12"),
+             (14336, 0, "wg:16:16")]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_epilogue_plan_table(ce, dtype):
+    E = 4 if dtype == "f32" else 8
+    code = {"f32": 0, "f16": 1, "bf16": 2}[dtype]
+    for nvec, ragged, shape in EPI_TABLE:
+        V = nvec * E - (E - 1 if ragged else 0)
+        M = 300 if nvec <= 3072 else 150
+        plan = ce.ce_plan_describe(M, V, code, "mean", op=ce.CE_OP_FWD_BWD)
+        assert plan.startswith(shape), (dtype, V, plan, shape)
+        run_and_check(ce, dtype, M, V, 4.0, seed=nvec, reduction="mean", op="fwd_bwd")
+        run_and_check(ce, dtype, M, V, 4.0, seed=nvec + 1, reduction="none", op="fwd_bwd",
+                      offset=1)
 
 
 # ------------------------------------------------------------------ edge cases
