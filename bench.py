@@ -352,7 +352,8 @@ def measure_ceilings(log):
     st = torch.cuda.current_stream()
 
     def best(fn, n=5):
-        fn()
+        rc = fn()
+        assert not isinstance(rc, int) or rc == 0, "probe launch failed: %d" % rc
         torch.cuda.synchronize()
         t = []
         for _ in range(n):
@@ -371,11 +372,25 @@ def measure_ceilings(log):
     copy = max(2 * half / best(lambda: lib.probe_copy(buf.data_ptr() + half, buf.data_ptr(), half,
                                                        g, u, st.cuda_stream)) / 1e6
                for g, u in ((4096, 104), (2048, 8), (4096, 4)))
-    del buf, out
+    # in place: rows of 256 and 128 KB held in registers between read and
+    # write (the fused backward's pattern without its arithmetic), and
+    # torch's own in-place elementwise kernel for comparison
+    lib.probe_inplace_rows.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    inplace = max(2 * nb / best(lambda: lib.probe_inplace_rows(buf.data_ptr(), nb, 16, k, g,
+                                                                st.cuda_stream)) / 1e6
+                  for k, g in ((16, 256), (16, 512), (8, 512)))
+    xb = buf.view(torch.bfloat16)
+    inplace_torch = 2 * nb / best(lambda: xb.mul_(1.0)) / 1e6
+    del buf, out, xb
     torch.cuda.empty_cache()
-    log("measured ceilings: read %.0f GB/s, copy %.0f GB/s (read + write)" % (read, copy))
+    log("measured ceilings: read %.0f GB/s, copy %.0f GB/s (read + write), in place %.0f GB/s "
+        "(rows in registers; torch's in-place multiply %.0f GB/s)"
+        % (read, copy, inplace, inplace_torch))
     return {"read_GBps": round(read, 1), "copy_GBps": round(copy, 1),
-            "how": "probe/bw_probe.hip over 4 GiB (copy: 2 GiB each way), best launch shape"}
+            "inplace_rows_GBps": round(inplace, 1), "inplace_torch_GBps": round(inplace_torch, 1),
+            "how": "probe/bw_probe.hip over 4 GiB (copy: 2 GiB each way; in place: 4 GiB "
+                   "rewritten), best launch shape; torch: bf16 mul_(1.0) over the same 4 GiB"}
 
 
 def time_tiny(ce, log, calls=1000, cpu_sample=False):

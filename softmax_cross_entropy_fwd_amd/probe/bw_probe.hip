@@ -94,6 +94,30 @@ __global__ void __launch_bounds__(256) copy_nt_kernel(V4 *__restrict__ dst,
     }
 }
 
+// In place, with the access pattern of the fused backward over rows held in
+// registers: a W-wavefront workgroup reads a row of W*64*K vectors, waits at
+// a barrier, and writes the same vectors back (non-temporal); rows are
+// grid-strided.  No arithmetic: the rate is what this pattern alone allows.
+template <int W, int K>
+__global__ void __launch_bounds__(W * 64) inplace_rows_kernel(V4 *__restrict__ p, int64_t nrows)
+{
+    constexpr int64_t RV = (int64_t)W * 64 * K;
+    for (int64_t row = blockIdx.x; row < nrows; row += gridDim.x) {
+        V4 *q = p + row * RV;
+        V4 r[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            r[k] = q[threadIdx.x + k * W * 64];
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                __builtin_nontemporal_store(r[k].w[j], &q[threadIdx.x + k * W * 64].w[j]);
+        }
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -134,6 +158,25 @@ int probe_copy(void *dst, const void *src, int64_t bytes, int grid, int unroll, 
     case 101: hipLaunchKernelGGL(copy_nt_kernel<1>, dim3(grid), dim3(256), 0, s, (V4 *)dst, (const V4 *)src, nvec); break;
     default: return -1;
     }
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Rewrite `bytes` in place, rows of W*64*K vectors (W = 16, K = 16 or 8) held
+// in registers between the read and the write; bytes must be a multiple of
+// the row size.
+int probe_inplace_rows(void *p, int64_t bytes, int W, int K, int grid, void *stream)
+{
+    const int64_t rv = (int64_t)W * 64 * K;
+    if (!p || grid < 1 || bytes < 16 * rv || (bytes / 16) % rv || bytes % 16)
+        return -1;
+    const int64_t nrows = bytes / 16 / rv;
+    hipStream_t s = (hipStream_t)stream;
+    if (W == 16 && K == 16)
+        hipLaunchKernelGGL((inplace_rows_kernel<16, 16>), dim3(grid), dim3(1024), 0, s, (V4 *)p, nrows);
+    else if (W == 16 && K == 8)
+        hipLaunchKernelGGL((inplace_rows_kernel<16, 8>), dim3(grid), dim3(1024), 0, s, (V4 *)p, nrows);
+    else
+        return -1;
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
