@@ -335,9 +335,11 @@ def time_linear(ce, op, steps, warmup, log, chunk=0):
     return res
 
 
-def measure_ceilings(log):
+def measure_ceilings(log, size_bytes=None):
     """What plain kernels reach on this machine (the probe library): a read-only
-    stream and a copy over 4 GiB, best of a few launch shapes, in GB/s."""
+    stream and a copy over 4 GiB, best of a few launch shapes, in GB/s; and,
+    given the headline workload's logits size, the read over that many bytes
+    (alternating between two buffers, so that each pass misses the caches)."""
     import ctypes
     import torch
     lib = ctypes.CDLL(os.path.join(ROOT, "softmax_cross_entropy_fwd_amd", "libce_probe.so"))
@@ -368,6 +370,17 @@ def measure_ceilings(log):
     read = max(nb / best(lambda: lib.probe_read(buf.data_ptr(), nb, g, u, blk, out.data_ptr(),
                                                 st.cuda_stream)) / 1e6
                for g, u, blk in ((1024, 8, 256), (512, 4, 1024), (2048, 8, 256)))
+    read_at_size = None
+    if size_bytes and size_bytes % 16 == 0 and size_bytes <= nb // 2:
+        flip = [0]
+
+        def read_rotating(g, u, blk):
+            flip[0] ^= 1
+            return lib.probe_read(buf.data_ptr() + flip[0] * (nb // 2), size_bytes, g, u, blk,
+                                  out.data_ptr(), st.cuda_stream)
+        read_at_size = max(size_bytes / best(lambda: read_rotating(g, u, blk), n=10) / 1e6
+                           for g, u, blk in ((1024, 8, 256), (512, 4, 1024), (2048, 8, 256),
+                                             (256, 16, 256)))
     half = nb // 2
     copy = max(2 * half / best(lambda: lib.probe_copy(buf.data_ptr() + half, buf.data_ptr(), half,
                                                        g, u, st.cuda_stream)) / 1e6
@@ -387,7 +400,10 @@ def measure_ceilings(log):
     log("measured ceilings: read %.0f GB/s, copy %.0f GB/s (read + write), in place %.0f GB/s "
         "(rows in registers; torch's in-place multiply %.0f GB/s)"
         % (read, copy, inplace, inplace_torch))
+    if read_at_size is not None:
+        log("read over the headline workload's %d bytes: %.0f GB/s" % (size_bytes, read_at_size))
     return {"read_GBps": round(read, 1), "copy_GBps": round(copy, 1),
+            "read_at_size_GBps": None if read_at_size is None else round(read_at_size, 1),
             "inplace_rows_GBps": round(inplace, 1), "inplace_torch_GBps": round(inplace_torch, 1),
             "how": "probe/bw_probe.hip over 4 GiB (copy: 2 GiB each way; in place: 4 GiB "
                    "rewritten), best launch shape; torch: bf16 mul_(1.0) over the same 4 GiB"}
@@ -701,7 +717,8 @@ def main():
             also.append(time_linear(ce, lop, max(5, args.steps // 20), 2, log))
             also[-1]["cpu_oracle"] = lin_cpu
     # after the timed lines, so the 4 GiB probe buffers do not precede them
-    ceilings = None if args.no_extra else measure_ceilings(log)
+    ceilings = None if args.no_extra else measure_ceilings(
+        log, c["M"] * c["V"] * inputs.ELEM_BYTES[c["dtype"]])
     traffic = load_traffic(args.workload, op, red)
     cpu = None if args.no_cpu else cpu_baseline(args.workload, op, red, log)
 
@@ -730,7 +747,9 @@ def main():
         "ms_per_step_median": round(head["kernel_ms_median"], 5),
         "ms_per_step_min": round(head["kernel_ms_min"], 5),
         "measured_ceiling": None if ceilings is None else dict(
-            ceilings, frac_of_read=round(head["alg_GBps"] / ceilings["read_GBps"], 4)),
+            ceilings, frac_of_read=round(head["alg_GBps"] / ceilings["read_GBps"], 4),
+            frac_of_read_at_size=(None if not ceilings.get("read_at_size_GBps") else
+                                  round(head["alg_GBps"] / ceilings["read_at_size_GBps"], 4))),
         "counter_GBps": head.get("counter_GBps"),
         "cpu_baseline": cpu,
         "env": host_env(),
