@@ -1152,13 +1152,18 @@ __global__ void __launch_bounds__(W * 64) stream_kernel(Params p)
         const TargetPos tp = target_pos<DT>(t, p.V, w.head);
 
         float m, s, xt;
+        // the sum of the terms other than the target's, when pass 1 gives it
+        // (p_t > 1/2 then needs no second read of the row)
+        bool have_excl = false;
+        float s_other = 0.0f;
         if constexpr (OP == EPI_LSE_GRAD) {
             // statistics given: m = lse, s = 1
             m = p.lse_in[row];
             s = 1.0f;
             xt = tp.valid ? load_logit<DT>(p, row, t) : __builtin_nanf("");
         } else {
-            // pass 1: online (max, sum) per lane, rescaled once per chunk
+            // pass 1: online (max, sum) per lane, rescaled once per chunk; the
+            // max takes every element, the sum every element but the target
             float m_run = -__builtin_inff();
             float s_run = 0.0f;
             for (int cb = 0; cb < w.nvec; cb += CH) {
@@ -1170,14 +1175,20 @@ __global__ void __launch_bounds__(W * 64) stream_kernel(Params p)
                                        cb == 0 ? w.head : 0,
                                        cb == 0 ? p.V : p.V + w.head - (int64_t)cb * E,
                                        p.aligned != 0);
+                // the lane holding the target keeps its logit aside and drops it
+                // from the vector: it enters the max below, not the sum
+                float tval = -__builtin_inff();
                 if (tp.valid && tp.vt >= cb && tp.vt < cb + CH) {
                     const int off = tp.vt - cb;
 #pragma unroll
                     for (int k = 0; k < K; ++k)
-                        if (off == tid + NT * k)
-                            s_xt = vec_elem_dyn<DT>(raw[k], tp.jt);
+                        if (off == tid + NT * k) {
+                            tval = vec_elem_dyn<DT>(raw[k], tp.jt);
+                            s_xt = tval;
+                            set_elem<DT>(raw[k], tp.jt, -__builtin_inff());
+                        }
                 }
-                float cm = m_run;
+                float cm = fmaxf(m_run, tval);
 #pragma unroll
                 for (int k = 0; k < K; ++k)
                     cm = vec_max<DT>(raw[k], cm);
@@ -1210,17 +1221,21 @@ __global__ void __launch_bounds__(W * 64) stream_kernel(Params p)
             if (lane == 0)
                 s_sum[wave] = ls;
             __syncthreads();
-            s = s_sum[0];
+            s_other = s_sum[0];
 #pragma unroll
             for (int i = 1; i < W; ++i)
-                s += s_sum[i];
+                s_other += s_sum[i];
+            have_excl = true;
+            s = s_other;
         }
         const float mL = m * kLog2e;
 
         const float et = fast_exp2(__builtin_fmaf(xt, kLog2e, -mL));
+        if (have_excl && tp.valid)
+            s = s_other + et;
         const bool accurate = tp.valid && et > 0.5f * s;
-        float s_excl = s - et;
-        if (accurate) {
+        float s_excl = have_excl ? s_other : s - et;
+        if (accurate && !have_excl) {
             // re-read the row and sum every term but the target's
             float lx = 0.0f;
             for (int cb = 0; cb < w.nvec; cb += CH) {

@@ -256,6 +256,40 @@ def test_dominant_target_loss_and_grad_accuracy(ce):
                 check_grads(host_grad_bits(xg), want, dtype, 1.0, want64)
 
 
+@pytest.mark.parametrize("shape", [None, "stream:4:4", "stream:8:4", "stream:16:4"])
+def test_dominant_target_small_loss_relative(ce, shape, monkeypatch):
+    import torch
+    # p_t > 1/2: the loss log1p(sum of the other terms / e_t) keeps its
+    # relative accuracy however small it is (no absolute floor here), in the
+    # streamed kernels (which leave the target out of their first pass) and
+    # in the default mappings (which sum the other terms on a second read)
+    if shape:
+        monkeypatch.setenv("CE_FORCE_PLAN", shape)
+    for dtype in DTYPES:
+        for V in (3000, 20000, 50257):
+            for gap in (12.0, 30.0):
+                M = 6
+                x, t = inputs.make(dtype, M, V, 1.0, seed=int(gap) + V)
+                xf = x.float()
+                xf[torch.arange(M), t] = xf.max(dim=1).values + gap
+                xd = xf.to(x.dtype)
+                xb, tn = inputs.host_bits(xd), t.numpy()
+                want = oracle.loss_rows(xb, tn, dtype=dtype)
+                for op in ("fwd", "fwd_bwd"):
+                    xg, buf = place(xd, V % 3)
+                    tg = t.to("cuda:0")
+                    got = (ce.ce_fwd(xg, tg, "none") if op == "fwd"
+                           else ce.ce_fwd_bwd_inplace(xg, tg, "none"))
+                    got = got.cpu().numpy().astype(np.float64)
+                    assert np.all(want > 0) and np.all(want < math.log(2)), want
+                    err = np.abs(got - want) / want
+                    assert err.max() <= 1e-4, (dtype, V, gap, op, got, want)
+                    if op == "fwd_bwd":
+                        w, w64 = oracle.grad_rows(xb, tn, dtype=dtype, c=1.0, want64=True)
+                        check_grads(host_grad_bits(xg), w, dtype, 1.0, w64)
+                    assert canaries_intact(buf, V % 3, M * V, dtype)
+
+
 def test_uniform_rows_closed_form(ce):
     import torch
     for dtype in DTYPES:
