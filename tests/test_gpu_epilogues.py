@@ -329,3 +329,28 @@ def test_fused_and_split_backward_agree(ce):
             torch.cuda.synchronize()
             check_grads(host_grad_bits(g), host_grad_bits(y), dtype, 1.0 / 16,
                         inputs.host_bits(y).astype(np.float64) if dtype == "f32" else None)
+
+
+# The default mapping of the epilogues for rows past 16 KB (window vectors of
+# 16 bytes): streamed twice by 8-wave workgroups up to 3072 vectors, by
+# 16-wave ones up to 8192 unless the row fills a register tile exactly,
+# register tiles beyond; the backward from a given lse streams 16-bit rows
+# of 4096 vectors or more.
+EPI_DEFAULTS = [(1500, "stream:8:4"), (4096, "wg:16:4"), (6000, "stream:16:4"),
+                (7168, "wg:16:7"), (10240, "wg:16:12")]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_epilogue_default_mappings(ce, dtype):
+    E = 4 if dtype == "f32" else 8
+    for nvec, shape in EPI_DEFAULTS:
+        V = nvec * E
+        M = 40
+        for op in (ce.CE_OP_SOFTMAX, ce.CE_OP_LOG_SOFTMAX):
+            plan = ce.ce_plan_describe(M, V, DCODE[dtype], "none", op=op)
+            assert plan.startswith(shape), (dtype, V, plan, shape)
+        softmax_case(ce, dtype, M, V, 4.0, seed=nvec + 61, log=False)
+        softmax_case(ce, dtype, M, V, 4.0, seed=nvec + 62, log=True, inplace=True)
+        bwd_case(ce, dtype, M, V, 4.0, seed=nvec + 63, reduction="mean")
+        bwd_case(ce, dtype, M, V, 4.0, seed=nvec + 64, reduction="none", inplace=True,
+                 offset=1, lse_from="library")
