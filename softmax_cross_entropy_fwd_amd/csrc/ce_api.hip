@@ -65,7 +65,7 @@ int64_t tile_vectors(int kind, int a, int b)
 {
     if (kind == cek::KIND_ROWS)
         return (int64_t)a * b;
-    if (kind == cek::KIND_WG)
+    if (kind == cek::KIND_WG || kind == cek::KIND_WG2)
         return (int64_t)a * 64 * b;
     return 0;
 }
@@ -92,9 +92,12 @@ int pow2ceil(int64_t n)
 //    A register tile that the row leaves partly empty costs nearly as much
 //    as a full one: the workgroup waits out each row's loads, so the tile,
 //    not the data, sets the time.
+// 16-bit rows of 4097-6656 vectors that do not fill a 16-wave tile exactly
+// sit in 8-wave register tiles, two workgroups per CU, so that one row's
+// reduction overlaps the other's memory traffic.
 // *waves: waves per CU the grid is sized for (0: the mapping's default).
-void choose_shape(int64_t nvec, bool bwd, bool aligned, int *kind, int *a, int *b, int *nbuf,
-                  int *waves)
+void choose_shape(int64_t nvec, bool bwd, bool aligned, bool wide, int *kind, int *a, int *b,
+                  int *nbuf, int *waves)
 {
     *nbuf = 1;
     *waves = 0;
@@ -140,6 +143,14 @@ void choose_shape(int64_t nvec, bool bwd, bool aligned, int *kind, int *a, int *
         *a = 8;
         *b = 4;
         *waves = 32;
+    } else if (bwd && wide && nvec > 4096 && nvec <= 6656) {
+        // measured (fused fwd+bwd, 1 GiB of bf16 logits, us): 4500 vectors
+        // 445 against 488 streamed; 5000: 418 / 494; 6000: 424 / 457; the
+        // stress rows 354 / 360; at 7000 the two tie, at 7500 streaming wins
+        *kind = cek::KIND_WG2;
+        *a = 8;
+        *b = (int)((nvec + 511) / 512);
+        *waves = 16;
     } else if (bwd && nvec <= 8192) {
         // measured: the stress rows (6283 vectors, fp16) 358 us against 394
         // in an 8192 tile and 371 in a 7168 one; fp32 6000 vectors 484
@@ -167,7 +178,8 @@ void choose_shape(int64_t nvec, bool bwd, bool aligned, int *kind, int *a, int *
     }
 }
 
-// CE_FORCE_PLAN=rows:G:K | wg:W:K | stream:W:K overrides the mapping (tuning).
+// CE_FORCE_PLAN=rows:G:K | wg:W:K | wg2:W:K | stream:W:K | wstream:1:K overrides the
+// mapping (tuning).
 bool forced_shape(int *kind, int *a, int *b)
 {
     const char *s = std::getenv("CE_FORCE_PLAN");
@@ -175,7 +187,7 @@ bool forced_shape(int *kind, int *a, int *b)
         return false;
     char name[16] = {0};
     int x = 0, y = 0;
-    if (std::sscanf(s, "%15[a-z]:%d:%d", name, &x, &y) != 3)
+    if (std::sscanf(s, "%15[a-z0-9]:%d:%d", name, &x, &y) != 3)
         return false;
     if (!std::strcmp(name, "rows"))
         *kind = cek::KIND_ROWS;
@@ -185,6 +197,8 @@ bool forced_shape(int *kind, int *a, int *b)
         *kind = cek::KIND_STREAM;
     else if (!std::strcmp(name, "wstream"))
         *kind = cek::KIND_WSTREAM;
+    else if (!std::strcmp(name, "wg2"))
+        *kind = cek::KIND_WG2;
     else
         return false;
     *a = x;
@@ -287,7 +301,7 @@ int make_plan(int64_t M, int64_t V, int dtype, int op, bool aligned, Plan *plan)
     const int E = 16 / (int)elem_size(dtype);
     const int64_t nvec = window_vectors(V, E, aligned);
     int kind = 0, a = 0, b = 0, nbuf = 1, waves = 0;
-    choose_shape(nvec, op != cek::EPI_NONE, aligned, &kind, &a, &b, &nbuf, &waves);
+    choose_shape(nvec, op != cek::EPI_NONE, aligned, E == 8, &kind, &a, &b, &nbuf, &waves);
     // The backward from a given lse needs no row in registers: for long
     // 16-bit rows, 8-wave streaming workgroups, as many as fit, beat the
     // register-resident workgroup (measured: LM head 5.24 against 4.98 TB/s,
@@ -742,7 +756,7 @@ int ce_plan_describe(int64_t M, int64_t V, ce_dtype_t dtype, ce_reduction_t redu
     int rc = make_plan(M, V, (int)dtype, ops[op], aligned, &plan);
     if (rc)
         return rc;
-    static const char *names[] = {"rows", "wg", "stream", "wstream"};
+    static const char *names[] = {"rows", "wg", "stream", "wstream", "wg2"};
     std::snprintf(buf, buf_len, "%s:%d:%d%s%s block=%d grid=%lld occupancy=%d cus=%d",
                   names[plan.kind], plan.a, plan.b, plan.exact ? " exact" : "",
                   plan.nbuf == 2 ? " nbuf=2" : "", plan.k.block, (long long)plan.grid,

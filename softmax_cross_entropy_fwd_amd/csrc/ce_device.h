@@ -999,8 +999,11 @@ __global__ void __launch_bounds__(NW * 64) rows_kernel(Params p)
 }
 
 // ---- one row per workgroup, row in registers --------------------------------
-template <int DT, int W, int K, int OP, bool EXACT>
-__global__ void __launch_bounds__(W * 64) wg_kernel(Params p)
+// OCC: waves per SIMD the register allocation must leave room for (4 with 8
+// waves per workgroup: two workgroups per CU, each holding its own row).
+template <int DT, int W, int K, int OP, bool EXACT, int OCC = 1>
+__global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC)))
+wg_kernel(Params p)
 {
     constexpr int E = Traits<DT>::E;
     constexpr int NT = W * 64;

@@ -3,7 +3,8 @@
 
 namespace cek {
 
-enum Kind : int { KIND_ROWS = 0, KIND_WG = 1, KIND_STREAM = 2, KIND_WSTREAM = 3 };
+// KIND_WG2: one row per 8-wave workgroup held to 128 VGPRs, two workgroups per CU.
+enum Kind : int { KIND_ROWS = 0, KIND_WG = 1, KIND_STREAM = 2, KIND_WSTREAM = 3, KIND_WG2 = 4 };
 
 struct KernelRef {
     const void *fn;   // host stub of a __global__ instance, or nullptr

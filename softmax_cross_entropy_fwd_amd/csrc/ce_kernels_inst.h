@@ -16,6 +16,9 @@ namespace {
     if (a == G && b == K) return KernelRef{(const void *)&rows_kernel<DT, G, K, OP, EXACT, 1>, 256};
 #define CE_WG(W, K) \
     if (a == W && b == K) return KernelRef{(const void *)&wg_kernel<DT, W, K, OP, EXACT>, W * 64};
+// 8-wave workgroups held to 128 VGPRs, so that two share a CU
+#define CE_WG2(W, K) \
+    if (a == W && b == K) return KernelRef{(const void *)&wg_kernel<DT, W, K, OP, EXACT, 4>, W * 64};
 #define CE_STREAM(W, K) \
     if (a == W && b == K) return KernelRef{(const void *)&stream_kernel<DT, W, K, OP>, W * 64};
 
@@ -38,6 +41,8 @@ KernelRef pick_all(int kind, int a, int b, int nbuf)
     } else if (kind == KIND_WG) {
         CE_WG(4, 8) CE_WG(8, 8) CE_WG(8, 12) CE_WG(8, 16) CE_WG(16, 8) CE_WG(16, 12) CE_WG(16, 16)
         CE_WG(4, 16) CE_WG(16, 4) CE_WG(16, 2) CE_WG(16, 3) CE_WG(16, 5) CE_WG(16, 6) CE_WG(16, 7)
+    } else if (kind == KIND_WG2 && DT != DT_F32) {
+        CE_WG2(8, 9) CE_WG2(8, 10) CE_WG2(8, 11) CE_WG2(8, 12) CE_WG2(8, 13)
     } else if (kind == KIND_WSTREAM && !EXACT && OP == EPI_NONE) {
         if (a == 1 && b == 4) return KernelRef{(const void *)&wstream_kernel<DT, 4>, 256};
         if (a == 1 && b == 2) return KernelRef{(const void *)&wstream_kernel<DT, 2>, 256};
@@ -64,6 +69,8 @@ KernelRef pick_table(int kind, int a, int b, int nbuf)
     } else if (kind == KIND_WG) {
         CE_WG(16, 2) CE_WG(16, 3) CE_WG(16, 4) CE_WG(16, 5) CE_WG(16, 6) CE_WG(16, 7)
         CE_WG(16, 8) CE_WG(16, 12) CE_WG(16, 16)
+    } else if (kind == KIND_WG2 && DT != DT_F32) {
+        CE_WG2(8, 9) CE_WG2(8, 10) CE_WG2(8, 11) CE_WG2(8, 12) CE_WG2(8, 13)
     } else if (kind == KIND_STREAM && !EXACT) {
         CE_STREAM(4, 4) CE_STREAM(8, 4) CE_STREAM(16, 4)
     }
@@ -73,6 +80,7 @@ KernelRef pick_table(int kind, int a, int b, int nbuf)
 #undef CE_ROWS
 #undef CE_ROWS1
 #undef CE_WG
+#undef CE_WG2
 #undef CE_STREAM
 
 }  // namespace

@@ -284,11 +284,14 @@ def test_every_softmax_and_grad_shape(ce, monkeypatch):
                        ("rows:32:4", 128), ("rows:64:4", 256), ("rows:64:8", 512),
                        ("rows:64:16", 1024), ("wg:16:2", 2048), ("wg:16:3", 3072),
                        ("wg:16:4", 4096), ("wg:16:5", 5120), ("wg:16:6", 6144),
-                       ("wg:16:7", 7168), ("wg:16:8", 8192),
+                       ("wg:16:7", 7168), ("wg:16:8", 8192), ("wg2:8:9", 4608),
+                       ("wg2:8:13", 6656),
                        ("wg:16:12", 12288), ("wg:16:16", 16384), ("stream:8:4", 1 << 30),
                        ("stream:16:4", 1 << 30)):
         monkeypatch.setenv("CE_FORCE_PLAN", shape)
         for dtype in DTYPES:
+            if shape.startswith("wg2") and dtype == "f32":
+                continue   # 16-bit storage only
             E = 4 if dtype == "f32" else 8
             for V in (3, 4 * E + 1, 64 * E, 3000, 20000):
                 if (V + 2 * E - 2) // E > cap:
@@ -333,17 +336,20 @@ def test_fused_and_split_backward_agree(ce):
 
 # The default mapping of the epilogues for rows past 16 KB (window vectors of
 # 16 bytes): streamed twice by 8-wave workgroups up to 3072 vectors, by
-# 16-wave ones up to 8192 unless the row fills a register tile exactly,
-# register tiles beyond; the backward from a given lse streams 16-bit rows
-# of 4096 vectors or more.
-EPI_DEFAULTS = [(1500, "stream:8:4"), (4096, "wg:16:4"), (6000, "stream:16:4"),
-                (7168, "wg:16:7"), (10240, "wg:16:12")]
+# 16-wave ones up to 8192 unless the row fills a register tile exactly
+# (16-bit rows of 4097-6656 vectors: 8-wave tiles, two per CU), register
+# tiles beyond; the backward from a given lse streams 16-bit rows of 4096
+# vectors or more.
+EPI_DEFAULTS = [(1500, "stream:8:4", "stream:8:4"), (4096, "wg:16:4", "wg:16:4"),
+                (6000, "stream:16:4", "wg2:8:12"), (7168, "wg:16:7", "wg:16:7"),
+                (7800, "stream:16:4", "stream:16:4"), (10240, "wg:16:12", "wg:16:12")]
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_epilogue_default_mappings(ce, dtype):
     E = 4 if dtype == "f32" else 8
-    for nvec, shape in EPI_DEFAULTS:
+    for nvec, shape32, shape16 in EPI_DEFAULTS:
+        shape = shape32 if dtype == "f32" else shape16
         V = nvec * E
         M = 40
         for op in (ce.CE_OP_SOFTMAX, ce.CE_OP_LOG_SOFTMAX):

@@ -139,7 +139,7 @@ SHAPES = ["rows:1:1", "rows:1:2", "rows:1:4", "rows:2:4", "rows:4:4", "rows:8:4"
           "rows:16:2", "rows:32:1", "rows:32:8", "rows:32:16", "rows:32:32", "rows:2:16",
           "wg:4:8", "wg:8:8", "wg:8:12", "wg:8:16", "wg:16:8", "wg:16:12", "wg:16:16",
           "wg:4:16", "wg:16:4", "wg:16:2", "wg:16:3", "wg:16:5", "wg:16:6", "wg:16:7",
-          "stream:4:8", "stream:8:4", "stream:8:8", "stream:16:4",
+          "wg2:8:9", "wg2:8:11", "wg2:8:13", "stream:4:8", "stream:8:4", "stream:8:8", "stream:16:4",
           "stream:4:16", "stream:1:4", "stream:2:4", "stream:4:4", "stream:1:8", "stream:2:8",
           "stream:1:16", "stream:16:2", "stream:16:1", "stream:8:2",
           "wstream:1:2", "wstream:1:4", "wstream:1:8"]
@@ -152,7 +152,7 @@ NBUFS = {"rows:64:16": ("1", "2", "17", "18"), "rows:4:8": ("1", "2", "17", "18"
 def test_every_kernel_shape(ce, shape, monkeypatch):
     kind, a, b = shape.split(":")
     a, b = int(a), int(b)
-    cap = a * b if kind == "rows" else (a * 64 * b if kind == "wg" else 1 << 30)
+    cap = a * b if kind == "rows" else (a * 64 * b if kind in ("wg", "wg2") else 1 << 30)
     monkeypatch.setenv("CE_FORCE_PLAN", shape)
     for nbuf in NBUFS.get(shape, ("1", "2") if kind == "rows" else ("1",)):
         monkeypatch.setenv("CE_FORCE_NBUF", nbuf)
@@ -161,6 +161,8 @@ def test_every_kernel_shape(ce, shape, monkeypatch):
 
 def _check_shape(ce, shape, kind, cap):
     for dtype in DTYPES:
+        if kind == "wg2" and dtype == "f32":
+            continue   # 16-bit storage only
         E = 4 if dtype == "f32" else 8
         for V in (1, 5, 13 * E + 3, 64 * E, 64 * E + 1, 3000, 20000):
             if (V + 2 * E - 2) // E > cap:
@@ -178,19 +180,23 @@ def _check_shape(ce, shape, kind, cap):
 # The fused backward's mapping for rows past 16 KB, one case per branch of the
 # plan table (window vectors: 16 bytes each): streamed twice by 8-wave
 # workgroups up to 3072 vectors, by 16-wave ones up to 8192 unless the row
-# fills a register tile exactly, register tiles of 12 or 16 x 1024 vectors up
-# to 16384.
-EPI_TABLE = [(1500, 0, "stream:8:4"), (3072, 0, "stream:8:4"), (4096, 0, "wg:16:4"),
-             (5120, 0, "wg:16:5"), (6283, 1, "stream:16:4"), (7168, 0, "wg:16:7"),
-             (8192, 0, "wg:16:8"), (8000, 0, "stream:16:4"), (10240, 0, "wg:16:12"),
-             (14336, 0, "wg:16:16")]
+# fills a register tile exactly (16-bit rows of 4097-6656 vectors: 8-wave
+# register tiles, two workgroups per CU), register tiles of 12 or 16 x 1024
+# vectors up to 16384.
+EPI_TABLE = [(1500, 0, "stream:8:4", "stream:8:4"), (3072, 0, "stream:8:4", "stream:8:4"),
+             (4096, 0, "wg:16:4", "wg:16:4"), (5120, 0, "wg:16:5", "wg:16:5"),
+             (5000, 0, "stream:16:4", "wg2:8:10"), (6283, 1, "stream:16:4", "wg2:8:13"),
+             (7168, 0, "wg:16:7", "wg:16:7"), (8192, 0, "wg:16:8", "wg:16:8"),
+             (8000, 0, "stream:16:4", "stream:16:4"), (10240, 0, "wg:16:12", "wg:16:12"),
+             (14336, 0, "wg:16:16", "wg:16:16")]
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_epilogue_plan_table(ce, dtype):
     E = 4 if dtype == "f32" else 8
     code = {"f32": 0, "f16": 1, "bf16": 2}[dtype]
-    for nvec, ragged, shape in EPI_TABLE:
+    for nvec, ragged, shape32, shape16 in EPI_TABLE:
+        shape = shape32 if dtype == "f32" else shape16
         V = nvec * E - (E - 1 if ragged else 0)
         M = 300 if nvec <= 3072 else 150
         plan = ce.ce_plan_describe(M, V, code, "mean", op=ce.CE_OP_FWD_BWD)
