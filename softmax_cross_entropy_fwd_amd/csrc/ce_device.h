@@ -201,12 +201,16 @@ __device__ __forceinline__ Vec ldv(const Vec *p)
 #endif
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// One 16-byte store.  Issued as a single vector store, so that the compiler
+// cannot merge its words with the element-wise stores of a row's boundary
+// vector (fp32 epilogues were split into 4- and 8-byte stores that way).
 __device__ __forceinline__ void stv(Vec *p, const Vec &v)
 {
 #if CE_NT_STORE
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        __builtin_nontemporal_store(v.w[i], &p->w[i]);
+    const u32x4_t x = {v.w[0], v.w[1], v.w[2], v.w[3]};
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t *>(p));
 #else
     *p = v;
 #endif
