@@ -115,14 +115,43 @@ def ce_plan_describe(M, V, dtype, reduction="mean", fwd_bwd=False, op=None):
 
 def workspace_for(device, stream, nbytes):
     """A workspace cached per (device, stream) (its contents need no initialization)."""
+    return _cached_workspace(device, int(stream.cuda_stream), nbytes, stream)
+
+
+def _cached_workspace(device, handle, nbytes, stream=None):
     import torch
-    key = (device.index, int(stream.cuda_stream))
+    key = (device.index, handle)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
+        if stream is None:
+            stream = torch.cuda.current_stream(device)
         with torch.cuda.stream(stream):
             ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
+
+
+def _stream_handle(dev):
+    """The raw hipStream_t of torch's current stream on dev (torch's own
+    accessor when it has one: the Stream object costs ~2 us per call)."""
+    import torch
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return int(raw(dev.index))
+    return int(torch.cuda.current_stream(dev).cuda_stream)
+
+
+_ws_bytes = {}
+
+
+def _workspace_bytes(lib, M, V, code, red):
+    key = (M, V, code, red)
+    n = _ws_bytes.get(key)
+    if n is None:
+        n = int(lib.ce_workspace_bytes(M, V, code, red))
+        if len(_ws_bytes) < 4096:
+            _ws_bytes[key] = n
+    return n
 
 
 def _check_logits(logits):
@@ -173,11 +202,11 @@ def _call(fn_name, logits, targets, reduction, out, workspace, lse=None):
         out = torch.empty((M,) if red == CE_NONE else (), dtype=torch.float32, device=dev)
     else:
         _check_rows(out, M if red == CE_NONE else 1, dev, "out")
-    stream = torch.cuda.current_stream(dev)
+    stream = _stream_handle(dev)
     code = _dtype_code(logits)
-    nbytes = int(lib.ce_workspace_bytes(M, V, code, red))
+    nbytes = _workspace_bytes(lib, M, V, code, red)
     if nbytes and workspace is None:
-        workspace = workspace_for(dev, stream, nbytes)
+        workspace = _cached_workspace(dev, stream, nbytes)
     ws_ptr = workspace.data_ptr() if nbytes else None
     ws_len = workspace.numel() * workspace.element_size() if nbytes else 0
     args = [logits.data_ptr(), targets.data_ptr(), M, V, code, red,
@@ -185,7 +214,7 @@ def _call(fn_name, logits, targets, reduction, out, workspace, lse=None):
     if fn_name == "ce_fwd_lse":
         _check_rows(lse, M, dev, "lse")
         args.append(lse.data_ptr() if M else None)
-    rc = _invoke(getattr(lib, fn_name), dev, args + [ws_ptr, ws_len, stream.cuda_stream])
+    rc = _invoke(getattr(lib, fn_name), dev, args + [ws_ptr, ws_len, stream])
     if rc:
         raise CEError(rc, fn_name)
     return out
@@ -217,11 +246,11 @@ def _workspace(lib, logits, red, workspace):
     unless one is given; (None, 0) when the call uses none."""
     import torch
     M, V = logits.shape
-    nbytes = int(lib.ce_workspace_bytes(M, V, _dtype_code(logits), red))
+    nbytes = _workspace_bytes(lib, M, V, _dtype_code(logits), red)
     if not nbytes:
         return None, 0
     if workspace is None:
-        workspace = workspace_for(logits.device, torch.cuda.current_stream(logits.device), nbytes)
+        workspace = _cached_workspace(logits.device, _stream_handle(logits.device), nbytes)
     return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
@@ -241,12 +270,12 @@ def ce_bwd(logits, targets, lse, reduction="mean", dloss=None, grad=None, worksp
     if grad is None:
         grad = torch.empty_like(logits)
     _check_like(grad, logits, "grad")
-    stream = torch.cuda.current_stream(dev)
+    stream = _stream_handle(dev)
     ws_ptr, ws_len = _workspace(lib, logits, red, workspace)
     rc = _invoke(lib.ce_bwd, dev,
                  [logits.data_ptr(), targets.data_ptr(), lse.data_ptr() if M else None,
                   dloss.data_ptr() if dloss is not None else None, M, V, _dtype_code(logits),
-                  red, grad.data_ptr() if M else None, ws_ptr, ws_len, stream.cuda_stream])
+                  red, grad.data_ptr() if M else None, ws_ptr, ws_len, stream])
     if rc:
         raise CEError(rc, "ce_bwd")
     return grad
@@ -266,13 +295,13 @@ def ce_softmax(logits, log_softmax=False, out=None, lse=None, workspace=None):
     _check_like(out, logits, "out")
     if lse is not None:
         _check_rows(lse, M, dev, "lse")
-    stream = torch.cuda.current_stream(dev)
+    stream = _stream_handle(dev)
     ws_ptr, ws_len = _workspace(lib, logits, CE_NONE, workspace)
     rc = _invoke(lib.ce_softmax, dev,
                  [logits.data_ptr(), M, V, _dtype_code(logits), int(bool(log_softmax)),
                   out.data_ptr() if M else None,
                   lse.data_ptr() if (lse is not None and M) else None,
-                  ws_ptr, ws_len, stream.cuda_stream])
+                  ws_ptr, ws_len, stream])
     if rc:
         raise CEError(rc, "ce_softmax")
     return out
