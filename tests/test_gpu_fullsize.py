@@ -61,6 +61,12 @@ def test_full_size(ce, name):
     check_scalar(loss.item(), oracle.reduce(per_row, "mean"))
     cscale = 1.0 / M
     rows = sample_rows(M, 48, seed=M + V)
+    # plus the rows whose target dominates (smallest losses) and rows whose
+    # loss is ln V (all-equal rows, in the stress structure)
+    order = np.argsort(per_row)
+    special = set(order[:4].tolist())
+    special.update(np.nonzero(np.abs(per_row - np.log(V)) < 1e-9)[0][:4].tolist())
+    rows = sorted(set(rows) | special)
     for r in rows:
         want, want64 = oracle.grad_rows(xb, tn, dtype=dtype, c=cscale, row0=r, nrows=1,
                                         want64=True)
