@@ -719,6 +719,17 @@ def main():
     # after the timed lines, so the 4 GiB probe buffers do not precede them
     ceilings = None if args.no_extra else measure_ceilings(
         log, c["M"] * c["V"] * inputs.ELEM_BYTES[c["dtype"]])
+    if ceilings:
+        # each line against the probe with its own access pattern: a read for
+        # the forwards, a copy for the out-of-place writers, an in-place
+        # rewrite of rows held in registers for the in-place fused backward
+        ref = {"fwd": "read_GBps", "fwd_lse": "read_GBps", "bwd": "copy_GBps",
+               "softmax": "copy_GBps", "log_softmax": "copy_GBps",
+               "fwd_bwd": "inplace_rows_GBps"}
+        for a in also:
+            key = ref.get(a.get("op"))
+            if key and a.get("alg_GBps") and ceilings.get(key):
+                a["frac_of_probe"] = {"probe": key, "frac": a["alg_GBps"] / ceilings[key]}
     traffic = load_traffic(args.workload, op, red)
     cpu = None if args.no_cpu else cpu_baseline(args.workload, op, red, log)
 
