@@ -156,3 +156,42 @@ def test_batch_beyond_2_31_elements(ce):
     for r in rows:
         check_grads(inputs.host_bits(x[r]), want[r], dtype, 1.0 / M)
     say("ok")
+
+
+@pytest.mark.parametrize("dtype,V", [("f32", 17), ("f16", 9)])
+def test_short_rows_beyond_2_31_elements(ce, dtype, V):
+    # many short ragged rows held in the registers of a few lanes each (the
+    # rows kernel), past the 32-bit element range
+    import torch
+    M = (2 ** 31) // V + 4099
+    assert M * V > 2 ** 31
+    dev = torch.device("cuda:0")
+    say("short rows", dtype, M, V, "elements", M * V)
+    x, t = inputs.make(dtype, M, V, sigma=3.0, seed=2026, device=dev, chunk_rows=1 << 24)
+    xb, tn = inputs.host_bits(x), t.cpu().numpy()
+    m = x.max(dim=1).values.float().cpu().numpy()
+    xt = x.gather(1, t[:, None])[:, 0].float().cpu().numpy()
+    say("plan", ce.ce_plan_describe(M, V, DCODE[dtype], "none"))
+    loss_o = oracle.loss_rows(xb, tn, dtype=dtype)
+    say("oracle losses done")
+
+    got = ce.ce_fwd(x, t, "none")
+    torch.cuda.synchronize()
+    check_row_losses(got.cpu().numpy(), loss_o, None, tn, dtype, m=m, xt=xt)
+    del got
+    check_scalar(ce.ce_fwd(x, t, "sum").item(), oracle.reduce(loss_o, "sum"))
+    say("forward ok")
+
+    boundary = (2 ** 31) // V
+    rng = np.random.default_rng(12)
+    rows = sorted({0, 1, boundary - 1, boundary, boundary + 1, M - 2, M - 1}
+                  | set(rng.choice(M, size=64, replace=False).tolist()))
+    want = {r: oracle.grad_rows(xb, tn, dtype=dtype, c=1.0 / M, row0=r, nrows=1)[0]
+            for r in rows}
+    del xb
+    mean = ce.ce_fwd_bwd_inplace(x, t, "mean")
+    torch.cuda.synchronize()
+    check_scalar(mean.item(), oracle.reduce(loss_o, "mean"))
+    for r in rows:
+        check_grads(inputs.host_bits(x[r]), want[r], dtype, 1.0 / M)
+    say("ok")
