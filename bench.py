@@ -153,8 +153,16 @@ def summarize_pmc(fetch_csv, write_csv, workload, op, reduction, kernel_prefix, 
     is_probe_copy = lambda k: "(anonymous namespace)::copy_kernel<" in k and "native" not in k
     f_copy = pick(f, is_probe_copy)
     w_copy = pick(w, is_probe_copy)
-    f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
     f_ce, w_ce = pick(f, ce_kernel), pick(w, ce_kernel)
+    missing = [what for what, v in (("the calibration copy's FETCH_SIZE", f_copy),
+                                    ("the calibration copy's WRITE_SIZE", w_copy),
+                                    ("FETCH_SIZE of kernel '%s'" % kernel_prefix, f_ce),
+                                    ("WRITE_SIZE of kernel '%s'" % kernel_prefix, w_ce))
+               if v is None]
+    if missing:
+        raise ValueError("no counter rows for %s in %s / %s (kernels seen: %s)" % (
+            ", ".join(missing), fetch_csv, write_csv, sorted(set(f) | set(w))[:8]))
+    f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
     hbm = f_ce * f_scale + w_ce * w_scale
     lines = [
         "# HBM traffic of the %s %s (%s) kernel, from rocprofv3 counters" % (workload, op, reduction),
@@ -367,9 +375,22 @@ def measure_ceilings(log, size_bytes=None):
             t.append(a.elapsed_time(b))
         return min(t)
 
-    read = max(nb / best(lambda: lib.probe_read(buf.data_ptr(), nb, g, u, blk, out.data_ptr(),
-                                                st.cuda_stream)) / 1e6
-               for g, u, blk in ((1024, 8, 256), (512, 4, 1024), (2048, 8, 256)))
+    lib.probe_read_tiles.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    tiles_out = torch.empty(2048 * 256, dtype=torch.float32, device="cuda:0")
+    # (grid, tile vectors per lane, non-temporal) of the rows-pattern read:
+    # persistent grids of 1-8 workgroups of 4 wavefronts per CU
+    tile_shapes = [(g, k, nt) for g in (256, 512, 1024, 2048) for k in (8, 16) for nt in (0, 1)]
+
+    def read_tiles(ptr, nbytes, g, k, nt):
+        return lib.probe_read_tiles(ptr, nbytes, g, k, nt, tiles_out.data_ptr(), st.cuda_stream)
+
+    read_plain = max(nb / best(lambda: lib.probe_read(buf.data_ptr(), nb, g, u, blk,
+                                                      out.data_ptr(), st.cuda_stream)) / 1e6
+                     for g, u, blk in ((1024, 8, 256), (512, 4, 1024), (2048, 8, 256)))
+    read_tiles_4g = max(nb / best(lambda: read_tiles(buf.data_ptr(), nb, g, k, nt)) / 1e6
+                        for g, k, nt in tile_shapes)
+    read = max(read_plain, read_tiles_4g)
     read_at_size = None
     if size_bytes and size_bytes % 16 == 0 and size_bytes <= nb // 2:
         flip = [0]
@@ -378,9 +399,20 @@ def measure_ceilings(log, size_bytes=None):
             flip[0] ^= 1
             return lib.probe_read(buf.data_ptr() + flip[0] * (nb // 2), size_bytes, g, u, blk,
                                   out.data_ptr(), st.cuda_stream)
-        read_at_size = max(size_bytes / best(lambda: read_rotating(g, u, blk), n=10) / 1e6
-                           for g, u, blk in ((1024, 8, 256), (512, 4, 1024), (2048, 8, 256),
-                                             (256, 16, 256)))
+
+        def tiles_rotating(g, k, nt):
+            flip[0] ^= 1
+            return read_tiles(buf.data_ptr() + flip[0] * (nb // 2), size_bytes, g, k, nt)
+        plain_at_size = max(size_bytes / best(lambda: read_rotating(g, u, blk), n=10) / 1e6
+                            for g, u, blk in ((1024, 8, 256), (512, 4, 1024), (2048, 8, 256),
+                                              (256, 16, 256)))
+        tiles_at_size = {(g, k, nt): size_bytes / best(lambda: tiles_rotating(g, k, nt), n=10) / 1e6
+                         for g, k, nt in tile_shapes}
+        best_shape = max(tiles_at_size, key=tiles_at_size.get)
+        read_at_size = max(plain_at_size, tiles_at_size[best_shape])
+        log("read over %d bytes: plain %.0f GB/s, rows pattern %.0f GB/s (grid %d, %d vectors "
+            "per lane, non-temporal %d)" % (size_bytes, plain_at_size, tiles_at_size[best_shape],
+                                           *best_shape))
     half = nb // 2
     copy = max(2 * half / best(lambda: lib.probe_copy(buf.data_ptr() + half, buf.data_ptr(), half,
                                                        g, u, st.cuda_stream)) / 1e6
@@ -395,50 +427,65 @@ def measure_ceilings(log, size_bytes=None):
                   for k, g in ((16, 256), (16, 512), (8, 512)))
     xb = buf.view(torch.bfloat16)
     inplace_torch = 2 * nb / best(lambda: xb.mul_(1.0)) / 1e6
-    del buf, out, xb
+    # torch's own copy (out of place) over the same bytes, for the copy ceiling
+    half_b = buf.view(torch.bfloat16)[:nb // 4]
+    dst_b = buf.view(torch.bfloat16)[nb // 4:nb // 2]
+    copy_torch = 2 * (nb // 2) / best(lambda: dst_b.copy_(half_b)) / 1e6
+    del buf, out, xb, tiles_out, half_b, dst_b
     torch.cuda.empty_cache()
-    log("measured ceilings: read %.0f GB/s, copy %.0f GB/s (read + write), in place %.0f GB/s "
-        "(rows in registers; torch's in-place multiply %.0f GB/s)"
-        % (read, copy, inplace, inplace_torch))
+    log("measured ceilings: read %.0f GB/s (plain %.0f, rows pattern %.0f), copy %.0f GB/s "
+        "(read + write; torch's copy %.0f), in place %.0f GB/s (rows in registers; torch's "
+        "in-place multiply %.0f GB/s)" % (read, read_plain, read_tiles_4g, copy, copy_torch,
+                                         inplace, inplace_torch))
     if read_at_size is not None:
         log("read over the headline workload's %d bytes: %.0f GB/s" % (size_bytes, read_at_size))
-    return {"read_GBps": round(read, 1), "copy_GBps": round(copy, 1),
+    # the best read and the best read + write anything measured here reached:
+    # the ceilings each line is held against (a copy, an in-place rewrite and
+    # torch's kernels all move one read and one write per element)
+    best_rw = max(copy, copy_torch, inplace, inplace_torch)
+    return {"read_GBps": round(read, 1), "read_plain_GBps": round(read_plain, 1),
+            "read_rows_pattern_GBps": round(read_tiles_4g, 1), "copy_GBps": round(copy, 1),
+            "copy_torch_GBps": round(copy_torch, 1),
             "read_at_size_GBps": None if read_at_size is None else round(read_at_size, 1),
             "inplace_rows_GBps": round(inplace, 1), "inplace_torch_GBps": round(inplace_torch, 1),
+            "best_read_GBps": round(read, 1), "best_read_write_GBps": round(best_rw, 1),
             "how": "probe/bw_probe.hip over 4 GiB (copy: 2 GiB each way; in place: 4 GiB "
-                   "rewritten), best launch shape; torch: bf16 mul_(1.0) over the same 4 GiB"}
+                   "rewritten), best launch shape; the reads also with the rows kernel's tile "
+                   "pattern over persistent grids; torch: bf16 mul_(1.0) in place and copy_ "
+                   "over the same bytes"}
 
 
-def time_tiny(ce, log, calls=1000, cpu_sample=False):
+def time_tiny(ce, log, calls=1000, cpu_sample=False, reduction="mean"):
     """The tiny workload is launch-bound: 1000 back-to-back calls timed as a
     whole, in microseconds per call."""
     import torch
     from softmax_cross_entropy_fwd_amd import inputs
     x, t = inputs.make_config("tiny", device="cuda:0")
-    out = torch.empty((), dtype=torch.float32, device="cuda:0")
+    out = torch.empty((64,) if reduction == "none" else (), dtype=torch.float32, device="cuda:0")
     for _ in range(100):
-        ce.ce_fwd(x, t, "mean", out=out)
+        ce.ce_fwd(x, t, reduction, out=out)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     w0 = time.perf_counter()
     a.record()
     for _ in range(calls):
-        ce.ce_fwd(x, t, "mean", out=out)
+        ce.ce_fwd(x, t, reduction, out=out)
     b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     us = a.elapsed_time(b) * 1e3 / calls
     # the same call captured in a HIP graph (the launch-bound case graphs are for)
-    ws = torch.empty(ce.ce_workspace_bytes(64, 1000, 0, "mean"), dtype=torch.uint8, device="cuda:0")
+    ws = torch.empty(max(1, ce.ce_workspace_bytes(64, 1000, 0, reduction)), dtype=torch.uint8,
+                     device="cuda:0")
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        ce.ce_fwd(x, t, "mean", out=out, workspace=ws)
+        ce.ce_fwd(x, t, reduction, out=out, workspace=ws)
     torch.cuda.current_stream().wait_stream(s)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for _ in range(10):
-            ce.ce_fwd(x, t, "mean", out=out, workspace=ws)
+            ce.ce_fwd(x, t, reduction, out=out, workspace=ws)
     for _ in range(10):
         graph.replay()
     torch.cuda.synchronize()
@@ -448,10 +495,10 @@ def time_tiny(ce, log, calls=1000, cpu_sample=False):
     b.record()
     torch.cuda.synchronize()
     gus = a.elapsed_time(b) * 1e3 / calls
-    log("tiny fwd mean: %.2f us per call over %d back-to-back calls (wall %.2f us); "
+    log("tiny fwd " + reduction + ": %.2f us per call over %d back-to-back calls (wall %.2f us); "
         "%.2f us per call replayed from a HIP graph of 10 calls" % (
             us, calls, wall * 1e6 / calls, gus))
-    res = {"workload": "tiny", "op": "fwd", "reduction": "mean", "M": 64, "V": 1000,
+    res = {"workload": "tiny", "op": "fwd", "reduction": reduction, "M": 64, "V": 1000,
            "us_per_call": us, "wall_us_per_call": wall * 1e6 / calls, "calls": calls,
            "graph_us_per_call": gus, "note": "launch-bound; no roofline claim"}
     if cpu_sample:
@@ -463,7 +510,7 @@ def time_tiny(ce, log, calls=1000, cpu_sample=False):
             oracle.set_num_threads(n)
             reps, t0 = 0, time.perf_counter()
             while time.perf_counter() - t0 < 0.5:
-                oracle.fwd(xb, tn, dtype="f32", reduction="mean")
+                oracle.fwd(xb, tn, dtype="f32", reduction=reduction)
                 reps += 1
             res[key] = (time.perf_counter() - t0) * 1e6 / reps
         oracle.set_num_threads(threads)
@@ -704,8 +751,13 @@ def main():
                         ("stress", "fwd"), ("stress", "fwd_bwd"), ("skinny", "fwd")):
             also.append(time_workload(ce, wl, eop, "mean", max(20, args.steps // 5),
                                       max(3, args.warmup // 5), log, cpu_sample=not args.no_cpu))
+        # the skinny workload's per-row losses (reduction none: one kernel, M
+        # fp32 losses written)
+        also.append(time_workload(ce, "skinny", "fwd", "none", max(20, args.steps // 5),
+                                  max(3, args.warmup // 5), log, cpu_sample=not args.no_cpu))
         # the tiny workload: launch-bound, microseconds per call
         also.append(time_tiny(ce, log, cpu_sample=not args.no_cpu))
+        also.append(time_tiny(ce, log, reduction="none", cpu_sample=not args.no_cpu))
         if args.extra_shapes:
             # one GPU's share of a sharded LM head: rows (M / 8) and vocabulary
             # (V / 8)
@@ -723,9 +775,12 @@ def main():
         # each line against the probe with its own access pattern: a read for
         # the forwards, a copy for the out-of-place writers, an in-place
         # rewrite of rows held in registers for the in-place fused backward
-        ref = {"fwd": "read_GBps", "fwd_lse": "read_GBps", "bwd": "copy_GBps",
-               "softmax": "copy_GBps", "log_softmax": "copy_GBps",
-               "fwd_bwd": "inplace_rows_GBps"}
+        # each line against the best rate measured on the box for its traffic:
+        # the best read for the forwards, the best read + write (copy, in-place
+        # probe, torch's copy and in-place multiply) for the writers
+        ref = {"fwd": "best_read_GBps", "fwd_lse": "best_read_GBps",
+               "bwd": "best_read_write_GBps", "softmax": "best_read_write_GBps",
+               "log_softmax": "best_read_write_GBps", "fwd_bwd": "best_read_write_GBps"}
         for a in also:
             key = ref.get(a.get("op"))
             if key and a.get("alg_GBps") and ceilings.get(key):

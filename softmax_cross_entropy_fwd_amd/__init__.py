@@ -145,7 +145,9 @@ _ws_bytes = {}
 
 
 def _workspace_bytes(lib, M, V, code, red):
-    key = (M, V, code, red)
+    # the size also depends on the split and plan overrides the library reads
+    env = os.environ
+    key = (M, V, code, red, env.get("CE_FORCE_SPLIT"), env.get("CE_FORCE_PLAN"))
     n = _ws_bytes.get(key)
     if n is None:
         n = int(lib.ce_workspace_bytes(M, V, code, red))

@@ -41,6 +41,61 @@ __global__ void __launch_bounds__(NT) read_kernel(const V4 *__restrict__ src, in
     }
 }
 
+// The read with the cross-entropy rows kernel's access pattern: each
+// wavefront takes tiles of 64*K contiguous vectors (lane l reads vectors l,
+// l + 64, ...), tiles grid-strided over all wavefronts of a persistent grid;
+// the next tile's K loads are issued (into a second register set) before the
+// current tile is folded, so every wavefront keeps a tile of loads in flight.
+// NT: non-temporal loads.
+template <int K, bool NT>
+__device__ __forceinline__ void load_tile(V4 (&r)[K], const V4 *src, int64_t tile, int64_t nvec,
+                                          int lane)
+{
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        int64_t i = tile * 64 * K + lane + 64 * k;
+        i = i < nvec ? i : nvec - 1;
+        if constexpr (NT) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                r[k].w[j] = __builtin_nontemporal_load(&src[i].w[j]);
+        } else {
+            r[k] = src[i];
+        }
+    }
+}
+
+template <int K, bool NT>
+__global__ void __launch_bounds__(256) read_tiles_kernel(const V4 *__restrict__ src, int64_t nvec,
+                                                         float *__restrict__ out)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+    const int64_t ntiles = (nvec + 64 * K - 1) / (64 * K);
+    int64_t tile = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    uint32_t acc = 0;
+    if (tile < ntiles) {
+        V4 a[K], b[K];
+        load_tile<K, NT>(a, src, tile, nvec, lane);
+        for (; tile < ntiles; tile += 2 * nwaves) {
+            const int64_t t1 = tile + nwaves < ntiles ? tile + nwaves : tile;
+            load_tile<K, NT>(b, src, t1, nvec, lane);
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                acc ^= a[k].w[0] ^ a[k].w[1] ^ a[k].w[2] ^ a[k].w[3];
+            if (tile + nwaves >= ntiles)
+                break;
+            const int64_t t2 = tile + 2 * nwaves < ntiles ? tile + 2 * nwaves : t1;
+            load_tile<K, NT>(a, src, t2, nvec, lane);
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                acc ^= b[k].w[0] ^ b[k].w[1] ^ b[k].w[2] ^ b[k].w[3];
+        }
+    }
+    // one value per lane so the loads cannot be dropped
+    out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = __uint_as_float(acc & 0x7fffffu);
+}
+
 template <int U>
 __global__ void __launch_bounds__(256) copy_kernel(V4 *__restrict__ dst, const V4 *__restrict__ src,
                                                    int64_t nvec)
@@ -139,6 +194,26 @@ int probe_read(const void *src, int64_t bytes, int grid, int unroll, int block, 
     PROBE_READ(1, 256) PROBE_READ(4, 256) PROBE_READ(8, 256) PROBE_READ(16, 256)
     PROBE_READ(1, 1024) PROBE_READ(2, 1024) PROBE_READ(4, 1024) PROBE_READ(8, 1024)
 #undef PROBE_READ
+    return -1;
+}
+
+// The rows-kernel pattern read (read_tiles_kernel): tiles of 64*k vectors,
+// k = 8 or 16; nt != 0 for non-temporal loads; 256 threads per workgroup, out
+// needs 256 * grid floats.
+int probe_read_tiles(const void *src, int64_t bytes, int grid, int k, int nt, float *out,
+                     void *stream)
+{
+    const int64_t nvec = bytes / 16;
+    if (!src || !out || nvec < 1 || grid < 1)
+        return -1;
+    hipStream_t s = (hipStream_t)stream;
+    const V4 *p = (const V4 *)src;
+#define PROBE_TILES(K, N) \
+    if (k == K && (nt != 0) == N) { \
+        hipLaunchKernelGGL((read_tiles_kernel<K, N>), dim3(grid), dim3(256), 0, s, p, nvec, out); \
+        return hipGetLastError() == hipSuccess ? 0 : -6; }
+    PROBE_TILES(8, false) PROBE_TILES(16, false) PROBE_TILES(8, true) PROBE_TILES(16, true)
+#undef PROBE_TILES
     return -1;
 }
 

@@ -207,3 +207,36 @@ def check_lse(got, want, xb, dtype, m=None):
     bad = err > bound
     assert not bad.any(), "lse mismatch at rows %s: got %s want %s" % (
         np.nonzero(ok)[0][bad][:5], got[ok][bad][:5], want[ok][bad][:5])
+
+
+def check_grads_on_device(got, want_bits, dtype):
+    """Every element of got (a device tensor of fp16/bf16 gradients) within
+    GRAD_ULP units in the last place of want_bits (the oracle's uint16 bit
+    patterns, computed on the host), with NaN positions equal.  The oracle's
+    values are copied to the device and compared there, so that rows of the
+    full-size workloads are checked in seconds.  Returns the largest ulp
+    distance."""
+    import torch
+    assert dtype in ("f16", "bf16")
+    w = torch.from_numpy(np.ascontiguousarray(want_bits).view(np.int16)).to(got.device)
+    g = got.detach().reshape(w.shape).view(torch.int16)
+    gi, wi = g.to(torch.int32) & 0xFFFF, w.to(torch.int32) & 0xFFFF
+    nan_mask = 0x7C00 if dtype == "f16" else 0x7F80
+    frac_mask = 0x03FF if dtype == "f16" else 0x007F
+
+    def is_nan(b):
+        return ((b & nan_mask) == nan_mask) & ((b & frac_mask) != 0)
+
+    def ordered(b):
+        mag = b & 0x7FFF
+        return torch.where((b & 0x8000) != 0, -mag, mag)
+
+    gnan, wnan = is_nan(gi), is_nan(wi)
+    assert torch.equal(gnan, wnan), "NaN positions differ"
+    d = (ordered(gi) - ordered(wi)).abs()
+    d = torch.where(wnan, torch.zeros_like(d), d)
+    worst = int(d.max().item()) if d.numel() else 0
+    if worst > GRAD_ULP:
+        bad = torch.nonzero(d > GRAD_ULP)[:5].cpu().tolist()
+        raise AssertionError("grad ulp mismatch (max %d) at %s" % (worst, bad))
+    return worst

@@ -75,6 +75,21 @@ def test_traffic_summary_scales_by_the_copy_and_checks_the_source(tmp_path, monk
     assert bench.load_traffic("classifier", "fwd", "mean") is None
 
 
+def test_traffic_summary_refuses_a_kernel_with_no_counter_rows(tmp_path):
+    copy = "void (anonymous namespace)::copy_kernel<4>((anonymous namespace)::V4*)"
+    ce = "void cek::rows_kernel<0, 64, 16, 0, true, 1, 4>(cek::Params)"
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", [(copy, 512 * 1024), (ce, 262144)])
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", [(copy, 1024 * 1024), (ce, 1)])
+    with pytest.raises(ValueError, match="wg_kernel"):
+        bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "lmhead",
+                            "fwd_bwd", "mean", "wg_kernel<2, 16, 16", "cmd")
+    # no calibration copy in the run: also refused, by name
+    _counter_csv(tmp_path / "f2.csv", "FETCH_SIZE", [(ce, 262144)])
+    with pytest.raises(ValueError, match="calibration copy"):
+        bench.summarize_pmc(str(tmp_path / "f2.csv"), str(tmp_path / "w.csv"), "classifier",
+                            "fwd", "mean", "rows_kernel<0, 64, 16, 0, true", "cmd")
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)

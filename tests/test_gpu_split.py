@@ -6,7 +6,8 @@ each other.  Tolerances are those of the other parity tests (gpu_util)."""
 import numpy as np
 import pytest
 
-from gpu_util import check_grads, check_scalar, host_grad_bits, oracle, inputs, say
+from gpu_util import (check_grads, check_row_losses, check_scalar, host_grad_bits, oracle,
+                      inputs, say)
 from test_gpu_epilogues import bwd_case, fwd_lse_case, softmax_case
 from test_gpu_parity import DTYPES, run_and_check
 
@@ -114,13 +115,21 @@ def test_split_dominant_targets_and_bad_targets(ce, monkeypatch):
 
 
 def test_split_matches_one_row_path(ce, monkeypatch):
+    # The split and the one-row paths agree with each other, and both with the
+    # oracle element by element.  For bf16 rows of 131072 the one-row path is
+    # the exact 16-wave register tile the full-size LM head runs.
     import torch
     for dtype, V in LONG:
         x, t = inputs.make(dtype, 24, V, 2.0, seed=V + 99, device="cuda:0")
+        xb, tn = inputs.host_bits(x), t.cpu().numpy()
         a = ce.ce_fwd(x, t, "none")
         ga = x.clone()
         la = ce.ce_fwd_bwd_inplace(ga, t, "mean")
         monkeypatch.setenv("CE_FORCE_SPLIT", "0")
+        plan = ce.ce_plan_describe(24, V, DCODE[dtype], "mean", fwd_bwd=True)
+        say("one-row plan", dtype, V, plan)
+        if (dtype, V) == ("bf16", 131072):
+            assert plan.startswith("wg:16:16 exact "), plan
         b = ce.ce_fwd(x, t, "none")
         gb = x.clone()
         lb = ce.ce_fwd_bwd_inplace(gb, t, "mean")
@@ -130,6 +139,27 @@ def test_split_matches_one_row_path(ce, monkeypatch):
         check_scalar(la.item(), lb.item(), rtol=2e-6)
         check_grads(host_grad_bits(ga), host_grad_bits(gb), dtype, 1.0 / 24,
                     inputs.host_bits(gb).astype(np.float64) if dtype == "f32" else None)
+        # both against the oracle
+        per_row = oracle.loss_rows(xb, tn, dtype=dtype)
+        check_row_losses(b.cpu().numpy(), per_row, xb, tn, dtype)
+        check_row_losses(a.cpu().numpy(), per_row, xb, tn, dtype)
+        check_scalar(lb.item(), oracle.reduce(per_row, "mean"))
+        want, want64 = oracle.grad_rows(xb, tn, dtype=dtype, c=1.0 / 24, want64=True)
+        check_grads(host_grad_bits(gb), want, dtype, 1.0 / 24, want64)
+        check_grads(host_grad_bits(ga), want, dtype, 1.0 / 24, want64)
+
+
+@pytest.mark.parametrize("M", [129, 160])
+def test_lmhead_register_tile_every_element(ce, M):
+    # More than 128 rows of 131072 bf16: the default plan is the exact 16-wave
+    # register tile (no split), compared with the oracle on every element.
+    plan = ce.ce_plan_describe(M, 131072, DCODE["bf16"], "mean", fwd_bwd=True)
+    say("plan", M, plan)
+    assert plan.startswith("wg:16:16 exact "), plan
+    run_and_check(ce, "bf16", M, 131072, 2.0, seed=103 + M, reduction="mean", op="fwd_bwd")
+    run_and_check(ce, "bf16", M, 131072, 2.0, seed=104 + M, reduction="none", op="fwd_bwd")
+    run_and_check(ce, "bf16", M, 131072, 8.0, seed=105 + M, structure="stress",
+                  reduction="sum", op="fwd_bwd")
 
 
 def test_split_forced_slice_counts(ce, monkeypatch):
