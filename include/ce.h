@@ -65,7 +65,9 @@ enum {
     CE_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed */
     CE_ERR_ALIGNMENT = -7,   /* a pointer not aligned to its element size, or an
                                 output not at the logits' address modulo 16 */
-    CE_ERR_ALIAS = -8        /* an output overlaps another output or an input */
+    CE_ERR_ALIAS = -8,       /* an output overlaps another output or an input */
+    CE_ERR_SCRATCH = -9      /* ce_fwd_noalloc: the call needs more than the
+                                library's static scratch holds */
 };
 
 /* Largest supported row length (classes per row). */
@@ -104,6 +106,32 @@ size_t ce_workspace_bytes(int64_t M, int64_t V, ce_dtype_t dtype,
 int ce_fwd(const void *logits, const int64_t *targets, int64_t M, int64_t V,
            ce_dtype_t dtype, ce_reduction_t reduction, float *out,
            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * forward as ce_fwd (same kernels, plans and bits) without a workspace
+ * argument: the scratch its kernels need (the fp64 partial sums of a mean or
+ * sum, the statistics of split rows) is a static device array of the library,
+ * CE_NOALLOC_SCRATCH_BYTES per GPU, held by every GPU the library runs on until
+ * the process ends.  The call allocates nothing (no hipMalloc, no library
+ * allocation); its device address is looked up on the first call on each
+ * device.
+ *
+ * The scratch covers every call under the default launch plans.  A call that
+ * would need more (only a split forced for tuning through CE_FORCE_SPLIT can)
+ * returns CE_ERR_SCRATCH before any HIP call; other argument errors are those
+ * of ce_fwd, and none involves a workspace.
+ *
+ * All calls on one GPU share its scratch and nothing in it needs clearing
+ * between calls.  Calls that may run concurrently on one GPU (on different
+ * streams, or from different host threads without ordering) race on it and
+ * must not overlap; calls on one stream are ordered and safe.
+ */
+#define CE_NOALLOC_SCRATCH_BYTES 229888 /* 128 KiB + 128 * (64 * 12 + 4) bytes */
+int ce_fwd_noalloc(const void *logits, const int64_t *targets, int64_t M,
+                   int64_t V, ce_dtype_t dtype, ce_reduction_t reduction,
+                   float *out, void *stream);
 
 /*
  * Forward that also saves each row's log-sum-exp, for a later ce_bwd:

@@ -7,6 +7,7 @@ sizes and pass torch's current HIP stream.  Every step of the computation runs
 in the library's HIP kernels; if the library is missing, every call raises.
 
     loss = ce_fwd(logits, targets, reduction="mean")
+    loss = ce_fwd_noalloc(logits, targets, reduction="mean", out=out)   # no workspace
     loss = ce_fwd_bwd_inplace(logits, targets, reduction="mean")   # logits <- grad
     loss, lse = ce_fwd_lse(logits, targets, reduction="mean")
     grad = ce_bwd(logits, targets, lse, reduction="mean", dloss=None)
@@ -26,6 +27,8 @@ CE_NONE, CE_MEAN, CE_SUM = 0, 1, 2
 CE_OK = 0
 CE_ERR_NULL, CE_ERR_SHAPE, CE_ERR_DTYPE, CE_ERR_REDUCTION = -1, -2, -3, -4
 CE_ERR_WORKSPACE, CE_ERR_HIP, CE_ERR_ALIGNMENT, CE_ERR_ALIAS = -5, -6, -7, -8
+CE_ERR_SCRATCH = -9
+CE_NOALLOC_SCRATCH_BYTES = 229888
 CE_OP_FWD, CE_OP_FWD_BWD, CE_OP_SOFTMAX, CE_OP_LOG_SOFTMAX, CE_OP_BWD = 0, 1, 2, 3, 4
 REDUCTIONS = {"none": CE_NONE, "mean": CE_MEAN, "sum": CE_SUM}
 
@@ -56,6 +59,8 @@ def load_library(path=None):
         lib.ce_workspace_bytes.restype = sz
         lib.ce_fwd.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, sz, vp]
         lib.ce_fwd.restype = i32
+        lib.ce_fwd_noalloc.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp]
+        lib.ce_fwd_noalloc.restype = i32
         lib.ce_fwd_bwd_inplace.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, sz, vp]
         lib.ce_fwd_bwd_inplace.restype = i32
         lib.ce_fwd_lse.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, vp, sz, vp]
@@ -230,6 +235,28 @@ def ce_fwd(logits, targets, reduction="mean", out=None, workspace=None):
     return _call("ce_fwd", logits, targets, reduction, out, workspace)
 
 
+def ce_fwd_noalloc(logits, targets, reduction="mean", out=None):
+    """ce_fwd with the library's static per-device scratch in place of a
+    workspace: the C call allocates no device memory (pass out to allocate
+    nothing here either).  Calls that overlap on one GPU race on the scratch."""
+    import torch
+    lib = load_library()
+    _check(logits, targets)
+    red = REDUCTIONS[reduction]
+    M, V = logits.shape
+    dev = logits.device
+    if out is None:
+        out = torch.empty((M,) if red == CE_NONE else (), dtype=torch.float32, device=dev)
+    else:
+        _check_rows(out, M if red == CE_NONE else 1, dev, "out")
+    rc = _invoke(lib.ce_fwd_noalloc, dev,
+                 [logits.data_ptr(), targets.data_ptr(), M, V, _dtype_code(logits), red,
+                  out.data_ptr() if out.numel() else None, _stream_handle(dev)])
+    if rc:
+        raise CEError(rc, "ce_fwd_noalloc")
+    return out
+
+
 def ce_fwd_bwd_inplace(logits, targets, reduction="mean", out=None, workspace=None):
     """Loss as ce_fwd, and logits overwritten with d(loss)/d(logits)."""
     return _call("ce_fwd_bwd_inplace", logits, targets, reduction, out, workspace)
@@ -359,7 +386,7 @@ def ce_linear_fwd_bwd(hidden, weight, targets, reduction="mean", chunk=0, worksp
                    True)
 
 
-__all__ = ["ce_fwd", "ce_fwd_lse", "ce_fwd_bwd_inplace", "ce_bwd", "ce_softmax",
+__all__ = ["ce_fwd", "ce_fwd_noalloc", "ce_fwd_lse", "ce_fwd_bwd_inplace", "ce_bwd", "ce_softmax",
            "ce_linear_fwd", "ce_linear_fwd_bwd",
            "ce_workspace_bytes", "ce_status_string", "ce_plan_describe", "load_library",
            "CEError", "LIB_PATH"]

@@ -410,6 +410,7 @@ struct Call {
     void *ws = nullptr;
     size_t ws_bytes = 0;
     bool loss = true;              // computes losses (needs targets and out)
+    bool own_scratch = false;      // ws is the library's static scratch (ce_fwd_noalloc)
 };
 
 struct Region {
@@ -417,10 +418,13 @@ struct Region {
     size_t n;
 };
 
-// Slices per row this call uses: split rows need the workspace's scratch.
-int call_split(const Call &c, int *slice_vecs)
+// Slices per row the plan would split this call's rows into given room for
+// the split scratch (0: not split), and the workspace bytes that takes.
+int planned_split(const Call &c, int *slice_vecs, size_t *bytes)
 {
-    if (c.M < 1 || !c.ws)
+    const bool reduced = c.loss && c.reduction != CE_NONE;
+    *bytes = used_workspace(c.M, reduced, 0);
+    if (c.M < 1)
         return 0;
     const size_t s = elem_size(c.dtype);
     const int E = 16 / (int)s;
@@ -428,8 +432,23 @@ int call_split(const Call &c, int *slice_vecs)
     const bool aligned = head0 == 0 && c.V % E == 0;
     int sv = 0;
     const int S = split_slices(c.M, window_vectors(c.V, E, aligned), &sv);
-    const bool reduced = c.loss && c.reduction != CE_NONE;
-    if (S < 2 || c.ws_bytes < used_workspace(c.M, reduced, S))
+    if (S < 2)
+        return 0;
+    *bytes = used_workspace(c.M, reduced, S);
+    if (slice_vecs)
+        *slice_vecs = sv;
+    return S;
+}
+
+// Slices per row this call uses: split rows need the workspace's scratch.
+int call_split(const Call &c, int *slice_vecs)
+{
+    if (c.M < 1 || !c.ws)
+        return 0;
+    size_t need = 0;
+    int sv = 0;
+    const int S = planned_split(c, &sv, &need);
+    if (S < 2 || c.ws_bytes < need)
         return 0;
     if (slice_vecs)
         *slice_vecs = sv;
@@ -464,7 +483,8 @@ int check_args(const Call &c)
     // the output is written with the vectors the input is read with
     if (has_y && (uintptr_t)c.y % 16 != (uintptr_t)c.logits % 16)
         return CE_ERR_ALIGNMENT;
-    if (reduced) {
+    // (the library's own scratch is sized and placed by ce_fwd_noalloc)
+    if (reduced && !c.own_scratch) {
         if (!c.ws || c.ws_bytes < kPartialBytes || (uintptr_t)c.ws % 8)
             return CE_ERR_WORKSPACE;
     }
@@ -480,7 +500,8 @@ int check_args(const Call &c)
         {c.lse_out, per_row},
         {c.y == c.logits ? nullptr : c.y, has_y ? xb : 0},
         {c.y == c.logits ? c.y : nullptr, has_y ? xb : 0},
-        {c.ws, used_workspace(c.M, reduced, call_split(c, nullptr))},
+        // a static device symbol of the library cannot overlap the caller's buffers
+        {c.own_scratch ? nullptr : c.ws, used_workspace(c.M, reduced, call_split(c, nullptr))},
     };
     const Region ins[] = {
         {c.y == c.logits ? nullptr : c.logits, xb},
@@ -595,6 +616,45 @@ int run(const Call &c, void *stream)
     return CE_OK;
 }
 
+// ---- the library's own scratch (the entry point that allocates nothing) ----
+// Room for what a forward's kernels keep beyond their inputs and outputs under
+// the default plans: the fp64 partial sums of a mean or sum (at most
+// kMaxPartials slots, the launch plan's cap) and the split-row statistics of
+// up to kSplitMaxRows rows of kMaxSplit slices.  Nothing in it needs to start
+// at zero: every slot a call reads was written earlier in the same call.
+constexpr size_t kScratchBytes =
+    kPartialBytes + (size_t)kSplitMaxRows * (kMaxSplit * kSplitBytesPerSlice + 4);
+static_assert(kScratchBytes == CE_NOALLOC_SCRATCH_BYTES, "ce.h states the scratch size");
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+}  // namespace
+
+// One copy per GPU, held until the process ends.  In host code `scratch` only
+// names the symbol: kernels get the device address looked up below.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// The current device's address of `scratch`, looked up once per device (with
+// that device current) and kept.
+int scratch_address(void **ptr)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return CE_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return CE_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return CE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -630,6 +690,34 @@ int ce_fwd(const void *logits, const int64_t *targets, int64_t M, int64_t V, ce_
     c.out = out;
     c.ws = workspace;
     c.ws_bytes = workspace_bytes;
+    return run(c, stream);
+}
+
+int ce_fwd_noalloc(const void *logits, const int64_t *targets, int64_t M, int64_t V,
+                   ce_dtype_t dtype, ce_reduction_t reduction, float *out, void *stream)
+{
+    Call c;
+    c.logits = logits;
+    c.targets = targets;
+    c.M = M;
+    c.V = V;
+    c.dtype = (int)dtype;
+    c.reduction = (int)reduction;
+    c.out = out;
+    c.own_scratch = true;
+    int rc = check_args(c);
+    if (rc)
+        return rc;
+    size_t need = 0;
+    planned_split(c, nullptr, &need);
+    if (need > kScratchBytes)
+        return CE_ERR_SCRATCH;
+    if (need > 0) {
+        rc = scratch_address(&c.ws);
+        if (rc)
+            return rc;
+        c.ws_bytes = kScratchBytes;
+    }
     return run(c, stream);
 }
 
@@ -724,6 +812,9 @@ const char *ce_status_string(int status)
         return "a pointer not aligned to its element size, or an output not at the logits' "
                "address modulo 16";
     case CE_ERR_ALIAS: return "an output overlaps another output or an input";
+    case CE_ERR_SCRATCH:
+        return "the call needs more scratch than the library's static per-device scratch "
+               "holds (ce_fwd_noalloc)";
     default: return "unknown status";
     }
 }

@@ -216,6 +216,44 @@ def test_split_workspace_checks(lib):
                     grad=FAKE + big, ws=FAKE + 64, ws_bytes=n) == ce.CE_ERR_ALIAS
 
 
+def call_noalloc(lib, logits=FAKE, targets=FAKE, M=4, V=8, dtype=0, red=1, out=FAKE + 4096):
+    return lib.ce_fwd_noalloc(VP(logits) if logits else None, VP(targets) if targets else None,
+                              M, V, dtype, red, VP(out) if out else None, None)
+
+
+def test_noalloc_argument_errors(lib, monkeypatch):
+    import softmax_cross_entropy_fwd_amd as ce
+    assert call_noalloc(lib, dtype=3) == ce.CE_ERR_DTYPE
+    assert call_noalloc(lib, red=3) == ce.CE_ERR_REDUCTION
+    assert call_noalloc(lib, M=-1) == ce.CE_ERR_SHAPE
+    assert call_noalloc(lib, V=0) == ce.CE_ERR_SHAPE
+    assert call_noalloc(lib, logits=0) == ce.CE_ERR_NULL
+    assert call_noalloc(lib, targets=0) == ce.CE_ERR_NULL
+    assert call_noalloc(lib, out=0) == ce.CE_ERR_NULL
+    assert call_noalloc(lib, logits=FAKE + 1) == ce.CE_ERR_ALIGNMENT
+    assert call_noalloc(lib, out=FAKE + 16) == ce.CE_ERR_ALIAS       # inside the logits
+    # Beyond the scratch: 512 rows of 131072 bf16 split 16 ways (forced) would
+    # need 128 KiB + 512 * (16 * 12 + 4) bytes, more than it holds; refused
+    # before any HIP call.  Unforced, 512 rows are not split and need only the
+    # partial sums (such a call would run; it is not made here, without a GPU).
+    big = 1 << 40
+    monkeypatch.setenv("CE_FORCE_SPLIT", "64")
+    assert (128 << 10) + 512 * (16 * 12 + 4) > ce.CE_NOALLOC_SCRATCH_BYTES
+    assert call_noalloc(lib, logits=FAKE, targets=FAKE + big, M=512, V=1 << 17, dtype=2,
+                        out=FAKE + 2 * big) == ce.CE_ERR_SCRATCH
+    assert call_noalloc(lib, logits=FAKE, targets=FAKE + big, M=512, V=1 << 17, dtype=2, red=0,
+                        out=FAKE + 2 * big) == ce.CE_ERR_SCRATCH
+    assert "scratch" in ce.ce_status_string(ce.CE_ERR_SCRATCH)
+
+
+def test_noalloc_scratch_size_is_stated_in_the_header():
+    import re
+    import softmax_cross_entropy_fwd_amd as ce
+    text = open(HEADERS[0]).read()
+    m = re.search(r"#define CE_NOALLOC_SCRATCH_BYTES (\d+)", text)
+    assert m and int(m.group(1)) == ce.CE_NOALLOC_SCRATCH_BYTES == (128 << 10) + 128 * (64 * 12 + 4)
+
+
 def test_workspace_bytes(lib):
     assert lib.ce_workspace_bytes(100, 1000, 0, 0) == 0         # none
     mean = lib.ce_workspace_bytes(100, 1000, 0, 1)
@@ -229,11 +267,11 @@ def test_workspace_bytes(lib):
 def test_status_strings(lib):
     import softmax_cross_entropy_fwd_amd as ce
     seen = set()
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         s = lib.ce_status_string(code).decode()
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 9
+    assert len(seen) == 10
     assert lib.ce_status_string(-99).decode() == "unknown status"
     assert "overlaps" in ce.ce_status_string(ce.CE_ERR_ALIAS)
 
