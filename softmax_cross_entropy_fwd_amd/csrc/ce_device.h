@@ -716,6 +716,36 @@ __device__ __forceinline__ Window row_window(const Params &p, int64_t row)
     return w;
 }
 
+// The same sum over a row held in registers (lane lidx holds window vectors
+// lidx + STRIDE*k): the epilogues still hold the row when the sum is needed.
+// Window elements outside the row are masked again (the backward from a given
+// lse has not masked them).  Only the rare dominant-target rows take it.
+template <int DT, int K, int STRIDE, bool EXACT>
+__device__ __forceinline__ float regs_sum_without_target(const Params &p, const Vec (&raw)[K],
+                                                         const Window &w, int lidx, int kfull,
+                                                         float mL, int vt, int jt)
+{
+    constexpr int E = Traits<DT>::E;
+    const bool masked = !EXACT && !p.aligned;
+    float lx = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int v = lidx + STRIDE * k;
+        Vec x = raw[k];
+        if (masked) {
+            if (k == 0 && lidx == 0 && w.head > 0)
+                mask_outside<DT>(x, w.head, E);
+            if (k + 1 >= kfull && v >= w.nvec - 1)
+                mask_outside<DT>(x, 0, (int)(w.head + p.V - (int64_t)(w.nvec - 1) * E));
+        }
+        float e = vec_sumexp<DT>(x, mL);
+        if (v == vt)
+            e = vec_sumexp_skip<DT>(x, mL, jt);
+        lx += vec_valid<STRIDE, EXACT>(k, kfull, lidx, w.nvec) ? e : 0.0f;
+    }
+    return lx;
+}
+
 // The gradient scale of a row: 1/M (mean) or 1, times the upstream gradient
 // (per row for none, one value otherwise) when one is given.
 __device__ __forceinline__ float row_scale(const Params &p, int64_t row)
@@ -831,9 +861,18 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
     const float et = fast_exp2(__builtin_fmaf(xt, kLog2e, -mL));
     const bool accurate = tp.valid && et > 0.5f * s;
     float s_excl = s - et;
-    if (accurate)
-        s_excl = red.sum_excl(sum_without_target<DT>(p, w.xrow, lidx, STRIDE, w.nvec, w.head,
-                                                     mL, tp.vt, tp.jt));
+    if (accurate) {
+        // the epilogues still hold the row in registers; the forward has
+        // refilled them with the next row and reads this one again
+        if constexpr (BWD) {
+            opt_barrier<DT, K>(raw);   // widen again rather than keep the fold's copies
+            s_excl = red.sum_excl(regs_sum_without_target<DT, K, STRIDE, EXACT>(
+                p, raw, w, lidx, kfull, mL, tp.vt, tp.jt));
+        } else {
+            s_excl = red.sum_excl(sum_without_target<DT>(p, w.xrow, lidx, STRIDE, w.nvec, w.head,
+                                                         mL, tp.vt, tp.jt));
+        }
+    }
     const float c = cur.c;
     const RowResult rr = row_result(tp.valid, m, xt, et, s, s_excl, accurate, c);
     const float log2s = OP == EPI_LSE_GRAD ? 0.0f : __log2f(s);
