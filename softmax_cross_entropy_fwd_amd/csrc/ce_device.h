@@ -180,25 +180,31 @@ __device__ __forceinline__ void store_partial(Vec *p, const Vec &v, int lo, int 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Row data is read once and written once: loads and stores can carry the
-// non-temporal (streaming) hint.
-#ifndef CE_NT_LOAD
-#define CE_NT_LOAD 0
-#endif
-#ifndef CE_NT_STORE
-#define CE_NT_STORE 1
-#endif
-
+// non-temporal (streaming) hint.  Stores do for rows that start and end on
+// 16-byte boundaries (the outputs are not read again here); the rows of a
+// misaligned batch share their boundary cache lines with their neighbours,
+// and there plain stores, which let the cache merge the two rows' halves of a
+// line, measured faster (stress rows' fused backward: 354 -> 335 us).  Loads
+// do where nothing reads the row again and every load
+// instruction of a wavefront covers whole 128-byte lines (NT): the forwards
+// of rows of at least 8 lanes (measured on MI355X: 5-8 % faster for the
+// classifier, LM-head and stress forwards).  The hint lets the line go
+// early, so it is not used where the next load of the same line follows
+// (rows of fewer than 8 lanes: 24 % slower for the skinny rows) or where the
+// row is read again or written back in place (the epilogues: 6 % slower for
+// the stress rows' fused backward).
+template <bool NT = false>
 __device__ __forceinline__ Vec ldv(const Vec *p)
 {
-#if CE_NT_LOAD
-    Vec v;
+    if constexpr (NT) {
+        Vec v;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        v.w[i] = __builtin_nontemporal_load(&p->w[i]);
-    return v;
-#else
-    return *p;
-#endif
+        for (int i = 0; i < 4; ++i)
+            v.w[i] = __builtin_nontemporal_load(&p->w[i]);
+        return v;
+    } else {
+        return *p;
+    }
 }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -206,14 +212,27 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // One 16-byte store.  Issued as a single vector store, so that the compiler
 // cannot merge its words with the element-wise stores of a row's boundary
 // vector (fp32 epilogues were split into 4- and 8-byte stores that way).
+template <bool NT = true>
 __device__ __forceinline__ void stv(Vec *p, const Vec &v)
 {
-#if CE_NT_STORE
     const u32x4_t x = {v.w[0], v.w[1], v.w[2], v.w[3]};
-    __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t *>(p));
-#else
-    *p = v;
-#endif
+    if constexpr (NT)
+        __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t *>(p));
+    else
+        *reinterpret_cast<u32x4_t *>(p) = x;
+}
+
+// A row's target read through the constant address space: the kernels never
+// write the targets, and a uniform address then becomes a scalar load.  A
+// vector load retires behind every row load already in flight, and the fused
+// epilogues move the uniform value to a scalar register at once, which made
+// them wait for all of them (vector loads complete in order).  (The given
+// log-sum-exps and upstream gradients stay vector loads: read this way they
+// measured 3-4 % slower in the backward from a given lse.)
+template <class T>
+__device__ __forceinline__ T row_scalar(const T *base, int64_t i)
+{
+    return ((const __attribute__((address_space(4))) T *)base)[i];
 }
 
 // ------------------------------------------------------- lane reductions
@@ -312,7 +331,7 @@ __device__ __forceinline__ void opt_barrier(Vec (&raw)[K])
 // lane's vector lies inside every row's window.  Elements of the window
 // outside the row become -inf; only the first and the last window vector (and
 // copies of the last) can hold such elements.
-template <int DT, int K, int STRIDE>
+template <int DT, int K, int STRIDE, bool NTL = false>
 __device__ __forceinline__ void load_window(Vec (&raw)[K], const Vec *xrow, int lidx, int nvec,
                                             int kfull, int head, int64_t V, bool aligned)
 {
@@ -320,7 +339,7 @@ __device__ __forceinline__ void load_window(Vec (&raw)[K], const Vec *xrow, int 
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int v = lidx + STRIDE * k;
-        raw[k] = ldv(&xrow[v < nvec ? v : nvec - 1]);
+        raw[k] = ldv<NTL>(&xrow[v < nvec ? v : nvec - 1]);
     }
     if (!aligned) {
         if (lidx == 0 && head > 0)
@@ -525,7 +544,7 @@ __device__ __forceinline__ void store_grad(Vec *xrow, int v, const Vec &g, int h
     const int64_t lo = head - (int64_t)v * E;
     const int64_t hi = lo + V;
     if (lo <= 0 && hi >= E)
-        stv(&xrow[v], g);
+        stv<false>(&xrow[v], g);   // misaligned rows: plain stores (see stv)
     else
         store_partial<DT>(xrow + v, g, (int)(lo > 0 ? lo : 0), (int)(hi < E ? hi : E));
 }
@@ -540,13 +559,20 @@ __device__ __forceinline__ float rescale_to(float s, float m, float M)
     return m == M ? s : s * fast_exp2((m - M) * kLog2e);
 }
 
-// G lanes of one wavefront per row.
+// G lanes of one wavefront per row.  share_xt: the target logit held by lane
+// `owner_lane` of a row that spans the wavefront (G == 64 only).
 template <int G>
 struct GroupRed {
     __device__ __forceinline__ void combine(float m, float s, float &M, float &S)
     {
         M = group_reduce<G>(m, OpMax());
         S = group_reduce<G>(rescale_to(s, m, M), OpSum());
+    }
+    __device__ __forceinline__ float share_xt(float xt_own, int owner_lane)
+    {
+        static_assert(G == 64, "only a row spanning the wavefront has a uniform owner");
+        return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xt_own),
+                                                        __builtin_amdgcn_readfirstlane(owner_lane)));
     }
     __device__ __forceinline__ float sum_excl(float v) { return group_reduce<G>(v, OpSum()); }
     __device__ __forceinline__ void next_row() {}
@@ -561,8 +587,12 @@ struct WgRed {
     float (*smax)[W];
     float (*ssum)[W];
     float (*sexc)[W];
+    float *sxt;      // [2]: the target logit, written by its owner thread
     int wave, lane, bank;
-    __device__ __forceinline__ void combine(float m, float s, float &M, float &S)
+    // owner: this thread holds the row's target logit xt_own; it is published
+    // before the combine's barrier and read by everyone after it
+    __device__ __forceinline__ void combine(float m, float s, float &M, float &S, float xt_own = 0.0f,
+                                            bool owner = false)
     {
         const float mw = group_reduce<64>(m, OpMax());
         const float sw = group_reduce<64>(rescale_to(s, m, mw), OpSum());
@@ -570,6 +600,8 @@ struct WgRed {
             smax[bank][wave] = mw;
             ssum[bank][wave] = sw;
         }
+        if (owner)
+            sxt[bank] = xt_own;
         __syncthreads();
         M = smax[bank][0];
 #pragma unroll
@@ -580,6 +612,7 @@ struct WgRed {
         for (int w = 0; w < W; ++w)
             S += rescale_to(ssum[bank][w], smax[bank][w], M);
     }
+    __device__ __forceinline__ float xt() const { return sxt[bank]; }
     __device__ __forceinline__ float sum_excl(float v)
     {
         v = group_reduce<64>(v, OpSum());
@@ -616,14 +649,26 @@ __device__ __forceinline__ float load_logit(const Params &p, int64_t row, int64_
 // every row's window is exactly STRIDE*K vectors (aligned rows), so no index
 // is clamped.  Otherwise a lane past the window re-reads the window's last
 // vector (a cache hit) and the sums drop that copy (vec_valid).
-template <int DT, int K, int STRIDE, bool EXACT>
+// (The compiler may reorder these loads against the loop's refill order; its
+// merged wait at the loop head then covers most of the row before the first
+// vector is folded.  Kept in program order, the waits came per vector and the
+// classifier forward ran 2-3 % slower, so the order is left to the compiler.)
+template <int DT, int K, int STRIDE, bool EXACT, bool NTL = false>
 __device__ __forceinline__ void issue_loads(Vec (&raw)[K], const Vec *xrow, int lidx, int nvec)
 {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int v = lidx + STRIDE * k;
-        raw[k] = ldv(&xrow[(EXACT || v < nvec) ? v : nvec - 1]);
+        raw[k] = ldv<NTL>(&xrow[(EXACT || v < nvec) ? v : nvec - 1]);
     }
+}
+
+// The forward's loads in a register-resident kernel whose row groups span
+// STRIDE lanes (see ldv).
+template <int OP, int STRIDE>
+constexpr bool nt_fwd_loads()
+{
+    return OP == EPI_NONE && STRIDE >= 8;
 }
 
 // -inf over the window elements outside the row (unaligned rows only): only
@@ -782,8 +827,53 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
     constexpr bool BWD = OP != EPI_NONE;
     const Window &w = cur.w;
     const TargetPos tp = target_pos<DT>(cur.t, p.V, w.head);
-    const float xt = tp.valid ? load_logit<DT>(p, cur.row, cur.t) : __builtin_nanf("");
     const bool masked = !EXACT && !p.aligned;
+    // The target's logit.  Lane vt mod STRIDE of the row holds it in vector
+    // k = vt / STRIDE.  In the epilogues of rows that span a whole wavefront
+    // or workgroup (STRIDE >= 64) that k is the same for every lane: once the
+    // fold is done, the owner takes the logit from its registers (which
+    // still hold the row) and shares it (readlane, or the LDS slot of the
+    // cross-wave combine).  A load from memory there made every lane wait for
+    // all the row's loads before its fold could start: the value is uniform,
+    // and moving it to a scalar register waited for the load, which completes
+    // after every load issued before it.  The forward (its registers already
+    // hold the next row), the backward from a given lse (it has no fold: its
+    // epilogue starts as the row's vectors arrive, and taking the logit from
+    // the registers first made it wait for the whole row, 17 % slower on the
+    // classifier rows) and narrower rows read it from memory.
+    constexpr bool XT_REGS = BWD && OP != EPI_LSE_GRAD && STRIDE >= 64;
+    const int kt_own = tp.valid ? tp.vt / STRIDE : -1;
+    const bool xt_owner = tp.valid && lidx == tp.vt % STRIDE;
+    const int owner_lane = tp.valid ? tp.vt % STRIDE : 0;
+    float xt_own = 0.0f;
+    float xt = __builtin_nanf("");
+    if constexpr (!XT_REGS)
+        xt = tp.valid ? load_logit<DT>(p, cur.row, cur.t) : __builtin_nanf("");
+    auto take_xt = [&]() {
+        if constexpr (XT_REGS) {
+            // straight-line selects (kt_own is uniform): branches here made
+            // the compiler spill the row's registers
+            Vec tv = raw[0];
+#pragma unroll
+            for (int k = 1; k < K; ++k) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    tv.w[i] = k == kt_own ? raw[k].w[i] : tv.w[i];
+            }
+            xt_own = vec_elem_dyn<DT>(tv, tp.jt);
+        }
+    };
+    // after the combine (which, across wavefronts, also carried the logit)
+    auto shared_xt = [&]() {
+        if constexpr (XT_REGS) {
+            float sh;
+            if constexpr (STRIDE > 64)
+                sh = red.xt();
+            else
+                sh = red.share_xt(xt_own, owner_lane);
+            xt = tp.valid ? sh : __builtin_nanf("");
+        }
+    };
 
     float m, s;
     if constexpr (OP == EPI_LSE_GRAD) {
@@ -819,7 +909,12 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
             const float e = vec_sumexp<DT>(raw[k], mlL);
             sl += vec_valid<STRIDE, EXACT>(k, kfull, lidx, w.nvec) ? e : 0.0f;
         }
-        red.combine(ml, sl, m, s);
+        take_xt();
+        if constexpr (STRIDE > 64)
+            red.combine(ml, sl, m, s, xt_own, xt_owner);
+        else
+            red.combine(ml, sl, m, s);
+        shared_xt();
     } else {
         // One pass: each vector is folded into the lane's running (max, sum)
         // as it arrives -- the sum is rescaled by 2^((m_old - m_new) log2 e)
@@ -849,12 +944,18 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
             s_run = valid ? s_new : s_run;
             m_run = valid ? mn : m_run;
             if constexpr (!BWD) {
-                raw[k] = ldv(&next.w.xrow[(EXACT || v < next.w.nvec) ? v : next.w.nvec - 1]);
+                raw[k] = ldv<nt_fwd_loads<OP, STRIDE>()>(
+                    &next.w.xrow[(EXACT || v < next.w.nvec) ? v : next.w.nvec - 1]);
                 // keep each load after the use of the register it refills
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        red.combine(m_run, s_run, m, s);
+        take_xt();
+        if constexpr (STRIDE > 64)
+            red.combine(m_run, s_run, m, s, xt_own, xt_owner);
+        else
+            red.combine(m_run, s_run, m, s);
+        shared_xt();
     }
     const float mL = m * kLog2e;
 
@@ -952,7 +1053,7 @@ __device__ __forceinline__ RowRef row_ref(const Params &p, int64_t row)
     // The per-row scalars are read here, a step before they are used and
     // before the row's own loads: vector loads retire in order, so a late
     // load would make the wave wait for every prefetch issued before it.
-    r.t = (r.active && p.targets) ? p.targets[r.row] : -1;
+    r.t = (r.active && p.targets) ? row_scalar(p.targets, r.row) : -1;
     r.c = (OP == EPI_GRAD || OP == EPI_LSE_GRAD) ? row_scale(p, r.row) : 0.0f;
     r.lse = OP == EPI_LSE_GRAD ? p.lse_in[r.row] : 0.0f;
     r.w = row_window<DT>(p, r.row);
@@ -1009,7 +1110,7 @@ __global__ void __launch_bounds__(NW * 64) rows_kernel(Params p)
     if (rb < row_end) {
         RowRef a = row_ref<DT, OP>(p, rb + lane / G);
         Vec ra[K];
-        issue_loads<DT, K, G, EXACT>(ra, a.w.xrow, lig, a.w.nvec);
+        issue_loads<DT, K, G, EXACT, nt_fwd_loads<OP, G>()>(ra, a.w.xrow, lig, a.w.nvec);
         if constexpr (NBUF == 1) {
             for (; rb < row_end; rb += row_step) {
                 const RowRef an = ref_at(rb + row_step, a);
@@ -1019,7 +1120,7 @@ __global__ void __launch_bounds__(NW * 64) rows_kernel(Params p)
         } else {
             RowRef b = ref_at(rb + row_step, a);
             Vec rbuf[K];
-            issue_loads<DT, K, G, EXACT>(rbuf, b.w.xrow, lig, b.w.nvec);
+            issue_loads<DT, K, G, EXACT, nt_fwd_loads<OP, G>()>(rbuf, b.w.xrow, lig, b.w.nvec);
             for (; rb < row_end; rb += 2 * row_step) {
                 const RowRef an = ref_at(rb + 2 * row_step, a);
                 record(a, pipeline_step<DT, K, G, OP, EXACT>(p, red, ra, a, an, lig, kfull));
@@ -1050,11 +1151,12 @@ wg_kernel(Params p)
 {
     constexpr int E = Traits<DT>::E;
     constexpr int NT = W * 64;
-    __shared__ float s_max[2][W], s_sum[2][W], s_exc[2][W];
+    __shared__ float s_max[2][W], s_sum[2][W], s_exc[2][W], s_xt[2];
     WgRed<W> red;
     red.smax = s_max;
     red.ssum = s_sum;
     red.sexc = s_exc;
+    red.sxt = s_xt;
     red.wave = threadIdx.x >> 6;
     red.lane = threadIdx.x & 63;
     red.bank = 0;
@@ -1076,7 +1178,8 @@ wg_kernel(Params p)
     if (row < row_end) {
         RowRef cur = row_ref<DT, OP>(p, row);
         Vec raw[K];
-        issue_loads<DT, K, NT, EXACT>(raw, cur.w.xrow, threadIdx.x, cur.w.nvec);
+        issue_loads<DT, K, NT, EXACT, nt_fwd_loads<OP, NT>()>(raw, cur.w.xrow, threadIdx.x,
+                                                              cur.w.nvec);
         for (; row < row_end; row += row_step) {
             const bool has_next = row + row_step < row_end;
             const RowRef next = has_next ? row_ref<DT, OP>(p, row + row_step) : cur;
@@ -1117,7 +1220,7 @@ __global__ void __launch_bounds__(256) wstream_kernel(Params p)
 
     for (int64_t row = (int64_t)blockIdx.x * nwaves + wave; row < p.M; row += step) {
         const Window w = row_window<DT>(p, row);
-        const int64_t t = p.targets ? p.targets[row] : -1;
+        const int64_t t = p.targets ? row_scalar(p.targets, row) : -1;
         const TargetPos tp = target_pos<DT>(t, p.V, w.head);
         const float xt = tp.valid ? load_logit<DT>(p, row, t) : __builtin_nanf("");
         float m_run = -__builtin_inff();
@@ -1129,7 +1232,7 @@ __global__ void __launch_bounds__(256) wstream_kernel(Params p)
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const int v = lane + 64 * k;
-                raw[k] = ldv(&xc[v < n ? v : n - 1]);
+                raw[k] = ldv<true>(&xc[v < n ? v : n - 1]);
             }
 #pragma unroll
             for (int k = 0; k < K; ++k) {
@@ -1194,7 +1297,7 @@ __global__ void __launch_bounds__(W * 64) stream_kernel(Params p)
 
     for (int64_t row = blockIdx.x; row < p.M; row += gridDim.x) {
         const Window w = row_window<DT>(p, row);
-        const int64_t t = p.targets ? p.targets[row] : -1;
+        const int64_t t = p.targets ? row_scalar(p.targets, row) : -1;
         const TargetPos tp = target_pos<DT>(t, p.V, w.head);
 
         float m, s, xt;
@@ -1217,10 +1320,10 @@ __global__ void __launch_bounds__(W * 64) stream_kernel(Params p)
                 const int kfull = (w.nvec - cb) >= CH ? K : (w.nvec - cb) / NT;
                 // the chunk is a window of its own: the row's head lies in chunk 0,
                 // and its end is at element head + V - cb*E of the chunk
-                load_window<DT, K, NT>(raw, w.xrow + cb, tid, w.nvec - cb, kfull,
-                                       cb == 0 ? w.head : 0,
-                                       cb == 0 ? p.V : p.V + w.head - (int64_t)cb * E,
-                                       p.aligned != 0);
+                load_window<DT, K, NT, !BWD>(raw, w.xrow + cb, tid, w.nvec - cb, kfull,
+                                             cb == 0 ? w.head : 0,
+                                             cb == 0 ? p.V : p.V + w.head - (int64_t)cb * E,
+                                             p.aligned != 0);
                 // the lane holding the target keeps its logit aside and drops it
                 // from the vector: it enters the max below, not the sum
                 float tval = -__builtin_inff();
@@ -1374,7 +1477,7 @@ __global__ void __launch_bounds__(W * 64) split_stats_kernel(Params p)
     const int64_t row = blockIdx.x / p.S;
     const int slice = blockIdx.x % p.S;
     const Window w = row_window<DT>(p, row);
-    const int64_t t = p.targets ? p.targets[row] : -1;
+    const int64_t t = p.targets ? row_scalar(p.targets, row) : -1;
     const TargetPos tp = target_pos<DT>(t, p.V, w.head);
     const int v0 = slice * p.slice_vecs;
     const int v1 = v0 + p.slice_vecs < w.nvec ? v0 + p.slice_vecs : w.nvec;
@@ -1465,7 +1568,7 @@ __global__ void __launch_bounds__(W * 64) split_epi_kernel(Params p)
     const int64_t row = OP == EPI_NONE ? (int64_t)blockIdx.x : (int64_t)(blockIdx.x / p.S);
     const int slice = OP == EPI_NONE ? 0 : (int)(blockIdx.x % p.S);
     const Window w = row_window<DT>(p, row);
-    const int64_t t = p.targets ? p.targets[row] : -1;
+    const int64_t t = p.targets ? row_scalar(p.targets, row) : -1;
     const TargetPos tp = target_pos<DT>(t, p.V, w.head);
     const float c = (EOP == EPI_GRAD) ? row_scale(p, row) : 0.0f;
     const int v0 = slice * p.slice_vecs;
@@ -1590,7 +1693,7 @@ __global__ void __launch_bounds__(256) split_fix_kernel(Params p)
     const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (row >= p.M)
         return;
-    const int64_t t = p.targets[row];
+    const int64_t t = row_scalar(p.targets, row);
     const Window w = row_window<DT>(p, row);
     const TargetPos tp = target_pos<DT>(t, p.V, w.head);
     if (!tp.valid)
