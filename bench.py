@@ -660,7 +660,6 @@ def linear_main(ce, args, log):
         "roofline": {"bound": "mfma", "achieved": round(r["alg_TFLOPs"], 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(r["frac_of_peak"], 4), "traffic": None},
-        "counter_GBps": head.get("counter_GBps"),
         "cpu_baseline": cpu,
         "env": host_env(),
         "also": [{k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()}],
@@ -816,7 +815,6 @@ def main():
             ceilings, frac_of_read=round(head["alg_GBps"] / ceilings["read_GBps"], 4),
             frac_of_read_at_size=(None if not ceilings.get("read_at_size_GBps") else
                                   round(head["alg_GBps"] / ceilings["read_at_size_GBps"], 4))),
-        "counter_GBps": head.get("counter_GBps"),
         "cpu_baseline": cpu,
         "env": host_env(),
         "also": [{k: (round(v, 5) if isinstance(v, float) else v) for k, v in a.items()}

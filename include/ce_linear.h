@@ -5,28 +5,38 @@
  *     z = H W^T,   H [M, D] hidden states, W [V, D] weight (bf16),
  * fed to the row-wise softmax cross-entropy of ce.h (loss_i = lse(z_i) -
  * z[i, t_i], reduced by none, mean or sum), without ever holding the whole
- * [M, V] logits: the vocabulary is taken in chunks of C columns, each chunk's
- * logits are formed by a GEMM (bf16 inputs, fp32 accumulation and fp32
- * output) and folded into per-row statistics before the next chunk
- * overwrites them.  This is the fused linear + cross-entropy of "9 Triton
+ * [M, V] logits.  This is the fused linear + cross-entropy of "9 Triton
  * kernels in 9 weeks", week 8 (the lm_head projection chunked into the loss
  * to cut activation memory).
  *
- * The backward recomputes each chunk's logits, writes their gradient
+ * Two ways to the logits, the same numerics (bf16 products, fp32
+ * accumulation, fp32 row arithmetic):
+ *   - the library's own matrix-core kernels (bf16 MFMA), when D % 8 == 0,
+ *     D <= 2^20 and H and W sit on 16-byte boundaries: the forward forms
+ *     256 x 256 tiles of z and folds each into per-row statistics (max and
+ *     sum of exp over each 128 vocabulary rows, the target left out) in the
+ *     same kernel, so no logits are written at all;
+ *   - otherwise (or with the environment variable CE_LINEAR_GEMM=library)
+ *     rocBLAS GEMMs over vocabulary chunks of C columns, each chunk's fp32
+ *     logits folded into per-row statistics before the next overwrites them.
+ * The backward takes the vocabulary in chunks of C columns, recomputes each
+ * chunk's logits, writes their gradient
  *     G = (softmax(z) - onehot(t)) * c     (c = 1/M for mean, 1 otherwise)
- * in bf16, and accumulates dH = G W and dW = G^T H (fp32 outputs) with two
- * more GEMMs per chunk.  The GEMMs run in rocBLAS (plain library GEMMs);
- * the per-row statistics, the combine and the gradient chunk run in this
- * library's kernels, with the same numerics as ce.h (fp32 row arithmetic,
- * the target left out of the sums so dominant targets keep their relative
- * accuracy, fp64 fixed-order mean / sum).
+ * in bf16 (the matrix-core kernel writes it transposed), and accumulates
+ * dH = G W and dW = G^T H (fp32 outputs) with two rocBLAS GEMMs per chunk.
+ * The per-row combine has the numerics of ce.h (the target left out of the
+ * sums so dominant targets keep their relative accuracy, fp64 fixed-order
+ * mean / sum).
  *
- * Memory: every pointer is device memory owned by the caller.  The library
- * creates one rocBLAS handle per device on first use (rocBLAS allocates its
- * own small workspace then) and keeps it until the process ends; everything
- * else lives in the caller's workspace.  Calls are asynchronous on `stream`
- * (a hipStream_t); argument errors return before any launch.  Calls that may
- * run concurrently need distinct workspaces.
+ * Memory: every pointer is device memory owned by the caller.  Where
+ * rocBLAS runs (the backward, the library forward) the library creates one
+ * rocBLAS handle per device and stream on first use (rocBLAS allocates its
+ * own small workspace then) and keeps it until the process ends; a handle
+ * serves one call at a time, so calls on different streams do not wait for
+ * each other on the host.  Everything else lives in the caller's workspace.
+ * Calls are asynchronous on `stream` (a hipStream_t); argument errors return
+ * before any launch.  Calls that may run concurrently need distinct
+ * workspaces.
  *
  * Layout: H row-major [M, D], W row-major [V, D] (the nn.Linear weight
  * layout), both bf16 and 2-byte aligned; targets int64 [M]; dH row-major
@@ -55,9 +65,11 @@ int64_t ce_linear_chunk(int64_t M, int64_t D, int64_t V, int64_t chunk);
 
 /*
  * Workspace bytes ce_linear_fwd / ce_linear_fwd_bwd need for these sizes and
- * chunk (0 = the default): the fp32 logits chunk and the bf16 gradient chunk
- * (M * C * 6 bytes) plus per-row statistics.  0 for invalid sizes.  Contents
- * need no initialization.
+ * chunk (0 = the default): the larger of the library path's fp32 logits and
+ * bf16 gradient chunks (M * C * 6 bytes) with its chunk statistics, and the
+ * matrix-core path's statistics (8 bytes per token and 128 vocabulary rows)
+ * with its transposed gradient chunk; then per-row buffers.  0 for invalid
+ * sizes.  Contents need no initialization.
  */
 size_t ce_linear_workspace_bytes(int64_t M, int64_t D, int64_t V, int64_t chunk);
 

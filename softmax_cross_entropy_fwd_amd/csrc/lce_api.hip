@@ -1,14 +1,19 @@
 // lce_api.hip -- the C ABI of linear + cross-entropy: argument checks, the
-// chunk loop, the library GEMMs (rocBLAS) and the launches of the row
-// kernels between them.
+// choice of the matrix-core path (lce_mfma.hip) or the library GEMMs
+// (rocBLAS) with the row kernels (lce_kernels.hip), the chunk loop and the
+// launches.
 #include <hip/hip_runtime.h>
 #include <rocblas/rocblas.h>
 
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <memory>
 #include <mutex>
-#include <unordered_map>
+#include <utility>
 
 #include "ce.h"
 #include "ce_device.h"
@@ -43,12 +48,23 @@ int64_t chunk_for(int64_t M, int64_t V, int64_t chunk)
     return C < vmax ? C : vmax;
 }
 
-// Workspace layout (offsets in bytes, each 256-aligned).
+constexpr int64_t kMfmaTile = 256;   // vocabulary rows and tokens per matrix-core tile
+
+// Statistics entries per row of the matrix-core forward: one per 128
+// vocabulary rows.
+int64_t mfma_halves(int64_t V) { return 2 * ((V + kMfmaTile - 1) / kMfmaTile); }
+int64_t mfma_ldg(int64_t M) { return (M + 7) / 8 * 8; }
+
+// Workspace layout (offsets in bytes, each 256-aligned).  The head holds
+// either path's buffers -- library GEMMs: the fp32 logits chunk L, the bf16
+// gradient chunk G and the chunk statistics; matrix-core kernels: the
+// per-128-rows statistics and the transposed gradient chunk GT -- and the
+// per-row buffers follow the larger of the two.
 struct Layout {
-    size_t L, G, stats, rowx, lse, gt, partials, total;
+    size_t L, G, stats, stats_m, GT, rowx, lse, gt, partials, total;
 };
 
-Layout layout(int64_t M, int64_t C, int64_t nch)
+Layout layout(int64_t M, int64_t V, int64_t C, int64_t nch)
 {
     Layout l;
     size_t o = 0;
@@ -58,6 +74,13 @@ Layout layout(int64_t M, int64_t C, int64_t nch)
     o += align256((size_t)M * C * 2);
     l.stats = o;
     o += align256((size_t)M * nch * 8);
+    size_t om = 0;
+    l.stats_m = om;
+    om += align256((size_t)M * mfma_halves(V) * 8);
+    l.GT = om;
+    om += align256((size_t)C * mfma_ldg(M) * 2);
+    if (om > o)
+        o = om;
     l.rowx = o;
     o += align256((size_t)M * 4);
     l.lse = o;
@@ -78,8 +101,48 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb)
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-std::mutex g_mu;
-std::unordered_map<int, rocblas_handle> g_handles;
+// rocBLAS handles, one per (device, stream): a handle stays bound to its
+// stream and serves one call at a time (its own mutex, held while that call
+// enqueues its GEMMs), so calls on different streams never wait for each
+// other on the host.  Created on first use, kept until the process ends.
+struct Blas {
+    rocblas_handle h = nullptr;
+    std::mutex mu;
+};
+std::mutex g_map_mu;   // guards g_blas and g_cus
+std::map<std::pair<int, hipStream_t>, std::unique_ptr<Blas>> g_blas;
+std::map<int, int> g_cus;
+
+Blas *blas_for(int dev, hipStream_t st)
+{
+    std::lock_guard<std::mutex> lk(g_map_mu);
+    std::unique_ptr<Blas> &slot = g_blas[{dev, st}];
+    if (!slot) {
+        std::unique_ptr<Blas> b(new Blas);
+        if (rocblas_create_handle(&b->h) != rocblas_status_success)
+            return nullptr;
+        if (rocblas_set_stream(b->h, st) != rocblas_status_success) {
+            rocblas_destroy_handle(b->h);
+            return nullptr;
+        }
+        slot = std::move(b);
+    }
+    return slot.get();
+}
+
+// The device's compute units (the persistent forward's grid), 0 on error.
+int cu_count(int dev)
+{
+    std::lock_guard<std::mutex> lk(g_map_mu);
+    auto it = g_cus.find(dev);
+    if (it != g_cus.end())
+        return it->second;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    g_cus[dev] = n;
+    return n;
+}
 
 // C[m x n] (row-major, ldc) = op(A) op(B) + beta C with bf16 A, B and fp32
 // C, through rocBLAS's column-major interface (C^T = op(B)^T op(A)^T).
@@ -110,7 +173,7 @@ int run(const void *H, const void *W, const int64_t *targets, int64_t M, int64_t
         return CE_ERR_SHAPE;
     const int64_t C = chunk_for(M, V, chunk);
     const int64_t nch = (V + C - 1) / C;
-    const Layout lay = layout(M, C, nch);
+    const Layout lay = layout(M, V, C, nch);
     hipStream_t st = (hipStream_t)stream;
     const bool reduced = reduction != CE_NONE;
     if (M == 0) {
@@ -163,18 +226,26 @@ int run(const void *H, const void *W, const int64_t *targets, int64_t M, int64_t
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return CE_ERR_HIP;
-    std::lock_guard<std::mutex> lk(g_mu);   // the handle serves one call at a time
-    rocblas_handle h;
-    auto it = g_handles.find(dev);
-    if (it == g_handles.end()) {
-        if (rocblas_create_handle(&h) != rocblas_status_success)
+
+    // The logits on this library's matrix-core kernels when the rows are
+    // 16-byte vectors (D % 8 == 0, H and W on 16-byte boundaries) and a
+    // 256-row tile's bytes fit the kernels' 32-bit buffer offsets (D <=
+    // 2^20); else, or with CE_LINEAR_GEMM=library (comparisons), rocBLAS.
+    const char *gsel = std::getenv("CE_LINEAR_GEMM");
+    const int64_t tiles = ((V + kMfmaTile - 1) / kMfmaTile) * ((M + kMfmaTile - 1) / kMfmaTile);
+    const bool mfma = D % 8 == 0 && D <= (int64_t(1) << 20) && (uintptr_t)H % 16 == 0 &&
+                      (uintptr_t)W % 16 == 0 && tiles <= INT_MAX &&
+                      !(gsel && !std::strcmp(gsel, "library"));
+    // rocBLAS serves the library forward and the backward's dH and dW
+    rocblas_handle h = nullptr;
+    std::unique_lock<std::mutex> blas_lock;
+    if (!mfma || bwd) {
+        Blas *b = blas_for(dev, st);
+        if (!b)
             return CE_ERR_HIP;
-        g_handles[dev] = h;
-    } else {
-        h = it->second;
+        blas_lock = std::unique_lock<std::mutex>(b->mu);
+        h = b->h;
     }
-    if (rocblas_set_stream(h, st) != rocblas_status_success)
-        return CE_ERR_HIP;
 
     char *base = (char *)ws;
     lce::LceParams q;
@@ -196,9 +267,42 @@ int run(const void *H, const void *W, const int64_t *targets, int64_t M, int64_t
     const unsigned row_grid = (unsigned)((M + 3) / 4);
     const int m = (int)M, d = (int)D;
     float *Lw = (float *)(base + lay.L);
-
-    // forward: each chunk's logits, then its statistics
-    for (int64_t ci = 0; ci < nch; ++ci) {
+    lce::MfmaParams mp{};
+    mp.H = (const uint16_t *)H;
+    mp.W = (const uint16_t *)W;
+    mp.targets = targets;
+    mp.M = M;
+    mp.D = D;
+    mp.V = V;
+    mp.ntiles_t = (int)((M + kMfmaTile - 1) / kMfmaTile);
+    mp.rowx = q.rowx;
+    mp.lse = q.lse;
+    mp.gt = q.gt;
+    mp.c = q.c;
+    mp.GT = (uint16_t *)(base + lay.GT);
+    mp.ldg = mfma_ldg(M);
+    if (mfma) {
+        // forward: every tile's statistics in one launch over all of V, a
+        // persistent workgroup per compute unit
+        const int cus = cu_count(dev);
+        if (cus < 1)
+            return CE_ERR_HIP;
+        mp.v0 = 0;
+        mp.vn = (int)V;
+        mp.ntiles_v = (int)((V + kMfmaTile - 1) / kMfmaTile);
+        mp.stats = (float *)(base + lay.stats_m);
+        mp.nhalf = (int)mfma_halves(V);
+        mp.half0 = 0;
+        q.stats = mp.stats;
+        q.nchunks = mp.nhalf;
+        const int64_t ntiles = (int64_t)mp.ntiles_v * mp.ntiles_t;
+        void *args[] = {&mp};
+        if (!launch(lce::mfma_stats_kernel_fn(), (unsigned)(ntiles < cus ? ntiles : cus), 256, args,
+                    st))
+            return CE_ERR_HIP;
+    }
+    // forward (library GEMMs): each chunk's logits, then its statistics
+    for (int64_t ci = 0; ci < (mfma ? 0 : nch); ++ci) {
         q.v0 = ci * C;
         q.vn = (int)(V - q.v0 < C ? V - q.v0 : C);
         q.chunk_index = (int)ci;
@@ -234,6 +338,24 @@ int run(const void *H, const void *W, const int64_t *targets, int64_t M, int64_t
         q.vn = (int)(V - q.v0 < C ? V - q.v0 : C);
         q.chunk_index = (int)ci;
         const void *Wc = (const char *)W + (size_t)q.v0 * D * 2;
+        if (mfma) {
+            // the chunk's gradient, transposed, from the matrix-core kernel
+            mp.v0 = q.v0;
+            mp.vn = q.vn;
+            mp.ntiles_v = (int)((q.vn + kMfmaTile - 1) / kMfmaTile);
+            void *args[] = {&mp};
+            if (!launch(lce::mfma_grad_kernel_fn(), (unsigned)(mp.ntiles_v * mp.ntiles_t), 256,
+                        args, st))
+                return CE_ERR_HIP;
+            const int ldg = (int)mp.ldg;
+            if (!gemm_rm(h, true, false, m, d, q.vn, mp.GT, ldg, Wc, d, ci == 0 ? 0.0f : 1.0f, dH,
+                         d))
+                return CE_ERR_HIP;
+            if (!gemm_rm(h, false, false, q.vn, d, m, mp.GT, ldg, H, d, 0.0f,
+                         dW + (size_t)q.v0 * D, d))
+                return CE_ERR_HIP;
+            continue;
+        }
         if (!gemm_rm(h, false, true, m, q.vn, d, H, d, Wc, d, 0.0f, Lw, (int)C))
             return CE_ERR_HIP;
         void *args[] = {&q};
@@ -264,7 +386,7 @@ size_t ce_linear_workspace_bytes(int64_t M, int64_t D, int64_t V, int64_t chunk)
     if (M < 0 || D < 1 || V < 1 || M > INT_MAX || D > INT_MAX || V > INT_MAX || chunk < 0)
         return 0;
     const int64_t C = chunk_for(M, V, chunk);
-    return layout(M, C, (V + C - 1) / C).total;
+    return layout(M, V, C, (V + C - 1) / C).total;
 }
 
 int ce_linear_fwd(const void *hidden, const void *weight, const int64_t *targets, int64_t M,

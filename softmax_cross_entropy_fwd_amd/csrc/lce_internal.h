@@ -28,6 +28,35 @@ struct LceParams {
     float c;                  // gradient scale
 };
 
+// The matrix-core path (lce_mfma.hip): tiles of z^T = W H^T, 256 vocabulary
+// rows x 256 tokens per 256-thread workgroup, grid ntiles_v * ntiles_t.
+// Needs D % 8 == 0 and H, W on 16-byte boundaries.
+struct MfmaParams {
+    const uint16_t *H;        // [M, D] bf16
+    const uint16_t *W;        // [V, D] bf16 (the launch covers rows v0 .. v0 + vn)
+    const int64_t *targets;   // [M]
+    int64_t M, D, V;
+    int64_t v0;
+    int vn;
+    int ntiles_v, ntiles_t;
+    // forward: per token, (max, sum) of each 128 vocabulary rows with the
+    // target left out, [M][nhalf][2], entries half0 + 2 tv + (0, 1); the
+    // target's logit in rowx
+    float *stats;
+    int nhalf;
+    int half0;
+    float *rowx;
+    // backward: the row statistics and the gradient chunk, transposed
+    const float *lse;         // [M]
+    const float *gt;          // [M] the target's gradient
+    float c;                  // gradient scale, > 0
+    uint16_t *GT;             // [vn][ldg] bf16
+    int64_t ldg;              // row stride of GT (elements), a multiple of 8, >= M
+};
+
+const void *mfma_stats_kernel_fn();   // MfmaParams, 256 threads
+const void *mfma_grad_kernel_fn();    // MfmaParams, 256 threads
+
 const void *stats_kernel_fn();    // one wavefront per row, 256 threads
 const void *finish_kernel_fn();   // one wavefront per row, 256 threads
 const void *grad_kernel_fn();     // one wavefront per row, 256 threads

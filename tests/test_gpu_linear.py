@@ -1,6 +1,7 @@
-"""GPU parity of linear + cross-entropy (logits hidden @ weight.T over
-vocabulary chunks, library GEMMs plus this library's row kernels) against the
-fp64 oracle.
+"""GPU parity of linear + cross-entropy (logits hidden @ weight.T: this
+library's matrix-core kernels when D % 8 == 0 and the operands sit on 16-byte
+boundaries, else library GEMMs over vocabulary chunks, with this library's row
+kernels) against the fp64 oracle.
 
 Tolerances, derived from the arithmetic: the GEMMs add exact bf16 products in
 fp32, so each logit is within g_D = D 2^-24 times the sum of its products'
@@ -123,6 +124,33 @@ def test_linear_ragged_and_larger(ce):
     run_case(ce, 61, 257, 50257, 4096, "mean", seed=3)
     run_case(ce, 5, 513, 20011, 0, "none", seed=4, sigma=6.0)
     run_case(ce, 1, 64, 300, 0, "sum", seed=5)
+
+
+def test_linear_matrix_core_mid_size(ce):
+    # the matrix-core path: a mid size (M, D and V several tiles and K steps)
+    run_case(ce, 256, 1024, 32768, 0, "mean", seed=21)
+    run_case(ce, 256, 1024, 32768, 8192, "none", seed=22, bwd=False)
+
+
+def test_linear_matrix_core_ragged_tiles(ce):
+    # tokens and vocabulary rows past a 256 tile, D past a K step of 64, a
+    # single K chunk, tiles fewer than the XCDs
+    run_case(ce, 300, 200, 5003, 1024, "none", seed=23)
+    run_case(ce, 257, 8, 257, 0, "sum", seed=24)
+    run_case(ce, 3, 72, 77, 0, "mean", seed=25)
+
+
+def test_linear_both_gemm_paths(ce, monkeypatch):
+    # the same inputs through the matrix-core kernels and the library GEMMs:
+    # both within the oracle bounds, and within twice them of each other
+    h, w, t = inputs.make_linear(96, 512, 9000, 2.0, 26)
+    a = run_case(ce, 96, 512, 9000, 2048, "none", 0, h=h, w=w, t=t)
+    monkeypatch.setenv("CE_LINEAR_GEMM", "library")
+    b = run_case(ce, 96, 512, 9000, 2048, "none", 0, h=h, w=w, t=t)
+    monkeypatch.delenv("CE_LINEAR_GEMM")
+    e = logit_bounds(values(h), values(w))
+    bound = 2 * loss_bounds(b.cpu().numpy().astype(np.float64), 0.0, e)
+    assert np.all(np.abs(a.cpu().numpy() - b.cpu().numpy()) <= bound + 1e-6)
 
 
 def test_linear_dominant_and_out_of_range_targets(ce):
