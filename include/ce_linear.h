@@ -22,7 +22,7 @@
  * The backward takes the vocabulary in chunks of C columns, recomputes each
  * chunk's logits, writes their gradient
  *     G = (softmax(z) - onehot(t)) * c     (c = 1/M for mean, 1 otherwise)
- * in bf16 (the matrix-core kernel writes it transposed), and accumulates
+ * in bf16 ([M][C], from a matrix-core kernel or a row kernel), and accumulates
  * dH = G W and dW = G^T H (fp32 outputs) with two rocBLAS GEMMs per chunk.
  * The per-row combine has the numerics of ce.h (the target left out of the
  * sums so dominant targets keep their relative accuracy, fp64 fixed-order
@@ -68,7 +68,7 @@ int64_t ce_linear_chunk(int64_t M, int64_t D, int64_t V, int64_t chunk);
  * chunk (0 = the default): the larger of the library path's fp32 logits and
  * bf16 gradient chunks (M * C * 6 bytes) with its chunk statistics, and the
  * matrix-core path's statistics (8 bytes per token and 128 vocabulary rows)
- * with its transposed gradient chunk; then per-row buffers.  0 for invalid
+ * with its bf16 gradient chunk (M * C * 2 bytes); then per-row buffers.  0 for invalid
  * sizes.  Contents need no initialization.
  */
 size_t ce_linear_workspace_bytes(int64_t M, int64_t D, int64_t V, int64_t chunk);

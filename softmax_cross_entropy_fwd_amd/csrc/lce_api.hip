@@ -53,15 +53,14 @@ constexpr int64_t kMfmaTile = 256;   // vocabulary rows and tokens per matrix-co
 // Statistics entries per row of the matrix-core forward: one per 128
 // vocabulary rows.
 int64_t mfma_halves(int64_t V) { return 2 * ((V + kMfmaTile - 1) / kMfmaTile); }
-int64_t mfma_ldg(int64_t M) { return (M + 7) / 8 * 8; }
 
 // Workspace layout (offsets in bytes, each 256-aligned).  The head holds
 // either path's buffers -- library GEMMs: the fp32 logits chunk L, the bf16
-// gradient chunk G and the chunk statistics; matrix-core kernels: the
-// per-128-rows statistics and the transposed gradient chunk GT -- and the
+// gradient chunk G [M][C] and the chunk statistics; matrix-core kernels: the
+// per-128-rows statistics and the gradient chunk Gm [M][C] -- and the
 // per-row buffers follow the larger of the two.
 struct Layout {
-    size_t L, G, stats, stats_m, GT, rowx, lse, gt, partials, total;
+    size_t L, G, stats, stats_m, Gm, rowx, lse, gt, partials, total;
 };
 
 Layout layout(int64_t M, int64_t V, int64_t C, int64_t nch)
@@ -77,8 +76,8 @@ Layout layout(int64_t M, int64_t V, int64_t C, int64_t nch)
     size_t om = 0;
     l.stats_m = om;
     om += align256((size_t)M * mfma_halves(V) * 8);
-    l.GT = om;
-    om += align256((size_t)C * mfma_ldg(M) * 2);
+    l.Gm = om;
+    om += align256((size_t)M * C * 2);
     if (om > o)
         o = om;
     l.rowx = o;
@@ -279,8 +278,8 @@ int run(const void *H, const void *W, const int64_t *targets, int64_t M, int64_t
     mp.lse = q.lse;
     mp.gt = q.gt;
     mp.c = q.c;
-    mp.GT = (uint16_t *)(base + lay.GT);
-    mp.ldg = mfma_ldg(M);
+    mp.G = (uint16_t *)(base + lay.Gm);
+    mp.ldg = C;
     if (mfma) {
         // forward: every tile's statistics in one launch over all of V, a
         // persistent workgroup per compute unit
@@ -339,19 +338,23 @@ int run(const void *H, const void *W, const int64_t *targets, int64_t M, int64_t
         q.chunk_index = (int)ci;
         const void *Wc = (const char *)W + (size_t)q.v0 * D * 2;
         if (mfma) {
-            // the chunk's gradient, transposed, from the matrix-core kernel
+            // the chunk's gradient from the matrix-core kernel (persistent)
             mp.v0 = q.v0;
             mp.vn = q.vn;
             mp.ntiles_v = (int)((q.vn + kMfmaTile - 1) / kMfmaTile);
+            const int64_t ntiles = (int64_t)mp.ntiles_v * mp.ntiles_t;
+            const int cus = cu_count(dev);
+            if (cus < 1)
+                return CE_ERR_HIP;
             void *args[] = {&mp};
-            if (!launch(lce::mfma_grad_kernel_fn(), (unsigned)(mp.ntiles_v * mp.ntiles_t), 256,
+            if (!launch(lce::mfma_grad_kernel_fn(), (unsigned)(ntiles < cus ? ntiles : cus), 256,
                         args, st))
                 return CE_ERR_HIP;
-            const int ldg = (int)mp.ldg;
-            if (!gemm_rm(h, true, false, m, d, q.vn, mp.GT, ldg, Wc, d, ci == 0 ? 0.0f : 1.0f, dH,
+            const uint16_t *Gc = mp.G;
+            if (!gemm_rm(h, false, false, m, d, q.vn, Gc, (int)C, Wc, d, ci == 0 ? 0.0f : 1.0f, dH,
                          d))
                 return CE_ERR_HIP;
-            if (!gemm_rm(h, false, false, q.vn, d, m, mp.GT, ldg, H, d, 0.0f,
+            if (!gemm_rm(h, true, false, q.vn, d, m, Gc, (int)C, H, d, 0.0f,
                          dW + (size_t)q.v0 * D, d))
                 return CE_ERR_HIP;
             continue;

@@ -29,7 +29,9 @@ struct LceParams {
 };
 
 // The matrix-core path (lce_mfma.hip): tiles of z^T = W H^T, 256 vocabulary
-// rows x 256 tokens per 256-thread workgroup, grid ntiles_v * ntiles_t.
+// rows x 256 tokens per 256-thread workgroup; a persistent grid (any size,
+// a multiple of 8 keeps each workgroup's tiles on its XCD's L2) walks the
+// ntiles_v * ntiles_t tiles.
 // Needs D % 8 == 0 and H, W on 16-byte boundaries.
 struct MfmaParams {
     const uint16_t *H;        // [M, D] bf16
@@ -46,12 +48,12 @@ struct MfmaParams {
     int nhalf;
     int half0;
     float *rowx;
-    // backward: the row statistics and the gradient chunk, transposed
+    // backward: the row statistics and the gradient chunk
     const float *lse;         // [M]
     const float *gt;          // [M] the target's gradient
     float c;                  // gradient scale, > 0
-    uint16_t *GT;             // [vn][ldg] bf16
-    int64_t ldg;              // row stride of GT (elements), a multiple of 8, >= M
+    uint16_t *G;              // [M][ldg] bf16, columns 0 .. vn
+    int64_t ldg;              // row stride of G (elements), a multiple of 8, >= vn
 };
 
 const void *mfma_stats_kernel_fn();   // MfmaParams, 256 threads

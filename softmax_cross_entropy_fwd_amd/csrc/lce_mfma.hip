@@ -14,21 +14,22 @@
 //                 gradient.
 //   grad_kernel   the backward: the gradient g = exp(z - lse) c (the target
 //                 taking the gradient the combine computed), rounded to bf16
-//                 and written transposed, G^T [vocabulary rows][tokens], for
-//                 the dH and dW products.
+//                 and written as G [tokens][vocabulary rows of the chunk],
+//                 for the dH and dW products.
 //
 // Data path: A = W rows (vocabulary), B = H rows (tokens), both K-major (the
-// nn.Linear layout).  K runs in steps of 64: buffer loads bring the two
-// 256 x 64 tiles of step k + 2 into registers (16 bytes per thread and load,
-// whole 128-byte rows per 8 threads) while step k is multiplied, and they
-// are stored into the free one of two LDS buffers (rows of 128 bytes, the
-// 16-byte chunks XOR-swizzled by the row index so that the rows an MFMA
-// operand read serves together spread over the banks) during step k + 1; one
-// barrier per step.  Four wavefronts, one per SIMD, each own 128 x 128 of
-// the tile: 4 x 4 blocks of 32 x 32, 256 accumulator registers per lane.
-// With no second wavefront on the SIMD to hide latency, every LDS read and
-// write and every global load is placed between MFMAs: each sub-step of 16
-// in K reads its operands while the previous one's 16 MFMAs run.
+// nn.Linear layout).  K runs in stages of 64 through two LDS stages of 64
+// KiB: buffer loads write each stage's two 256 x 64 tiles straight into LDS
+// (no registers, no LDS store instructions), each lane fetching the 16-byte
+// chunk that the bank-conflict-free row swizzle puts at its slot; a stage's
+// loads go out as soon as the barrier before the last sub-step of the stage
+// two back frees its LDS, a whole stage before they are read.  Four
+// wavefronts, one per SIMD, each own 128 x 128 of the tile: 4 x 4 blocks of
+// 32 x 32, 256 accumulator registers per lane.  With no second wavefront on
+// the SIMD to hide latency, every LDS read and every load is placed between
+// MFMAs: each sub-step of 16 in K reads its operands while the previous
+// one's 16 MFMAs run.  The forward's grid is persistent (a workgroup per
+// CU, tiles one after another, the stages one stream across tiles).
 //
 // In the output of v_mfma_f32_32x32x16_bf16, lane l holds column l % 32 (a
 // token) and rows 8 (r / 4) + 4 (l / 32) + r % 4 (vocabulary rows) of its
@@ -63,7 +64,7 @@ constexpr int kChunks = kRowBytes / 16;             // 16-byte chunks per row an
 constexpr int kRowsPerLoad = 64 / kChunks;          // tile rows one 1 KiB load fills
 constexpr int kOpBytes = kTileV * kRowBytes;        // one operand's tile in a stage (16 KiB)
 constexpr int kStageBytes = 2 * kOpBytes;           // 32 KiB
-constexpr int kLdsBytes = kStages * kStageBytes;    // 160 KiB
+constexpr int kLdsBytes = kStages * kStageBytes;
 // loads per wavefront, operand and stage: 1 KiB each; loads per wavefront
 // and stage, both operands
 constexpr int kLoadsPerWave = kOpBytes / 1024 / (kThreads / 64);
@@ -71,13 +72,11 @@ constexpr int kStageLoads = 2 * kLoadsPerWave;
 static_assert(kStepK == 32 || kStepK == 64, "stages of 32 or 64 in K");
 static_assert(kStages >= 2 && kLdsBytes <= 160 * 1024, "the stages fit the LDS");
 constexpr float kNegInf = -__builtin_inff();
-static_assert(kLdsBytes >= kTileV * kTileT * 2, "the backward's gradient tile fits the LDS");
 
 // The workgroup's LDS, addressed by offset from the array itself so that
 // every access is known to be an LDS access (reached through a generic
 // pointer, the operand reads became flat loads, which also wait for the
-// global loads in flight).  The stages of both operands; the backward's
-// [256][256] bf16 gradient tile is staged in the same space afterwards.
+// global loads in flight).  The stages of both operands.
 __shared__ u32x4 g_lds[kLdsBytes / 16];
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -281,18 +280,18 @@ __device__ __forceinline__ void sub_step(f32x16 (&acc)[4][4], const Frags &cur, 
 // (a persistent grid takes several), each the product over all of K --
 // acc[vb][tb] is block (vb, tb) of the wavefront's 128 x 128 (vocabulary x
 // tokens) -- handed to epi(acc, tv, tt).  The K stages of all the tiles are
-// one stream through the kStages LDS stages: while stage g is multiplied,
-// stages g + 1 .. g + kStages - 1 are in flight or landed, across tile
-// boundaries, so a tile's first stages load during the last one's
-// epilogue.  Each stage runs kSub sub-steps, sub-step s on one register set
-// while sub-step s + 1's operands are read into the other; stage g +
-// kStages - 1's loads go out during sub-step 0 (into the stage the last
-// barrier freed), the barrier after stage g + 1's loads comes before the
-// last sub-step, which reads stage g + 1's first operands.  Past the last
-// stage the loads still go out, reading nothing and writing zeros into the
-// freed stage, and the reads take values no MFMA uses: every stage runs the
-// same code and the same wait.  PERSIST false: one tile per workgroup (the
-// grid covers the tiles), and epi may use the LDS after stage_barrier<0>.
+// one stream through the kStages LDS stages, across tile boundaries, so a
+// tile's first stages load during the last one's epilogue.  Stage g runs
+// kSub sub-steps, sub-step s on one register set while sub-step s + 1's
+// operands are read into the other; before the last sub-step comes the
+// barrier after stage g + 1's loads (stages g + 2 .. g + kStages - 1 may
+// stay in flight), which also frees stage g's LDS: the last sub-step reads
+// stage g + 1's first operands and sends stage g + kStages's loads into it.
+// Past the last stage the loads still go out, reading nothing and writing
+// zeros into the freed stage, and the reads take values no MFMA uses: every
+// stage runs the same code and the same wait.  PERSIST false: one tile per
+// workgroup (the grid covers the tiles), and epi may use the LDS after
+// stage_barrier<0>.
 template <bool PERSIST, class Epi>
 __device__ __forceinline__ void run_tiles(const MfmaParams &q, Epi &&epi)
 {
@@ -318,12 +317,12 @@ __device__ __forceinline__ void run_tiles(const MfmaParams &q, Epi &&epi)
                 R = tile_rsrcs(q, b + G * ij);
         }
     };
-    for (int s = 0; s < kStages - 1; ++s) {
+    for (int s = 0; s < kStages; ++s) {
         issue_stage(R, L, ist, ikt * kStepK, D, gi < T);
         advance();
     }
-    // stage 0 landed; the kStages - 2 after it may stay in flight
-    stage_barrier<(kStages - 2) * kStageLoads>();
+    // stage 0 landed; the kStages - 1 after it may stay in flight
+    stage_barrier<(kStages - 1) * kStageLoads>();
     Frags f0, f1;
     read_frags(f0, 0, 0);
 
@@ -338,15 +337,16 @@ __device__ __forceinline__ void run_tiles(const MfmaParams &q, Epi &&epi)
                 for (int r = 0; r < 16; ++r)
                     acc[vb][tb][r] = 0.0f;
         for (int kt = 0; kt < nk; ++kt) {
-            sub_step<true, true>(acc, f0, f1, st, 1, R, L, ist, ikt * kStepK, D, gi < T);
-            advance();
+            sub_step<true, false>(acc, f0, f1, st, 1, R, L, 0, 0, D, false);
             if constexpr (kSub == 4) {
                 sub_step<true, false>(acc, f1, f0, st, 2, R, L, 0, 0, D, false);
                 sub_step<true, false>(acc, f0, f1, st, 3, R, L, 0, 0, D, false);
             }
             const int st_next = st + 1 == kStages ? 0 : st + 1;
             stage_barrier<(kStages - 2) * kStageLoads>();
-            sub_step<true, false>(acc, f1, f0, st_next, 0, R, L, 0, 0, D, false);
+            // ist == st here: the stream is kStages stages ahead
+            sub_step<true, true>(acc, f1, f0, st_next, 0, R, L, st, ikt * kStepK, D, gi < T);
+            advance();
             st = st_next;
         }
         int tv, tt;
@@ -428,71 +428,60 @@ stats_kernel(MfmaParams q)
     run_tiles<true>(q, [&](f32x16 (&acc)[4][4], int tv, int tt) { stats_epilogue(q, acc, tv, tt); });
 }
 
-// The gradient tile, transposed and rounded to bf16, staged in LDS as
-// [256 vocabulary rows][256 tokens] (128 KiB, the operand buffers), then
-// written out in 16-byte vectors along the tokens.
+// The backward's tile of G = exp(z - lse) c (the target taking the gradient
+// the combine computed), rounded to bf16, written as G [tokens][ldg] from
+// the accumulators: a lane's registers 4 g .. 4 g + 3 of a block are 4
+// consecutive vocabulary rows of its token, one 8-byte store.
 __device__ __forceinline__ void grad_epilogue(const MfmaParams &q, f32x16 (&acc)[4][4], int tv, int tt)
 {
     const int vbase = tv * kTileV, tbase = tt * kTileT;
     const int t = threadIdx.x;
     const int wave = t >> 6, lane = t & 63;
     const int wv = wave >> 1, wt = wave & 1;
-    // the staged tile [256 vocabulary rows][256 tokens] bf16, as 32-bit words
-    // (pairs of tokens): a lane writes its token's half of each word
-    uint16_t *stage = reinterpret_cast<uint16_t *>(g_lds);
+    const int v0w = vbase + 128 * wv;   // first vocabulary row of the wavefront (chunk-local)
     const float l2c = __log2f(q.c);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-        const int tcol = 128 * wt + 32 * tb + (lane & 31);   // token within the tile
-        const int64_t tok = tbase + tcol;
-        const bool tin = tok < q.M;
+        const int64_t tok = tbase + 128 * wt + 32 * tb + (lane & 31);
+        if (tok >= q.M)
+            continue;
         // exp(z - lse) c = 2^(z log2 e - (lse log2 e - log2 c)), c > 0
-        const float bias = tin ? q.lse[tok] * kLog2e - l2c : 0.0f;
-        const float gt = tin ? q.gt[tok] : 0.0f;
-        int tl = -1;
-        if (tin) {
-            const int64_t g = cek::row_scalar(q.targets, tok) - q.v0 - vbase - 128 * wv;
-            tl = (g >= 0 && g < 128) ? (int)g : -1;
-        }
+        const float bias = q.lse[tok] * kLog2e - l2c;
+        const float gt = q.gt[tok];
+        const int64_t g = cek::row_scalar(q.targets, tok) - q.v0 - v0w;
+        const int tl = (g >= 0 && g < 128) ? (int)g : -1;
+        uint16_t *grow = q.G + tok * q.ldg + v0w;
 #pragma unroll
         for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int v = vrow(vb, r, lane);
-                float g = cek::fast_exp2(__builtin_fmaf(acc[vb][tb][r], kLog2e, -bias));
-                g = v == tl ? gt : g;
-                stage[(128 * wv + v) * kTileT + tcol] = (uint16_t)(cek::pack2<cek::DT_BF16>(g, g) & 0xffffu);
+            for (int gi = 0; gi < 4; ++gi) {
+                float e[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 4 * gi + j;
+                    const float x = cek::fast_exp2(__builtin_fmaf(acc[vb][tb][r], kLog2e, -bias));
+                    e[j] = vrow(vb, r, lane) == tl ? gt : x;
+                }
+                const int v = vrow(vb, 4 * gi, lane);   // the first of the 4 rows
+                const uint32_t lo = cek::pack2<cek::DT_BF16>(e[0], e[1]);
+                const uint32_t hi = cek::pack2<cek::DT_BF16>(e[2], e[3]);
+                if (v0w + v + 4 <= q.vn) {
+                    *reinterpret_cast<uint2 *>(grow + v) = make_uint2(lo, hi);
+                } else {
+                    const uint16_t h[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi,
+                                           (uint16_t)(hi >> 16)};
+                    for (int j = 0; j < 4 && v0w + v + j < q.vn; ++j)
+                        grow[v + j] = h[j];
+                }
             }
-    }
-    __syncthreads();
-    // rows of G^T: vocabulary row vbase + vr (chunk-local), tokens tbase ..
-    constexpr int kVecRow = kTileT / 8;   // 16-byte vectors per staged row
-    for (int i = t; i < kTileV * kVecRow; i += kThreads) {
-        const int vr = i / kVecRow, tv8 = i % kVecRow;
-        const int64_t v = vbase + vr;
-        const int64_t tok0 = tbase + 8 * tv8;
-        if (v >= q.vn || tok0 >= q.M)
-            continue;
-        uint16_t *dst = q.GT + v * q.ldg + tok0;
-        const u32x4 x = g_lds[i];
-        if (tok0 + 8 <= q.M) {
-            *reinterpret_cast<u32x4 *>(dst) = x;
-        } else {
-            const uint16_t *e = reinterpret_cast<const uint16_t *>(&x);
-            for (int j = 0; j < 8 && tok0 + j < q.M; ++j)
-                dst[j] = e[j];
-        }
     }
 }
 
-// The backward: a workgroup per tile (the epilogue uses the LDS).
+// The backward: a persistent grid like the forward's.
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 grad_kernel(MfmaParams q)
 {
-    run_tiles<false>(q, [&](f32x16 (&acc)[4][4], int tv, int tt) {
-        stage_barrier<0>();   // one tile per workgroup: every operand read done, LDS free
-        grad_epilogue(q, acc, tv, tt);
-    });
+    run_tiles<true>(q, [&](f32x16 (&acc)[4][4], int tv, int tt) { grad_epilogue(q, acc, tv, tt); });
 }
 
 }  // namespace

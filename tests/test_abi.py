@@ -304,7 +304,7 @@ def test_linear_chunk_and_workspace(lib):
     n = lib.ce_linear_workspace_bytes(64, 128, 5000, 1024)
     assert n >= 64 * 1024 * 6 + 64 * 5 * 8
     # the matrix-core path: (max, sum) per token and 128 vocabulary rows, and
-    # the transposed bf16 gradient chunk
+    # the bf16 gradient chunk
     assert n >= 64 * 2 * ((5000 + 255) // 256) * 8 + 1024 * 64 * 2
     assert lib.ce_linear_workspace_bytes(64, 0, 5000, 0) == 0
 
