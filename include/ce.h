@@ -22,11 +22,16 @@
  * accumulated in fp64 and the
  * mean/sum is formed in fp64 in a fixed order, so results are bitwise
  * reproducible for a given device and shape.  Gradients are rounded to the
- * storage type with round-to-nearest-even (subnormals kept).
+ * storage type with round-to-nearest-even (subnormals kept).  The final sum
+ * of a mean/sum runs as a second one-wavefront kernel, or, for inputs of at
+ * most 8 MiB outside graph capture, in the last workgroup of the same launch
+ * (the same fixed order, the same bits): that takes one integer counter per
+ * device and stream in the library's own device memory, zero between calls.
  *
  * Memory and ownership: every pointer is device memory owned by the caller.
  * The library allocates nothing, frees nothing and keeps no pointer after a
- * call returns.  Calls are asynchronous on `stream` (a hipStream_t; NULL is
+ * call returns (its static device memory -- the counters above and the
+ * scratch of ce_fwd_noalloc -- is part of the loaded library).  Calls are asynchronous on `stream` (a hipStream_t; NULL is
  * the null stream); argument errors are returned synchronously before any
  * launch.
  *
@@ -205,6 +210,15 @@ int ce_softmax(const void *logits, int64_t M, int64_t V, ce_dtype_t dtype,
 
 /* A static, human-readable name for a status code. */
 const char *ce_status_string(int status);
+
+/*
+ * The library reads its tuning environment variables once, at its first
+ * call: CE_FORCE_PLAN, CE_FORCE_SPLIT, CE_FORCE_NBUF, CE_WAVES_PER_CU,
+ * CE_FORCE_GRID, CE_ROW_MAP (kernel mapping and launch overrides) and
+ * CE_LINEAR_GEMM (ce_linear.h).  ce_tuning_reload reads them again; for
+ * tuning and tests, and not while other threads call the library.
+ */
+void ce_tuning_reload(void);
 
 /* Operations ce_plan_describe can describe. */
 enum {

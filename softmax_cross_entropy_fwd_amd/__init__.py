@@ -35,6 +35,9 @@ REDUCTIONS = {"none": CE_NONE, "mean": CE_MEAN, "sum": CE_SUM}
 _lib = None
 _lock = threading.Lock()
 _workspaces = {}
+_codes = None          # torch dtype -> CE_* code
+_raw_stream = None     # torch's accessor of the current raw stream handle
+_get_device = None     # torch's accessor of the current device index
 
 
 class CEError(RuntimeError):
@@ -82,17 +85,30 @@ def load_library(path=None):
         lib.ce_status_string.restype = ctypes.c_char_p
         lib.ce_plan_describe.argtypes = [i64, i64, i32, i32, i32, ctypes.c_char_p, sz]
         lib.ce_plan_describe.restype = i32
+        lib.ce_tuning_reload.argtypes = []
+        lib.ce_tuning_reload.restype = None
         if path is None:
             _lib = lib
         return lib
 
 
+def reload_tuning():
+    """Make the library read its tuning environment variables again (it reads
+    them once, at its first call); for tuning and tests, not while other
+    threads call the library."""
+    load_library().ce_tuning_reload()
+    _ws_bytes.clear()
+
+
 def _dtype_code(t):
-    import torch
-    codes = {torch.float32: CE_F32, torch.float16: CE_F16, torch.bfloat16: CE_BF16}
-    if t.dtype not in codes:
+    global _codes
+    if _codes is None:
+        import torch
+        _codes = {torch.float32: CE_F32, torch.float16: CE_F16, torch.bfloat16: CE_BF16}
+    code = _codes.get(t.dtype)
+    if code is None:
         raise TypeError("logits must be float32, float16 or bfloat16, got %s" % t.dtype)
-    return codes[t.dtype]
+    return code
 
 
 def ce_status_string(status):
@@ -139,20 +155,22 @@ def _cached_workspace(device, handle, nbytes, stream=None):
 def _stream_handle(dev):
     """The raw hipStream_t of torch's current stream on dev (torch's own
     accessor when it has one: the Stream object costs ~2 us per call)."""
-    import torch
-    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
-    if raw is not None:
-        return int(raw(dev.index))
-    return int(torch.cuda.current_stream(dev).cuda_stream)
+    global _raw_stream
+    if _raw_stream is None:
+        import torch
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _raw_stream = raw if raw is not None else (
+            lambda i: torch.cuda.current_stream(i).cuda_stream)
+    return int(_raw_stream(dev.index))
 
 
+# sizes from ce_workspace_bytes, which also depend on the split and plan
+# overrides the library read (cleared by reload_tuning)
 _ws_bytes = {}
 
 
 def _workspace_bytes(lib, M, V, code, red):
-    # the size also depends on the split and plan overrides the library reads
-    env = os.environ
-    key = (M, V, code, red, env.get("CE_FORCE_SPLIT"), env.get("CE_FORCE_PLAN"))
+    key = (M, V, code, red)
     n = _ws_bytes.get(key)
     if n is None:
         n = int(lib.ce_workspace_bytes(M, V, code, red))
@@ -185,14 +203,17 @@ def _check(logits, targets):
     _check_logits(logits)
     if targets.dtype != torch.int64 or targets.dim() != 1 or not targets.is_contiguous():
         raise ValueError("targets must be a contiguous int64 [M] tensor")
-    if targets.device != logits.device or targets.numel() != logits.shape[0]:
+    if targets.get_device() != logits.get_device() or targets.numel() != logits.shape[0]:
         raise ValueError("targets must be on the logits' device with M entries")
 
 
 def _invoke(fn, dev, args):
     """Calls a library entry point with dev current (switching only if needed)."""
+    global _get_device
     import torch
-    if torch.cuda.current_device() == dev.index:
+    if _get_device is None:
+        _get_device = getattr(torch._C, "_cuda_getDevice", torch.cuda.current_device)
+    if _get_device() == dev.index:
         return fn(*args)
     with torch.cuda.device(dev):
         return fn(*args)
@@ -200,7 +221,7 @@ def _invoke(fn, dev, args):
 
 def _call(fn_name, logits, targets, reduction, out, workspace, lse=None):
     import torch
-    lib = load_library()
+    lib = _lib or load_library()
     _check(logits, targets)
     red = REDUCTIONS[reduction]
     M, V = logits.shape

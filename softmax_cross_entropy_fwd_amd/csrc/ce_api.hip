@@ -9,8 +9,10 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <unordered_map>
+#include <utility>
 
 #include "ce.h"
 #include "ce_device.h"
@@ -180,9 +182,8 @@ void choose_shape(int64_t nvec, bool bwd, bool aligned, bool wide, int *kind, in
 
 // CE_FORCE_PLAN=rows:G:K | wg:W:K | wg2:W:K | stream:W:K | wstream:1:K overrides the
 // mapping (tuning).
-bool forced_shape(int *kind, int *a, int *b)
+bool parse_forced_shape(const char *s, int *kind, int *a, int *b)
 {
-    const char *s = std::getenv("CE_FORCE_PLAN");
     if (!s || !*s)
         return false;
     char name[16] = {0};
@@ -203,6 +204,66 @@ bool forced_shape(int *kind, int *a, int *b)
         return false;
     *a = x;
     *b = y;
+    return true;
+}
+
+// The tuning environment variables, read once (at the first call, and again
+// by ce_tuning_reload): CE_FORCE_PLAN, CE_FORCE_SPLIT, CE_FORCE_NBUF,
+// CE_WAVES_PER_CU, CE_FORCE_GRID, CE_ROW_MAP and CE_LINEAR_GEMM.
+// `generation` changes on every reload, so cached plans follow.
+struct Tuning {
+    bool plan_set = false;       // CE_FORCE_PLAN non-empty
+    bool plan_ok = false;        // ... and parsed
+    int fk = 0, fa = 0, fb = 0;  // its shape
+    int force_split = -1;        // CE_FORCE_SPLIT (-1: unset)
+    int force_nbuf = 0;          // CE_FORCE_NBUF (0: unset)
+    int waves_per_cu = 0;        // CE_WAVES_PER_CU (0: unset)
+    int64_t force_grid = 0;      // CE_FORCE_GRID (0: unset)
+    bool blocked = false;        // CE_ROW_MAP=blocked
+    bool linear_library = false; // CE_LINEAR_GEMM=library
+    unsigned generation = 0;
+};
+
+Tuning g_tuning;
+std::once_flag g_tuning_once;
+std::mutex g_tuning_mu;
+
+void read_tuning(Tuning *t)
+{
+    const unsigned gen = t->generation + 1;
+    *t = Tuning();
+    t->generation = gen;
+    const char *fp = std::getenv("CE_FORCE_PLAN");
+    t->plan_set = fp && *fp;
+    t->plan_ok = parse_forced_shape(fp, &t->fk, &t->fa, &t->fb);
+    const char *f = std::getenv("CE_FORCE_SPLIT");
+    t->force_split = (f && *f) ? std::atoi(f) : -1;
+    const char *nb = std::getenv("CE_FORCE_NBUF");
+    t->force_nbuf = nb ? std::atoi(nb) : 0;
+    const char *tw = std::getenv("CE_WAVES_PER_CU");
+    t->waves_per_cu = (tw && std::atoi(tw) > 0) ? std::atoi(tw) : 0;
+    const char *g = std::getenv("CE_FORCE_GRID");
+    t->force_grid = (g && *g && std::atoll(g) > 0) ? std::atoll(g) : 0;
+    const char *map = std::getenv("CE_ROW_MAP");
+    t->blocked = map && !std::strcmp(map, "blocked");
+    const char *lg = std::getenv("CE_LINEAR_GEMM");
+    t->linear_library = lg && !std::strcmp(lg, "library");
+}
+
+const Tuning &tuning()
+{
+    std::call_once(g_tuning_once, [] { read_tuning(&g_tuning); });
+    return g_tuning;
+}
+
+bool forced_shape(int *kind, int *a, int *b)
+{
+    const Tuning &t = tuning();
+    if (!t.plan_ok)
+        return false;
+    *kind = t.fk;
+    *a = t.fa;
+    *b = t.fb;
     return true;
 }
 
@@ -261,10 +322,9 @@ int64_t window_vectors(int64_t V, int E, bool aligned)
 // set.  Both are for tuning and tests.
 int split_slices(int64_t M, int64_t nvec, int *slice_vecs)
 {
-    const char *f = std::getenv("CE_FORCE_SPLIT");
-    const int forced = (f && *f) ? std::atoi(f) : -1;
-    const char *fp = std::getenv("CE_FORCE_PLAN");
-    if (forced == 0 || (forced < 0 && fp && *fp))
+    const Tuning &t = tuning();
+    const int forced = t.force_split;
+    if (forced == 0 || (forced < 0 && t.plan_set))
         return 0;
     const int64_t max_rows = forced > 0 ? kSplitMaxRowsForced : kSplitMaxRows;
     const int64_t min_vecs = forced > 0 ? 2 * cek::kSplitChunk : kSplitMinVecs;
@@ -331,10 +391,9 @@ int make_plan(int64_t M, int64_t V, int dtype, int op, bool aligned, Plan *plan)
     plan->b = b;
     plan->exact = aligned && tile_vectors(kind, a, b) == nvec;
     plan->nbuf = kind == cek::KIND_ROWS ? nbuf : 1;
-    const char *nb = std::getenv("CE_FORCE_NBUF");
-    if (kind == cek::KIND_ROWS && nb &&
-        (std::atoi(nb) == 1 || std::atoi(nb) == 2 || std::atoi(nb) == 17 || std::atoi(nb) == 18))
-        plan->nbuf = std::atoi(nb);
+    const int fnb = tuning().force_nbuf;
+    if (kind == cek::KIND_ROWS && (fnb == 1 || fnb == 2 || fnb == 17 || fnb == 18))
+        plan->nbuf = fnb;
     plan->k = lookup(dtype, op, kind, a, b, plan->exact, plan->nbuf);
     if (!plan->k.fn && plan->nbuf != nbuf) {   // an override with no such instance
         plan->nbuf = kind == cek::KIND_ROWS ? nbuf : 1;
@@ -359,8 +418,8 @@ int make_plan(int64_t M, int64_t V, int dtype, int op, bool aligned, Plan *plan)
     // a whole row of loads in flight, so the rows kernel runs 4 waves per CU
     // and the workgroup kernels 16.
     const int waves_per_wg = plan->k.block / 64;
-    const char *tw = std::getenv("CE_WAVES_PER_CU");
-    const int target_waves = (tw && std::atoi(tw) > 0) ? std::atoi(tw)
+    const int tw = tuning().waves_per_cu;
+    const int target_waves = tw > 0                   ? tw
                              : kind == cek::KIND_ROWS ? 4
                              : waves > 0              ? waves
                                                       : 16;
@@ -370,9 +429,8 @@ int make_plan(int64_t M, int64_t V, int dtype, int op, bool aligned, Plan *plan)
     if (wg_per_cu > plan->occupancy)
         wg_per_cu = plan->occupancy;
     int64_t cap = (int64_t)plan->cus * wg_per_cu;
-    const char *g = std::getenv("CE_FORCE_GRID");
-    if (g && *g && std::atoll(g) > 0)
-        cap = std::atoll(g);
+    if (tuning().force_grid > 0)
+        cap = tuning().force_grid;
     // one published partial per wavefront (rows kernels) or workgroup
     const int64_t units_per_wg =
         (kind == cek::KIND_ROWS || kind == cek::KIND_WSTREAM) ? plan->k.block / 64 : 1;
@@ -455,7 +513,9 @@ int call_split(const Call &c, int *slice_vecs)
     return S;
 }
 
-int check_args(const Call &c)
+// split: receives the slices per row the call uses (call_split), when the
+// arguments pass.
+int check_args(const Call &c, int *split = nullptr, int *slice_vecs = nullptr)
 {
     if (c.dtype != CE_F32 && c.dtype != CE_F16 && c.dtype != CE_BF16)
         return CE_ERR_DTYPE;
@@ -467,6 +527,8 @@ int check_args(const Call &c)
     if (c.M > 0 && (uint64_t)c.M > (uint64_t)INT64_MAX / (uint64_t)c.V / s)
         return CE_ERR_SHAPE;
     const bool reduced = c.loss && c.reduction != CE_NONE;
+    if (split)
+        *split = 0;
     if (c.M == 0) {
         if (reduced && !c.out)
             return CE_ERR_NULL;
@@ -495,13 +557,15 @@ int check_args(const Call &c)
     const size_t xb = (size_t)c.M * (size_t)c.V * s;
     const size_t per_row = (size_t)c.M * 4;
     const size_t nd = c.reduction == CE_NONE ? per_row : 4;
+    int sv = 0;
+    const int S = call_split(c, &sv);
     const Region outs[] = {
         {c.out, c.loss ? (c.reduction == CE_NONE ? per_row : 4) : 0},
         {c.lse_out, per_row},
         {c.y == c.logits ? nullptr : c.y, has_y ? xb : 0},
         {c.y == c.logits ? c.y : nullptr, has_y ? xb : 0},
         // a static device symbol of the library cannot overlap the caller's buffers
-        {c.own_scratch ? nullptr : c.ws, used_workspace(c.M, reduced, call_split(c, nullptr))},
+        {c.own_scratch ? nullptr : c.ws, used_workspace(c.M, reduced, S)},
     };
     const Region ins[] = {
         {c.y == c.logits ? nullptr : c.logits, xb},
@@ -518,12 +582,124 @@ int check_args(const Call &c)
             if (overlaps(outs[i].p, outs[i].n, ins[j].p, ins[j].n))
                 return CE_ERR_ALIAS;
     }
+    if (split)
+        *split = S;
+    if (slice_vecs)
+        *slice_vecs = sv;
     return CE_OK;
+}
+
+// Plans of recent calls, per host thread: a call repeats the last few
+// shapes far more often than not, and a hit skips make_plan's device
+// queries.  Keyed by everything make_plan reads, the tuning generation
+// included.
+struct PlanKey {
+    int64_t M = -1, V = 0;
+    int dtype = 0, op = 0, dev = -1;
+    bool aligned = false;
+    unsigned gen = 0;
+    bool operator==(const PlanKey &o) const
+    {
+        return M == o.M && V == o.V && dtype == o.dtype && op == o.op && dev == o.dev &&
+               aligned == o.aligned && gen == o.gen;
+    }
+};
+constexpr int kPlanCache = 8;
+thread_local PlanKey t_plan_keys[kPlanCache];
+thread_local Plan t_plans[kPlanCache];
+thread_local int t_plan_next = 0;
+
+int cached_plan(int64_t M, int64_t V, int dtype, int op, bool aligned, Plan *plan)
+{
+    PlanKey key;
+    key.M = M;
+    key.V = V;
+    key.dtype = dtype;
+    key.op = op;
+    key.aligned = aligned;
+    key.gen = tuning().generation;
+    if (hipGetDevice(&key.dev) != hipSuccess)
+        return CE_ERR_HIP;
+    for (int i = 0; i < kPlanCache; ++i)
+        if (t_plan_keys[i] == key) {
+            *plan = t_plans[i];
+            return CE_OK;
+        }
+    const int rc = make_plan(M, V, dtype, op, aligned, plan);
+    if (rc)
+        return rc;
+    t_plan_keys[t_plan_next] = key;
+    t_plans[t_plan_next] = *plan;
+    t_plan_next = (t_plan_next + 1) % kPlanCache;
+    return CE_OK;
+}
+
+// ---- the final sum in the rows kernel's own launch (finish_in_kernel) ----
+// For inputs up to kFuseMaxBytes a mean or sum finishes in the launch of the
+// rows kernel: launch-bound calls save the second launch.  Each (device,
+// stream) gets a counter in the library's device memory (zero at load, and
+// put back to zero by every launch that uses it); calls on one stream run
+// in order, so they never share a counter at the same time.  Calls being
+// captured into a graph, and streams past the last counter, keep the
+// second launch.
+constexpr size_t kFuseMaxBytes = 8u << 20;
+constexpr int kTicketSlots = 1024;
+constexpr int kMaxTicketDevices = 64;
+
+}  // namespace
+
+static __device__ unsigned tickets[kTicketSlots];
+
+namespace {
+
+std::mutex g_ticket_mu;
+unsigned *g_ticket_base[kMaxTicketDevices];
+std::map<std::pair<int, hipStream_t>, int> g_ticket_slot;
+thread_local int t_ticket_dev = -1;
+thread_local hipStream_t t_ticket_stream = nullptr;
+thread_local unsigned *t_ticket = nullptr;
+
+// The counter of (current device, st), or null (second launch instead).
+unsigned *ticket_for(hipStream_t st)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxTicketDevices)
+        return nullptr;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+        return nullptr;
+    if (t_ticket && t_ticket_dev == dev && t_ticket_stream == st)
+        return t_ticket;
+    std::lock_guard<std::mutex> lk(g_ticket_mu);
+    if (!g_ticket_base[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(tickets)) != hipSuccess || !p)
+            return nullptr;
+        g_ticket_base[dev] = (unsigned *)p;
+    }
+    auto it = g_ticket_slot.find({dev, st});
+    int slot;
+    if (it != g_ticket_slot.end()) {
+        slot = it->second;
+    } else {
+        slot = 0;
+        for (const auto &kv : g_ticket_slot)
+            if (kv.first.first == dev)
+                ++slot;
+        if (slot >= kTicketSlots)
+            return nullptr;
+        g_ticket_slot[{dev, st}] = slot;
+    }
+    t_ticket_dev = dev;
+    t_ticket_stream = st;
+    t_ticket = g_ticket_base[dev] + slot;
+    return t_ticket;
 }
 
 int run(const Call &c, void *stream)
 {
-    int rc = check_args(c);
+    int S = 0, slice_vecs = 0;
+    int rc = check_args(c, &S, &slice_vecs);
     if (rc)
         return rc;
     hipStream_t st = (hipStream_t)stream;
@@ -543,10 +719,8 @@ int run(const Call &c, void *stream)
     const int head0 = (int)((base % 16) / s);
     const bool aligned = head0 == 0 && c.V % E == 0;
     Plan plan;
-    int slice_vecs = 0;
-    const int S = call_split(c, &slice_vecs);
     if (S == 0) {
-        rc = make_plan(c.M, c.V, c.dtype, c.op, aligned, &plan);
+        rc = cached_plan(c.M, c.V, c.dtype, c.op, aligned, &plan);
         if (rc)
             return rc;
     }
@@ -562,8 +736,7 @@ int run(const Call &c, void *stream)
     p.V = c.V;
     p.head0 = head0;
     p.aligned = aligned ? 1 : 0;
-    const char *map = std::getenv("CE_ROW_MAP");
-    p.blocked = (map && !std::strcmp(map, "blocked")) ? 1 : 0;
+    p.blocked = tuning().blocked ? 1 : 0;
     // Only calls that compute losses reduce them (and have a workspace); the
     // split backward uses its reduction for the gradient scale and the shape
     // of dloss alone.
@@ -582,6 +755,10 @@ int run(const Call &c, void *stream)
     p.stats = S ? (float *)((char *)c.ws + kPartialBytes) : nullptr;
     p.fix = S ? p.stats + 2 * (size_t)c.M * (size_t)S : nullptr;
     p.rowx = S ? p.fix + (size_t)c.M * (size_t)S : nullptr;
+    p.ticket = nullptr;
+    if (reduction != CE_NONE && S == 0 && plan.kind == cek::KIND_ROWS &&
+        (size_t)c.M * (size_t)c.V * s <= kFuseMaxBytes)
+        p.ticket = ticket_for(st);
     void *args[] = {&p};
     unsigned nunits = 0;
     if (S) {
@@ -607,7 +784,7 @@ int run(const Call &c, void *stream)
             return CE_ERR_HIP;
         nunits = (unsigned)(plan.grid * plan.units_per_wg);
     }
-    if (reduction != CE_NONE) {
+    if (reduction != CE_NONE && !p.ticket) {
         // the fixed-order sum of the units' partials (same stream, after the grid)
         void *args2[] = {&p, &nunits};
         if (hipLaunchKernel(cek::sum_partials_fn(), dim3(1), dim3(64), args2, 0, st) != hipSuccess)
@@ -657,7 +834,18 @@ int scratch_address(void **ptr)
 
 }  // namespace
 
+namespace cek {
+bool tuning_linear_library() { return tuning().linear_library; }
+}  // namespace cek
+
 extern "C" {
+
+void ce_tuning_reload(void)
+{
+    tuning();   // the first read, if not done yet
+    std::lock_guard<std::mutex> lk(g_tuning_mu);
+    read_tuning(&g_tuning);
+}
 
 size_t ce_workspace_bytes(int64_t M, int64_t V, ce_dtype_t dtype, ce_reduction_t reduction)
 {

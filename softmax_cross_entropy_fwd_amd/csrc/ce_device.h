@@ -75,6 +75,9 @@ struct Params {
     float *stats;            // [M * S][2] slice (max, sum) with the target left out
     float *fix;              // [M * S] slice sums of p_j, j != t (backward from lse)
     float *rowx;             // [M] target logits, saved before any slice is overwritten
+    // non-null (rows kernels, mean or sum): the last workgroup to finish adds
+    // the partials and writes out[0] in this launch (finish_in_kernel)
+    unsigned *ticket;
 };
 
 // ------------------------------------------------------------ storage types
@@ -1041,6 +1044,33 @@ __device__ __forceinline__ double sum_partials(const double *partials, unsigned 
     return wave_sum_f64(acc);
 }
 
+// The final sum of a mean or sum in the launch that made the partials:
+// each workgroup, once all its wavefronts have published theirs, takes a
+// ticket (an integer counter, agent scope, acquire-release); the one that
+// takes the last adds all nunits partials with sum_partials, in the same
+// fixed order as the second-kernel form, so the result is that form's bit
+// for bit, and puts the counter back to zero for the next launch.
+__device__ __forceinline__ void finish_in_kernel(const Params &p, unsigned nunits, int lane,
+                                                 int wave)
+{
+    __shared__ unsigned s_last;
+    __syncthreads();   // the workgroup's partials are written
+    if (threadIdx.x == 0) {
+        const unsigned prev =
+            __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = prev + 1 == gridDim.x ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!s_last || wave != 0)
+        return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the other workgroups' partials
+    const double total = sum_partials(p.partials, nunits, lane);
+    if (lane == 0) {
+        p.out[0] = (float)(total * p.out_scale);
+        __hip_atomic_store(p.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 // ================================================================ kernels
 
 
@@ -1140,6 +1170,8 @@ __global__ void __launch_bounds__(NW * 64) rows_kernel(Params p)
     const double wave_total = wave_sum_f64(acc);
     if (lane == 0)
         p.partials[blockIdx.x * nwaves + wave] = wave_total;
+    if (p.ticket)
+        finish_in_kernel(p, (unsigned)(gridDim.x * nwaves), lane, wave);
 }
 
 // ---- one row per workgroup, row in registers --------------------------------

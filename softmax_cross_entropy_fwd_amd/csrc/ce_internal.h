@@ -48,4 +48,7 @@ SplitKernels split_kernels_bf16();
 const void *empty_reduce_fn();
 const void *sum_partials_fn();
 
+// CE_LINEAR_GEMM=library, as read with the other tuning variables.
+bool tuning_linear_library();
+
 }  // namespace cek

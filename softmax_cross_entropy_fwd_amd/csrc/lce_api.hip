@@ -230,11 +230,10 @@ int run(const void *H, const void *W, const int64_t *targets, int64_t M, int64_t
     // 16-byte vectors (D % 8 == 0, H and W on 16-byte boundaries) and a
     // 256-row tile's bytes fit the kernels' 32-bit buffer offsets (D <=
     // 2^20); else, or with CE_LINEAR_GEMM=library (comparisons), rocBLAS.
-    const char *gsel = std::getenv("CE_LINEAR_GEMM");
     const int64_t tiles = ((V + kMfmaTile - 1) / kMfmaTile) * ((M + kMfmaTile - 1) / kMfmaTile);
     const bool mfma = D % 8 == 0 && D <= (int64_t(1) << 20) && (uintptr_t)H % 16 == 0 &&
                       (uintptr_t)W % 16 == 0 && tiles <= INT_MAX &&
-                      !(gsel && !std::strcmp(gsel, "library"));
+                      !cek::tuning_linear_library();
     // rocBLAS serves the library forward and the backward's dH and dW
     rocblas_handle h = nullptr;
     std::unique_lock<std::mutex> blas_lock;

@@ -221,7 +221,7 @@ def call_noalloc(lib, logits=FAKE, targets=FAKE, M=4, V=8, dtype=0, red=1, out=F
                               M, V, dtype, red, VP(out) if out else None, None)
 
 
-def test_noalloc_argument_errors(lib, monkeypatch):
+def test_noalloc_argument_errors(lib, tuning):
     import softmax_cross_entropy_fwd_amd as ce
     assert call_noalloc(lib, dtype=3) == ce.CE_ERR_DTYPE
     assert call_noalloc(lib, red=3) == ce.CE_ERR_REDUCTION
@@ -237,7 +237,7 @@ def test_noalloc_argument_errors(lib, monkeypatch):
     # before any HIP call.  Unforced, 512 rows are not split and need only the
     # partial sums (such a call would run; it is not made here, without a GPU).
     big = 1 << 40
-    monkeypatch.setenv("CE_FORCE_SPLIT", "64")
+    tuning.setenv("CE_FORCE_SPLIT", "64")
     assert (128 << 10) + 512 * (16 * 12 + 4) > ce.CE_NOALLOC_SCRATCH_BYTES
     assert call_noalloc(lib, logits=FAKE, targets=FAKE + big, M=512, V=1 << 17, dtype=2,
                         out=FAKE + 2 * big) == ce.CE_ERR_SCRATCH

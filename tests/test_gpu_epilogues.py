@@ -99,10 +99,10 @@ def test_fwd_lse_workloads_small_m(ce):
                      reduction="mean")
 
 
-def test_fwd_lse_wave_stream_shapes(ce, monkeypatch):
+def test_fwd_lse_wave_stream_shapes(ce, tuning):
     # the wave-per-row streaming forward writes lse too
     for shape in ("wstream:1:2", "wstream:1:4", "wstream:1:8", "stream:8:4", "stream:16:4"):
-        monkeypatch.setenv("CE_FORCE_PLAN", shape)
+        tuning.setenv("CE_FORCE_PLAN", shape)
         for dtype in DTYPES:
             for V in (5, 3000, 20000):
                 fwd_lse_case(ce, dtype, 11, V, 4.0, seed=V + 3, reduction="sum", offset=V % 2)
@@ -277,7 +277,7 @@ def test_softmax_degenerate_rows(ce):
                 softmax_case(ce, dtype, 4, V, 0, 0, log=log, x=x.clone())
 
 
-def test_every_softmax_and_grad_shape(ce, monkeypatch):
+def test_every_softmax_and_grad_shape(ce, tuning):
     # the shapes the plan table gives softmax, log-softmax and the fused backward
     for shape, cap in (("rows:1:1", 1), ("rows:1:2", 2), ("rows:1:4", 4), ("rows:2:4", 8),
                        ("rows:4:4", 16), ("rows:4:8", 32), ("rows:16:4", 64),
@@ -288,7 +288,7 @@ def test_every_softmax_and_grad_shape(ce, monkeypatch):
                        ("wg2:8:13", 6656),
                        ("wg:16:12", 12288), ("wg:16:16", 16384), ("stream:8:4", 1 << 30),
                        ("stream:16:4", 1 << 30)):
-        monkeypatch.setenv("CE_FORCE_PLAN", shape)
+        tuning.setenv("CE_FORCE_PLAN", shape)
         for dtype in DTYPES:
             if shape.startswith("wg2") and dtype == "f32":
                 continue   # 16-bit storage only

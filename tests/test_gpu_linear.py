@@ -140,14 +140,14 @@ def test_linear_matrix_core_ragged_tiles(ce):
     run_case(ce, 3, 72, 77, 0, "mean", seed=25)
 
 
-def test_linear_both_gemm_paths(ce, monkeypatch):
+def test_linear_both_gemm_paths(ce, tuning):
     # the same inputs through the matrix-core kernels and the library GEMMs:
     # both within the oracle bounds, and within twice them of each other
     h, w, t = inputs.make_linear(96, 512, 9000, 2.0, 26)
     a = run_case(ce, 96, 512, 9000, 2048, "none", 0, h=h, w=w, t=t)
-    monkeypatch.setenv("CE_LINEAR_GEMM", "library")
+    tuning.setenv("CE_LINEAR_GEMM", "library")
     b = run_case(ce, 96, 512, 9000, 2048, "none", 0, h=h, w=w, t=t)
-    monkeypatch.delenv("CE_LINEAR_GEMM")
+    tuning.delenv("CE_LINEAR_GEMM")
     e = logit_bounds(values(h), values(w))
     bound = 2 * loss_bounds(b.cpu().numpy().astype(np.float64), 0.0, e)
     assert np.all(np.abs(a.cpu().numpy() - b.cpu().numpy()) <= bound + 1e-6)

@@ -149,13 +149,13 @@ NBUFS = {"rows:64:16": ("1", "2", "17", "18"), "rows:4:8": ("1", "2", "17", "18"
 
 
 @pytest.mark.parametrize("shape", SHAPES)
-def test_every_kernel_shape(ce, shape, monkeypatch):
+def test_every_kernel_shape(ce, shape, tuning):
     kind, a, b = shape.split(":")
     a, b = int(a), int(b)
     cap = a * b if kind == "rows" else (a * 64 * b if kind in ("wg", "wg2") else 1 << 30)
-    monkeypatch.setenv("CE_FORCE_PLAN", shape)
+    tuning.setenv("CE_FORCE_PLAN", shape)
     for nbuf in NBUFS.get(shape, ("1", "2") if kind == "rows" else ("1",)):
-        monkeypatch.setenv("CE_FORCE_NBUF", nbuf)
+        tuning.setenv("CE_FORCE_NBUF", nbuf)
         _check_shape(ce, shape, kind, cap)
 
 
@@ -263,14 +263,14 @@ def test_dominant_target_loss_and_grad_accuracy(ce):
 
 
 @pytest.mark.parametrize("shape", [None, "stream:4:4", "stream:8:4", "stream:16:4"])
-def test_dominant_target_small_loss_relative(ce, shape, monkeypatch):
+def test_dominant_target_small_loss_relative(ce, shape, tuning):
     import torch
     # p_t > 1/2: the loss log1p(sum of the other terms / e_t) keeps its
     # relative accuracy however small it is (no absolute floor here), in the
     # streamed kernels (which leave the target out of their first pass) and
     # in the default mappings (which sum the other terms on a second read)
     if shape:
-        monkeypatch.setenv("CE_FORCE_PLAN", shape)
+        tuning.setenv("CE_FORCE_PLAN", shape)
     for dtype in DTYPES:
         for V in (3000, 20000, 50257):
             for gap in (12.0, 30.0):

@@ -66,10 +66,10 @@ def test_split_softmax(ce, dtype, V):
                          want_lse=False)
 
 
-def test_split_stress_rows(ce, monkeypatch):
+def test_split_stress_rows(ce, tuning):
     # the stress structure at a few rows: dominant targets (the sum of the
     # other terms comes from the slices), -inf entries, all-equal rows
-    monkeypatch.setenv("CE_FORCE_SPLIT", "4")
+    tuning.setenv("CE_FORCE_SPLIT", "4")
     for dtype in DTYPES:
         for M in (100, 300):
             run_and_check(ce, dtype, M, 50257, 8.0, seed=104, structure="stress",
@@ -84,9 +84,9 @@ def test_split_stress_rows(ce, monkeypatch):
                          offset=1)
 
 
-def test_split_dominant_targets_and_bad_targets(ce, monkeypatch):
+def test_split_dominant_targets_and_bad_targets(ce, tuning):
     import torch
-    monkeypatch.setenv("CE_FORCE_SPLIT", "3")
+    tuning.setenv("CE_FORCE_SPLIT", "3")
     for dtype in DTYPES:
         V = 40000
         M = 6
@@ -114,7 +114,7 @@ def test_split_dominant_targets_and_bad_targets(ce, monkeypatch):
             check_grads(host_grad_bits(y), want, dtype, 1.0, want64)
 
 
-def test_split_matches_one_row_path(ce, monkeypatch):
+def test_split_matches_one_row_path(ce, tuning):
     # The split and the one-row paths agree with each other, and both with the
     # oracle element by element.  For bf16 rows of 131072 the one-row path is
     # the exact 16-wave register tile the full-size LM head runs.
@@ -125,7 +125,7 @@ def test_split_matches_one_row_path(ce, monkeypatch):
         a = ce.ce_fwd(x, t, "none")
         ga = x.clone()
         la = ce.ce_fwd_bwd_inplace(ga, t, "mean")
-        monkeypatch.setenv("CE_FORCE_SPLIT", "0")
+        tuning.setenv("CE_FORCE_SPLIT", "0")
         plan = ce.ce_plan_describe(24, V, DCODE[dtype], "mean", fwd_bwd=True)
         say("one-row plan", dtype, V, plan)
         if (dtype, V) == ("bf16", 131072):
@@ -133,7 +133,7 @@ def test_split_matches_one_row_path(ce, monkeypatch):
         b = ce.ce_fwd(x, t, "none")
         gb = x.clone()
         lb = ce.ce_fwd_bwd_inplace(gb, t, "mean")
-        monkeypatch.delenv("CE_FORCE_SPLIT")
+        tuning.delenv("CE_FORCE_SPLIT")
         torch.cuda.synchronize()
         np.testing.assert_allclose(a.cpu().numpy(), b.cpu().numpy(), rtol=2e-6, atol=2e-6)
         check_scalar(la.item(), lb.item(), rtol=2e-6)
@@ -162,10 +162,10 @@ def test_lmhead_register_tile_every_element(ce, M):
                   reduction="sum", op="fwd_bwd")
 
 
-def test_split_forced_slice_counts(ce, monkeypatch):
+def test_split_forced_slice_counts(ce, tuning):
     # every slice count the plan can take, including one slice per chunk
     for S in (2, 3, 16, 64):
-        monkeypatch.setenv("CE_FORCE_SPLIT", str(S))
+        tuning.setenv("CE_FORCE_SPLIT", str(S))
         for dtype, V in (("bf16", 131072), ("f32", 70001)):
             say("forced split", S, dtype, V)
             run_and_check(ce, dtype, 5, V, 3.0, seed=S + V, reduction="mean", offset=1)
