@@ -52,11 +52,21 @@
 extern "C" {
 #endif
 
+/* Compiled as C++, the enums below have int as their underlying type, so a
+ * caller's out-of-range code is a value the checks can reject (without it,
+ * C++ leaves an enum holding a value outside its enumerators' range
+ * undefined); compiled as C they are plain enums, as always. */
+#ifdef __cplusplus
+#define CE_INT_ENUM : int
+#else
+#define CE_INT_ENUM
+#endif
+
 /* Storage type of the logits (and of the in-place gradient). */
-typedef enum { CE_F32 = 0, CE_F16 = 1, CE_BF16 = 2 } ce_dtype_t;
+typedef enum ce_dtype_e CE_INT_ENUM { CE_F32 = 0, CE_F16 = 1, CE_BF16 = 2 } ce_dtype_t;
 
 /* Reduction over rows. */
-typedef enum { CE_NONE = 0, CE_MEAN = 1, CE_SUM = 2 } ce_reduction_t;
+typedef enum ce_reduction_e CE_INT_ENUM { CE_NONE = 0, CE_MEAN = 1, CE_SUM = 2 } ce_reduction_t;
 
 /* Status codes: 0 is success, negative values are errors. */
 enum {

@@ -34,7 +34,9 @@ _DTYPE_CODE = {"f32": F32, "fp32": F32, "float32": F32,
 _RED_CODE = {"none": NONE, "mean": MEAN, "sum": SUM}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libce_oracle.so")
+# ORACLE_LIBRARY: another build of ce_oracle.c (the host-sanitizer test's)
+_LIB_OVERRIDE = os.environ.get("ORACLE_LIBRARY")
+_LIB_PATH = _LIB_OVERRIDE or os.path.join(_HERE, "libce_oracle.so")
 _lib = None
 
 _dp = ctypes.POINTER(ctypes.c_double)
@@ -46,8 +48,8 @@ def _load():
     if _lib is not None:
         return _lib
     src = os.path.join(_HERE, "ce_oracle.c")
-    if (not os.path.exists(_LIB_PATH)
-            or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src)):
+    if not _LIB_OVERRIDE and (not os.path.exists(_LIB_PATH)
+                              or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src)):
         from . import build as _b
         _b.build()
     lib = ctypes.CDLL(_LIB_PATH)

@@ -20,7 +20,8 @@ import os
 import threading
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libce.so")
+# CE_LIBRARY: another build of the library (the host-sanitizer test's)
+LIB_PATH = os.environ.get("CE_LIBRARY") or os.path.join(_PKG, "libce.so")
 
 CE_F32, CE_F16, CE_BF16 = 0, 1, 2
 CE_NONE, CE_MEAN, CE_SUM = 0, 1, 2
