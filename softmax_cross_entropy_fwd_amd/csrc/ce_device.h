@@ -1013,8 +1013,10 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
 // one-wavefront kernel on the same stream adds the slots in index order and
 // writes the result.  No atomics, fences or barriers: a unit leaves as soon
 // as its rows are done, and the order of every addition is fixed by the
-// launch shape.  (Measured on MI355X, the kernel boundary costs less than a
-// ticket taken by the last unit of the grid.)
+// launch shape.  (Measured on MI355X, for large inputs the kernel boundary
+// costs less than a ticket taken by the last unit of the grid; inputs of at
+// most 8 MiB, bound by the host's launches, take the ticket instead:
+// finish_in_kernel, below.)
 
 // Sum over the 64 lanes in a fixed butterfly order; every lane gets the sum.
 __device__ __forceinline__ double wave_sum_f64(double v)
