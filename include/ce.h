@@ -23,10 +23,11 @@
  * mean/sum is formed in fp64 in a fixed order, so results are bitwise
  * reproducible for a given device and shape.  Gradients are rounded to the
  * storage type with round-to-nearest-even (subnormals kept).  The final sum
- * of a mean/sum runs as a second one-wavefront kernel, or, for inputs of at
- * most 8 MiB outside graph capture, in the last workgroup of the same launch
- * (the same fixed order, the same bits): that takes one integer counter per
- * device and stream in the library's own device memory, zero between calls.
+ * of a mean/sum runs in the last workgroup of the launch that made the
+ * partials, or, during graph capture and for split rows, as a second
+ * one-wavefront kernel (the same fixed order, the same bits): the first form
+ * takes one integer counter per device and stream in the library's own
+ * device memory, zero between calls.
  *
  * Memory and ownership: every pointer is device memory owned by the caller.
  * The library allocates nothing, frees nothing and keeps no pointer after a

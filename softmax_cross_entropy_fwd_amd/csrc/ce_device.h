@@ -75,8 +75,8 @@ struct Params {
     float *stats;            // [M * S][2] slice (max, sum) with the target left out
     float *fix;              // [M * S] slice sums of p_j, j != t (backward from lse)
     float *rowx;             // [M] target logits, saved before any slice is overwritten
-    // non-null (rows kernels, mean or sum): the last workgroup to finish adds
-    // the partials and writes out[0] in this launch (finish_in_kernel)
+    // non-null (mean or sum over whole rows): the last workgroup to finish
+    // adds the partials and writes out[0] in this launch (finish_in_kernel)
     unsigned *ticket;
 };
 
@@ -1009,14 +1009,12 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
 
 // --------------------------------------------- end of kernel: mean / sum
 // Every unit (a wavefront of the rows kernels, a workgroup of the row-per-
-// workgroup kernels) stores its fp64 loss sum in its own slot; a second,
-// one-wavefront kernel on the same stream adds the slots in index order and
-// writes the result.  No atomics, fences or barriers: a unit leaves as soon
-// as its rows are done, and the order of every addition is fixed by the
-// launch shape.  (Measured on MI355X, for large inputs the kernel boundary
-// costs less than a ticket taken by the last unit of the grid; inputs of at
-// most 8 MiB, bound by the host's launches, take the ticket instead:
-// finish_in_kernel, below.)
+// workgroup kernels) stores its fp64 loss sum in its own slot, and the slots
+// are added in index order by one wavefront: the last workgroup of the same
+// launch (finish_in_kernel, below), or, where the launch has no counter (a
+// graph capture, split rows), a second one-wavefront kernel on the same
+// stream.  The order of every addition is fixed by the launch shape, so the
+// two forms give the same bits.
 
 // Sum over the 64 lanes in a fixed butterfly order; every lane gets the sum.
 __device__ __forceinline__ double wave_sum_f64(double v)
@@ -1048,25 +1046,52 @@ __device__ __forceinline__ double sum_partials(const double *partials, unsigned 
 
 // The final sum of a mean or sum in the launch that made the partials:
 // each workgroup, once all its wavefronts have published theirs, takes a
-// ticket (an integer counter, agent scope, acquire-release); the one that
-// takes the last adds all nunits partials with sum_partials, in the same
-// fixed order as the second-kernel form, so the result is that form's bit
-// for bit, and puts the counter back to zero for the next launch.
+// ticket (an integer counter); the one that takes the last adds all nunits
+// partials in the same fixed order as the second-kernel form, so the result
+// is that form's bit for bit, and puts the counter back to zero for the
+// next launch.  No fences: each partial is stored through to memory (a
+// system-scope store that no cache keeps) and waited for before the
+// workgroup's ticket, and the last workgroup reads the partials the same
+// way (system-scope loads that miss every cache); an agent-scope release
+// would write back the whole L2 instead.
+__device__ __forceinline__ void publish_partial(const Params &p, unsigned idx, double v)
+{
+    if (p.ticket)
+        __hip_atomic_store(&p.partials[idx], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    else
+        p.partials[idx] = v;
+}
+
 __device__ __forceinline__ void finish_in_kernel(const Params &p, unsigned nunits, int lane,
                                                  int wave)
 {
     __shared__ unsigned s_last;
-    __syncthreads();   // the workgroup's partials are written
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's partial is in memory
+    __syncthreads();                                    // ... and every wavefront's
     if (threadIdx.x == 0) {
         const unsigned prev =
-            __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = prev + 1 == gridDim.x ? 1u : 0u;
     }
     __syncthreads();
     if (!s_last || wave != 0)
         return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the other workgroups' partials
-    const double total = sum_partials(p.partials, nunits, lane);
+    // sum_partials' order, with loads from memory
+    double acc = 0.0;
+    for (unsigned base = 0; base < nunits; base += 64 * 8) {
+        double v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const unsigned i = base + (unsigned)lane + 64u * j;
+            v[j] = i < nunits ? __hip_atomic_load(&p.partials[i], __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_SYSTEM)
+                              : 0.0;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            acc += v[j];
+    }
+    const double total = wave_sum_f64(acc);
     if (lane == 0) {
         p.out[0] = (float)(total * p.out_scale);
         __hip_atomic_store(p.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1171,7 +1196,7 @@ __global__ void __launch_bounds__(NW * 64) rows_kernel(Params p)
     // lanes other than each group's first hold 0
     const double wave_total = wave_sum_f64(acc);
     if (lane == 0)
-        p.partials[blockIdx.x * nwaves + wave] = wave_total;
+        publish_partial(p, blockIdx.x * nwaves + wave, wave_total);
     if (p.ticket)
         finish_in_kernel(p, (unsigned)(gridDim.x * nwaves), lane, wave);
 }
@@ -1232,7 +1257,9 @@ wg_kernel(Params p)
     }
     // thread 0 holds the workgroup's sum
     if (p.reduction != RED_NONE && threadIdx.x == 0)
-        p.partials[blockIdx.x] = acc;
+        publish_partial(p, blockIdx.x, acc);
+    if (p.ticket)
+        finish_in_kernel(p, gridDim.x, threadIdx.x & 63, threadIdx.x >> 6);
 }
 
 // ---- one row per wavefront, streamed in chunks ------------------------------
@@ -1312,7 +1339,9 @@ __global__ void __launch_bounds__(256) wstream_kernel(Params p)
         return;
     // lane 0 holds the wavefront's sum
     if (lane == 0)
-        p.partials[blockIdx.x * nwaves + wave] = acc;
+        publish_partial(p, blockIdx.x * nwaves + wave, acc);
+    if (p.ticket)
+        finish_in_kernel(p, (unsigned)(gridDim.x * nwaves), lane, wave);
 }
 
 // ---- one row per workgroup, streamed in chunks ---------------------------------
@@ -1485,7 +1514,9 @@ __global__ void __launch_bounds__(W * 64) stream_kernel(Params p)
         __syncthreads();   // s_xt and the LDS partials are reused by the next row
     }
     if (p.reduction != RED_NONE && tid == 0)
-        p.partials[blockIdx.x] = acc;
+        publish_partial(p, blockIdx.x, acc);
+    if (p.ticket)
+        finish_in_kernel(p, gridDim.x, tid & 63, tid >> 6);
 }
 
 

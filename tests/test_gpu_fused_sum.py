@@ -1,6 +1,7 @@
-"""The final sum of a mean or sum done in the rows kernel's own launch (the
-last workgroup adds the partials; inputs up to 8 MiB, outside graph
-capture): bit for bit the two-launch result, which a graph capture keeps,
+"""The final sum of a mean or sum done in the kernel's own launch (the last
+workgroup adds the partials; whole rows, outside graph capture): bit for
+bit the two-launch result, which a graph capture keeps, for every kernel
+shape (register rows, one row per wavefront, streamed rows, register tiles),
 call after call (every launch puts its counter back to zero), and with two
 streams running at once (each stream has its own counter)."""
 import pytest
@@ -44,13 +45,18 @@ def two_launch(ce, fn, *args, **kw):
     return res
 
 
+# forward / fused backward kernel shapes: register rows / register rows;
+# rows / rows; rows / rows; rows / rows; streamed / streamed; one row per
+# wavefront / streamed; streamed / 16-wave tile; streamed / two-part tile;
+# streamed / 16-wave tile
 @pytest.mark.parametrize("dtype,M,V", [("f32", 64, 1000), ("bf16", 1, 4096), ("f16", 300, 777),
-                                      ("f32", 2048, 1000), ("bf16", 129, 16384)])
+                                      ("f32", 2048, 1000), ("bf16", 129, 16384),
+                                      ("f32", 500, 5000), ("f32", 256, 16384),
+                                      ("f16", 200, 40000), ("bf16", 300, 131072)])
 def test_fused_sum_matches_two_launch_form(ce, dtype, M, V):
     import torch
     say("fused sum", dtype, M, V)
     x, t = inputs.make(dtype, M, V, 4.0, seed=M + V, device="cuda:0")
-    assert M * V * x.element_size() <= 8 << 20
     for red in ("mean", "sum"):
         nb = ce.ce_workspace_bytes(M, V, CODES[dtype], red)
         ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
@@ -96,3 +102,19 @@ def test_fused_sum_on_two_streams(ce):
     torch.cuda.synchronize()
     assert all(torch.equal(bits(o), ref1) for o in outs1)
     assert all(torch.equal(bits(o), ref2) for o in outs2)
+
+
+@pytest.mark.parametrize("dtype,M,V", [("f32", 32768, 4096), ("bf16", 2048, 50257)])
+def test_fused_sum_threshold_override(ce, tuning, dtype, M, V):
+    """CE_FUSE_MAX_BYTES moves the size limit of the in-launch final sum: a
+    large input finishes its mean in one launch with the two-launch form's
+    bits (about 2048 workgroups adding their partials)."""
+    import torch
+    say("fused sum, large", dtype, M, V)
+    x, t = inputs.make(dtype, M, V, 4.0, seed=M ^ V, device="cuda:0")
+    tuning.setenv("CE_FUSE_MAX_BYTES", "0")
+    ref = bits(ce.ce_fwd(x, t, "mean"))
+    tuning.setenv("CE_FUSE_MAX_BYTES", str(1 << 40))
+    outs = [ce.ce_fwd(x, t, "mean") for _ in range(20)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(bits(o), ref) for o in outs), [o.item() for o in outs]
