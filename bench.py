@@ -205,9 +205,14 @@ def summarize_util(csv_path, workload, op, reduction, kernel_prefix, command):
 
 
 def time_workload(ce, workload, op, reduction, steps, warmup, log, M=None, V=None,
-                  cpu_sample=False):
+                  cpu_sample=False, min_warm_ms=0.0):
     """One operation on one workload (M and V may override its sizes, e.g. a
-    shard's shape), timed per launch with HIP events on the launch stream."""
+    shard's shape), timed per launch with HIP events on the launch stream.
+    Warm-up: `warmup` calls, continued until they have taken `min_warm_ms`
+    (the secondary lines follow seconds of host-side work, after which the
+    device takes some milliseconds to come back to its steady rate: measured,
+    the stress rows' forward ran 160-180 us per call for its first ~60 calls
+    after a 0.5 s pause, 136 us from about the 100th on)."""
     import torch
     from softmax_cross_entropy_fwd_amd import inputs
     c = inputs.CONFIGS[workload]
@@ -239,10 +244,15 @@ def time_workload(ce, workload, op, reduction, steps, warmup, log, M=None, V=Non
     stream = torch.cuda.current_stream(dev)
     plan = ce.ce_plan_describe(M, V, {"f32": 0, "f16": 1, "bf16": 2}[dtype], reduction, op=code)
     log("workload %s op %s reduction %s plan %s buffers %d" % (workload, op, reduction, plan, nbuf))
-    for i in range(warmup):
+    t_warm = time.perf_counter()
+    i = 0
+    while i < warmup or (time.perf_counter() - t_warm) * 1e3 < min_warm_ms:
         if pristine is not None:
             xs[0].copy_(pristine)
         launch(xs[i % nbuf])
+        i += 1
+        if min_warm_ms and i % 8 == 0:
+            torch.cuda.synchronize()   # so that the host clock follows the device
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -289,6 +299,8 @@ def time_workload(ce, workload, op, reduction, steps, warmup, log, M=None, V=Non
 
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+# warm-up of each secondary line, in milliseconds of calls (time_workload)
+EXTRA_WARM_MS = 50.0
 
 
 def time_linear(ce, op, steps, warmup, log, chunk=0):
@@ -749,20 +761,25 @@ def main():
                         ("lmhead", "softmax"), ("classifier", "bwd"), ("classifier", "softmax"),
                         ("stress", "fwd"), ("stress", "fwd_bwd"), ("skinny", "fwd")):
             also.append(time_workload(ce, wl, eop, "mean", max(20, args.steps // 5),
-                                      max(3, args.warmup // 5), log, cpu_sample=not args.no_cpu))
+                                      max(3, args.warmup // 5), log, cpu_sample=not args.no_cpu,
+                                      min_warm_ms=EXTRA_WARM_MS))
         # the skinny workload's per-row losses (reduction none: one kernel, M
         # fp32 losses written)
         also.append(time_workload(ce, "skinny", "fwd", "none", max(20, args.steps // 5),
-                                  max(3, args.warmup // 5), log, cpu_sample=not args.no_cpu))
+                                  max(3, args.warmup // 5), log, cpu_sample=not args.no_cpu,
+                                  min_warm_ms=EXTRA_WARM_MS))
         # the tiny workload: launch-bound, microseconds per call
         also.append(time_tiny(ce, log, cpu_sample=not args.no_cpu))
         also.append(time_tiny(ce, log, reduction="none", cpu_sample=not args.no_cpu))
         if args.extra_shapes:
             # one GPU's share of a sharded LM head: rows (M / 8) and vocabulary
             # (V / 8)
-            also.append(time_workload(ce, "lmhead", "fwd", "mean", 50, 5, log, M=2048))
-            also.append(time_workload(ce, "lmhead", "fwd_bwd", "mean", 50, 5, log, M=2048))
-            also.append(time_workload(ce, "lmhead", "fwd_lse", "none", 50, 5, log, V=16384))
+            also.append(time_workload(ce, "lmhead", "fwd", "mean", 50, 5, log, M=2048,
+                                      min_warm_ms=EXTRA_WARM_MS))
+            also.append(time_workload(ce, "lmhead", "fwd_bwd", "mean", 50, 5, log, M=2048,
+                                      min_warm_ms=EXTRA_WARM_MS))
+            also.append(time_workload(ce, "lmhead", "fwd_lse", "none", 50, 5, log, V=16384,
+                                      min_warm_ms=EXTRA_WARM_MS))
         lin_cpu = None if args.no_cpu else linear_cpu_baseline(log, rows=1)
         for lop in ("fwd", "fwd_bwd"):
             also.append(time_linear(ce, lop, max(5, args.steps // 20), 2, log))
