@@ -206,6 +206,36 @@ def test_epilogue_plan_table(ce, dtype):
                       offset=1)
 
 
+# Both row orders of the rows and workgroup kernels (the grid striding over
+# the rows, or a contiguous band of rows per workgroup), for the forward with
+# one row per wavefront (blocked by default), a narrower-row forward, the
+# fused backward and a workgroup tile.  Batches that leave some workgroups'
+# bands empty (M below the grid's rows per pass) and ragged last bands.
+@pytest.mark.parametrize("row_map", ["interleaved", "blocked"])
+def test_row_maps(ce, tuning, row_map):
+    tuning.setenv("CE_ROW_MAP", row_map)
+    cases = [("f32", 1000, 4096, "fwd"), ("f32", 3, 4096, "fwd"), ("bf16", 777, 3000, "fwd"),
+             ("f16", 5000, 128, "fwd"), ("f32", 2049, 1000, "fwd_bwd"),
+             ("bf16", 300, 32768, "fwd_bwd")]
+    for dtype, M, V, op in cases:
+        code = {"f32": 0, "f16": 1, "bf16": 2}[dtype]
+        plan = ce.ce_plan_describe(M, V, code, "mean",
+                                   op=ce.CE_OP_FWD if op == "fwd" else ce.CE_OP_FWD_BWD)
+        assert (" blocked " in plan) == (row_map == "blocked"), plan
+        for red in ("mean", "none"):
+            run_and_check(ce, dtype, M, V, 3.0, seed=M + V, reduction=red, op=op,
+                          offset=0 if red == "mean" else 1)
+
+
+def test_default_row_map(ce):
+    # one row per wavefront in the forward: bands; everything else interleaved
+    assert " blocked " in ce.ce_plan_describe(32768, 4096, 0, "mean")
+    assert " blocked " in ce.ce_plan_describe(100, 2000, 2, "none")
+    assert " blocked " not in ce.ce_plan_describe(1048576, 128, 0, "mean")
+    assert " blocked " not in ce.ce_plan_describe(32768, 4096, 0, "mean", op=ce.CE_OP_FWD_BWD)
+    assert " blocked " not in ce.ce_plan_describe(16384, 131072, 2, "mean")
+
+
 # ------------------------------------------------------------------ edge cases
 
 def test_empty_batch(ce):
