@@ -422,13 +422,28 @@ int make_plan(int64_t M, int64_t V, int dtype, int op, bool aligned, Plan *plan)
                           : kind == cek::KIND_WSTREAM ? plan->k.block / 64
                                                       : 1;
     int64_t needed = (M + rows_per_wg - 1) / rows_per_wg;
-    // Few deep waves beat many shallow ones here (measured): each wave keeps
-    // a whole row of loads in flight, so the rows kernel runs 4 waves per CU
-    // and the workgroup kernels 16.
+    // Wavefronts per CU.  The rows kernels keep K vectors (K KiB) per
+    // wavefront in flight, one row ahead; enough wavefronts to hold about
+    // 64 KiB per CU in flight, or 128 KiB where each row is folded before
+    // its epilogue (softmax, fused backward) or is 16-bit (twice the VALU
+    // work per byte), between 4 and 16.  Measured on MI355X: fp32 4096-wide
+    // forward 85.7 us at 4 wavefronts against 89.8 at 8; its softmax 210 ->
+    // 200 us at 8; bf16 2000-wide forward 191 -> 100 us at 16; fp32
+    // 2000-wide forward 125 -> 90 us at 8.  Two-buffer rows kernels (narrow
+    // rows, two rows per lane in flight) keep 4: 8 cost 2-10 %.  The
+    // workgroup kernels run 16.
     const int waves_per_wg = plan->k.block / 64;
     const int tw = tuning().waves_per_cu;
+    int rows_waves = 4;
+    if (kind == cek::KIND_ROWS && plan->nbuf == 1) {
+        const bool folded_epilogue =
+            op == cek::EPI_GRAD || op == cek::EPI_SOFTMAX || op == cek::EPI_LOGSOFTMAX;
+        const int target_kib = (dtype != CE_F32 || folded_epilogue) ? 128 : 64;
+        rows_waves = target_kib / b;
+        rows_waves = rows_waves < 4 ? 4 : rows_waves > 16 ? 16 : rows_waves;
+    }
     const int target_waves = tw > 0                   ? tw
-                             : kind == cek::KIND_ROWS ? 4
+                             : kind == cek::KIND_ROWS ? rows_waves
                              : waves > 0              ? waves
                                                       : 16;
     int wg_per_cu = target_waves / waves_per_wg;
@@ -450,10 +465,12 @@ int make_plan(int64_t M, int64_t V, int dtype, int op, bool aligned, Plan *plan)
         plan->grid = 1;
     // Row order: the whole grid strides over the rows, or each workgroup
     // walks its own contiguous band.  Bands measured faster for the forward
-    // with one row per wavefront (32768 x 4096 fp32: 84.7-85.3 against
-    // 85.6-86.2 us, six alternating pairs on two boxes) and slower elsewhere
-    // (1048576 x 128 fp32 forward +3 %, LM head fused backward +1.4 %).
-    plan->blocked = kind == cek::KIND_ROWS && a == 64 && op == cek::EPI_NONE;
+    // with one row per wavefront at 4 wavefronts per CU (32768 x 4096 fp32:
+    // 84.7-85.3 against 85.6-86.2 us, alternating pairs on five boxes) and
+    // slower elsewhere (the same forward with 8 or 16 wavefronts per CU
+    // +1 %, 1048576 x 128 fp32 forward +3 %, LM head fused backward +1.4 %).
+    plan->blocked = kind == cek::KIND_ROWS && a == 64 && op == cek::EPI_NONE &&
+                    wg_per_cu * waves_per_wg == 4;
     if (tuning().row_map && (kind == cek::KIND_ROWS || kind == cek::KIND_WG || kind == cek::KIND_WG2))
         plan->blocked = tuning().row_map == 2;   // the kernels with a choice of row order
     return CE_OK;

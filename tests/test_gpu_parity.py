@@ -228,9 +228,12 @@ def test_row_maps(ce, tuning, row_map):
 
 
 def test_default_row_map(ce):
-    # one row per wavefront in the forward: bands; everything else interleaved
+    # one row per wavefront in the forward at 4 wavefronts per CU: bands;
+    # everything else interleaved
     assert " blocked " in ce.ce_plan_describe(32768, 4096, 0, "mean")
-    assert " blocked " in ce.ce_plan_describe(100, 2000, 2, "none")
+    assert " blocked " in ce.ce_plan_describe(100, 4096, 0, "none")
+    assert " blocked " not in ce.ce_plan_describe(65536, 2000, 0, "mean")
+    assert " blocked " not in ce.ce_plan_describe(100, 2000, 2, "none")
     assert " blocked " not in ce.ce_plan_describe(1048576, 128, 0, "mean")
     assert " blocked " not in ce.ce_plan_describe(32768, 4096, 0, "mean", op=ce.CE_OP_FWD_BWD)
     assert " blocked " not in ce.ce_plan_describe(16384, 131072, 2, "mean")
