@@ -657,12 +657,13 @@ __device__ __forceinline__ float load_logit(const Params &p, int64_t row, int64_
 // vector is folded.  Kept in program order, the waits came per vector and the
 // classifier forward ran 2-3 % slower, so the order is left to the compiler.)
 template <int DT, int K, int STRIDE, bool EXACT, bool NTL = false>
-__device__ __forceinline__ void issue_loads(Vec (&raw)[K], const Vec *xrow, int lidx, int nvec)
+__device__ __forceinline__ void issue_loads(Vec (&raw)[K], const Vec *xrow, int lidx, int nvec,
+                                            bool past_end = false)
 {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int v = lidx + STRIDE * k;
-        raw[k] = ldv<NTL>(&xrow[(EXACT || v < nvec) ? v : nvec - 1]);
+        raw[k] = ldv<NTL>(&xrow[past_end ? 0 : (EXACT || v < nvec) ? v : nvec - 1]);
     }
 }
 
@@ -808,18 +809,40 @@ __device__ __forceinline__ float row_scale(const Params &p, int64_t row)
 struct RowRef {
     int64_t row;     // the row held (clamped to a real row for idle lanes)
     bool active;     // this lane's row is a real row
+    bool past_end;   // no row follows (wave-uniform): its loads read one vector
     int64_t t;       // its target, -1 for idle lanes
     float c;         // gradient scale of the row (gradient epilogues)
     float lse;       // given log-sum-exp (EPI_LSE_GRAD)
     Window w;
 };
 
+// The "next row" after a wavefront's or workgroup's last: the last row again,
+// marked so that the pipeline's loads of it (kept unconditional) all read the
+// window's first vector -- one cache line per load instead of the whole row
+// fetched again (a row per wavefront at the end of every launch: 16 MB for
+// the 32768 x 4096 fp32 forward, 64 MB for the LM head's fused backward).
+__device__ __forceinline__ RowRef past_end(const RowRef &last)
+{
+    RowRef r = last;
+    r.past_end = true;
+    return r;
+}
+
+// Window vector v of `next` for lane loads (clamped to the window; the first
+// vector past the end).
+template <bool EXACT>
+__device__ __forceinline__ int next_vec(const RowRef &next, int v)
+{
+    return next.past_end ? 0 : (EXACT || v < next.w.nvec) ? v : next.w.nvec - 1;
+}
+
 // One pipeline step on a row held in registers (K vectors per lane, lane lidx
 // of STRIDE lanes): the loads of `next` are issued as soon as the registers
 // are free (during the sum pass for the forward; right after each gradient
 // vector is stored for the fused backward), so memory stays busy while this
-// row is reduced and written.  After the last row, `next` is the same row
-// again (a cache hit, never used), which keeps the loads unconditional.
+// row is reduced and written.  After the last row, `next` is that row
+// marked past_end: its loads (kept unconditional) all read the window's first
+// vector, and their values are never used.
 // Returns the row's loss (same in every lane).
 template <int DT, int K, int STRIDE, int OP, bool EXACT, class Red>
 __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&raw)[K],
@@ -947,8 +970,7 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
             s_run = valid ? s_new : s_run;
             m_run = valid ? mn : m_run;
             if constexpr (!BWD) {
-                raw[k] = ldv<nt_fwd_loads<OP, STRIDE>()>(
-                    &next.w.xrow[(EXACT || v < next.w.nvec) ? v : next.w.nvec - 1]);
+                raw[k] = ldv<nt_fwd_loads<OP, STRIDE>()>(&next.w.xrow[next_vec<EXACT>(next, v)]);
                 // keep each load after the use of the register it refills
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -999,7 +1021,7 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
             }
             if (cur.active && vec_valid<STRIDE, EXACT>(k, kfull, lidx, w.nvec))
                 store_grad<DT>(w.yrow, v, g, w.head, p.V, EXACT || p.aligned);
-            raw[k] = ldv(&next.w.xrow[(EXACT || v < next.w.nvec) ? v : next.w.nvec - 1]);
+            raw[k] = ldv(&next.w.xrow[next_vec<EXACT>(next, v)]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -1106,6 +1128,7 @@ __device__ __forceinline__ RowRef row_ref(const Params &p, int64_t row)
 {
     RowRef r;
     r.active = row < p.M;
+    r.past_end = false;
     r.row = r.active ? row : 0;   // idle lanes redo row 0, store nothing, drop the loss
     // The per-row scalars are read here, a step before they are used and
     // before the row's own loads: vector loads retire in order, so a late
@@ -1161,7 +1184,7 @@ __global__ void __launch_bounds__(NW * 64) rows_kernel(Params p)
     };
     // the group's row in the wave's row block `base`, or fallback past the end
     auto ref_at = [&](int64_t base, const RowRef &fallback) {
-        return base < row_end ? row_ref<DT, OP>(p, base + lane / G) : fallback;
+        return base < row_end ? row_ref<DT, OP>(p, base + lane / G) : past_end(fallback);
     };
     GroupRed<G> red;
     if (rb < row_end) {
@@ -1177,7 +1200,8 @@ __global__ void __launch_bounds__(NW * 64) rows_kernel(Params p)
         } else {
             RowRef b = ref_at(rb + row_step, a);
             Vec rbuf[K];
-            issue_loads<DT, K, G, EXACT, nt_fwd_loads<OP, G>()>(rbuf, b.w.xrow, lig, b.w.nvec);
+            issue_loads<DT, K, G, EXACT, nt_fwd_loads<OP, G>()>(rbuf, b.w.xrow, lig, b.w.nvec,
+                                                                b.past_end);
             for (; rb < row_end; rb += 2 * row_step) {
                 const RowRef an = ref_at(rb + 2 * row_step, a);
                 record(a, pipeline_step<DT, K, G, OP, EXACT>(p, red, ra, a, an, lig, kfull));
@@ -1252,7 +1276,7 @@ wg_kernel(Params p)
                                                               cur.w.nvec);
         for (; row < row_end; row += row_step) {
             const bool has_next = row + row_step < row_end;
-            const RowRef next = has_next ? row_ref<DT, OP>(p, row + row_step) : cur;
+            const RowRef next = has_next ? row_ref<DT, OP>(p, row + row_step) : past_end(cur);
             const float loss =
                 pipeline_step<DT, K, NT, OP, EXACT>(p, red, raw, cur, next, threadIdx.x, kfull);
             if (threadIdx.x == 0) {
