@@ -10,8 +10,9 @@ the classifier workload (fp32 [32768, 4096], forward, mean): algorithmic HBM
 GB/s = bytes the method must move / kernel time.  The same line carries:
 
   roofline      the kernel's achieved GB/s (algorithmic bytes per launch over
-                the average launch duration, from HIP events on the launch
-                stream) against MI355X's 8 TB/s, and the HBM traffic counted by
+                the average launch duration: the K launches run back to back
+                between one pair of HIP events on the launch stream) against
+                MI355X's 8 TB/s, and the HBM traffic counted by
                 rocprofv3 (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy)
                 when a summary taken on the current kernel source is committed
                 under profiles/;
@@ -31,7 +32,10 @@ GB/s = bytes the method must move / kernel time.  The same line carries:
 
 Inputs rotate over enough buffers (>= 1 GiB in total) that no launch finds its
 rows in the 256 MB last-level cache; the in-place backward restores its logits
-from a pristine copy between steps, outside the timed launch.
+from a pristine copy between steps, outside the timed launch, so its lines
+are timed launch by launch, each between its own pair of events (which adds
+about 2 us per launch).  Every line also reports that per-launch spread
+(launch_ms_*).
 """
 import argparse
 import hashlib
@@ -207,7 +211,9 @@ def summarize_util(csv_path, workload, op, reduction, kernel_prefix, command):
 def time_workload(ce, workload, op, reduction, steps, warmup, log, M=None, V=None,
                   cpu_sample=False, min_warm_ms=0.0):
     """One operation on one workload (M and V may override its sizes, e.g. a
-    shard's shape), timed per launch with HIP events on the launch stream.
+    shard's shape), timed with HIP events on the launch stream: around all
+    `steps` launches at once, or, for the in-place backward (whose logits are
+    restored between launches), around each launch.
     Warm-up: `warmup` calls, continued until they have taken `min_warm_ms`
     (the secondary lines follow seconds of host-side work, after which the
     device takes some milliseconds to come back to its steady rate: measured,
@@ -254,10 +260,28 @@ def time_workload(ce, workload, op, reduction, steps, warmup, log, M=None, V=Non
         if min_warm_ms and i % 8 == 0:
             torch.cuda.synchronize()   # so that the host clock follows the device
     torch.cuda.synchronize()
+    region_ms = None
+    if pristine is None:
+        # The timed region: `steps` launches back to back between one pair of
+        # HIP events on the launch stream, synchronized on both sides -- the
+        # whole job's time per step.
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        r0.record(stream)
+        for i in range(steps):
+            launch(xs[i % nbuf])
+        r1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        region_ms = r0.elapsed_time(r1) / steps
+    # The same launches again, each between its own pair of events (the
+    # spread per launch; the events' own packets add about 2 us to each).
+    # The in-place backward restores its logits before each launch, outside
+    # the launch's events: for it this pass is the timed one.
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
-    w0 = time.perf_counter()
+    w1 = time.perf_counter()
     for i in range(steps):
         if pristine is not None:
             xs[0].copy_(pristine)
@@ -265,9 +289,11 @@ def time_workload(ce, workload, op, reduction, steps, warmup, log, M=None, V=Non
         launch(xs[i % nbuf])
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
+    if pristine is not None:
+        wall = time.perf_counter() - w1
     ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    avg_ms = sum(ms) / len(ms)
+    launch_avg = sum(ms) / len(ms)
+    avg_ms = region_ms if region_ms is not None else launch_avg
     med_ms = sorted(ms)[len(ms) // 2]
     ab = alg_bytes(M, V, dtype, op, reduction)
     has_loss = op in ("fwd", "fwd_lse", "fwd_bwd") and reduction != "none"
@@ -275,7 +301,9 @@ def time_workload(ce, workload, op, reduction, steps, warmup, log, M=None, V=Non
         "workload": workload if (M, V) == (c["M"], c["V"]) else "%s_%dx%d" % (workload, M, V),
         "op": op, "reduction": reduction, "M": M, "V": V,
         "storage": dtype, "plan": plan,
-        "kernel_ms_avg": avg_ms, "kernel_ms_median": med_ms, "kernel_ms_min": min(ms),
+        "kernel_ms_avg": avg_ms,
+        "timing": "region" if region_ms is not None else "per launch",
+        "launch_ms_avg": launch_avg, "launch_ms_median": med_ms, "launch_ms_min": min(ms),
         "wall_ms_per_step": 1e3 * wall / steps,
         "alg_bytes_per_launch": ab,
         "alg_GBps": ab / (avg_ms * 1e-3) / 1e9,
@@ -402,7 +430,19 @@ def measure_ceilings(log, size_bytes=None):
                      for g, u, blk in ((1024, 8, 256), (512, 4, 1024), (2048, 8, 256)))
     read_tiles_4g = max(nb / best(lambda: read_tiles(buf.data_ptr(), nb, g, k, nt)) / 1e6
                         for g, k, nt in tile_shapes)
-    read = max(read_plain, read_tiles_4g)
+    # the streamed forward's pattern: whole 256 KB rows per workgroup, read in
+    # chunks, one to four workgroups per CU
+    lib.probe_read_rows.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    read_rows_4g = max(nb / best(lambda: lib.probe_read_rows(
+        buf.data_ptr(), nb, 256 << 10, w, k, g, tiles_out.data_ptr(), st.cuda_stream)) / 1e6
+        for w, k, g in ((16, 4, 256), (16, 4, 512), (8, 4, 512), (8, 4, 1024), (4, 4, 1024),
+                        (16, 8, 256), (8, 8, 512)))
+    # torch's own reduction over the same bytes (bf16 elements summed)
+    xr = buf.view(torch.bfloat16)
+    read_torch = nb / best(lambda: xr.sum(dtype=torch.float32)) / 1e6
+    del xr
+    read = max(read_plain, read_tiles_4g, read_rows_4g, read_torch)
     read_at_size = None
     if size_bytes and size_bytes % 16 == 0 and size_bytes <= nb // 2:
         flip = [0]
@@ -445,10 +485,11 @@ def measure_ceilings(log, size_bytes=None):
     copy_torch = 2 * (nb // 2) / best(lambda: dst_b.copy_(half_b)) / 1e6
     del buf, out, xb, tiles_out, half_b, dst_b
     torch.cuda.empty_cache()
-    log("measured ceilings: read %.0f GB/s (plain %.0f, rows pattern %.0f), copy %.0f GB/s "
-        "(read + write; torch's copy %.0f), in place %.0f GB/s (rows in registers; torch's "
-        "in-place multiply %.0f GB/s)" % (read, read_plain, read_tiles_4g, copy, copy_torch,
-                                         inplace, inplace_torch))
+    log("measured ceilings: read %.0f GB/s (plain %.0f, rows pattern %.0f, streamed rows %.0f, "
+        "torch's sum %.0f), copy %.0f GB/s (read + write; torch's copy %.0f), in place %.0f GB/s "
+        "(rows in registers; torch's in-place multiply %.0f GB/s)" % (
+            read, read_plain, read_tiles_4g, read_rows_4g, read_torch, copy, copy_torch, inplace,
+            inplace_torch))
     if read_at_size is not None:
         log("read over the headline workload's %d bytes: %.0f GB/s" % (size_bytes, read_at_size))
     # the best read and the best read + write anything measured here reached:
@@ -456,15 +497,17 @@ def measure_ceilings(log, size_bytes=None):
     # torch's kernels all move one read and one write per element)
     best_rw = max(copy, copy_torch, inplace, inplace_torch)
     return {"read_GBps": round(read, 1), "read_plain_GBps": round(read_plain, 1),
-            "read_rows_pattern_GBps": round(read_tiles_4g, 1), "copy_GBps": round(copy, 1),
+            "read_rows_pattern_GBps": round(read_tiles_4g, 1),
+            "read_streamed_rows_GBps": round(read_rows_4g, 1),
+            "read_torch_sum_GBps": round(read_torch, 1), "copy_GBps": round(copy, 1),
             "copy_torch_GBps": round(copy_torch, 1),
             "read_at_size_GBps": None if read_at_size is None else round(read_at_size, 1),
             "inplace_rows_GBps": round(inplace, 1), "inplace_torch_GBps": round(inplace_torch, 1),
             "best_read_GBps": round(read, 1), "best_read_write_GBps": round(best_rw, 1),
             "how": "probe/bw_probe.hip over 4 GiB (copy: 2 GiB each way; in place: 4 GiB "
                    "rewritten), best launch shape; the reads also with the rows kernel's tile "
-                   "pattern over persistent grids; torch: bf16 mul_(1.0) in place and copy_ "
-                   "over the same bytes"}
+                   "pattern over persistent grids and the streamed kernel's whole-row chunks; "
+                   "torch: bf16 sum, mul_(1.0) in place and copy_ over the same bytes"}
 
 
 def time_tiny(ce, log, calls=1000, cpu_sample=False, reduction="mean"):
@@ -683,7 +726,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # The headline's warm-up: about 40 ms of launches.  Measured on MI355X,
+    # the classifier forward's region time is 84.5-86 us per launch after 20
+    # warm-up launches and 82.6-82.8 us from the second 200-launch region on.
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="classifier")
     ap.add_argument("--op", default=None, choices=[None] + OPS,
                     help="for --workload lmhead_linear: fwd or fwd_bwd")
@@ -826,8 +872,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(head["alg_GBps"], 2), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(head["frac_of_peak"], 4),
                      "traffic": traffic},
-        "ms_per_step_median": round(head["kernel_ms_median"], 5),
-        "ms_per_step_min": round(head["kernel_ms_min"], 5),
+        "timing": head["timing"],
+        "launch_ms_avg": round(head["launch_ms_avg"], 5),
+        "launch_ms_median": round(head["launch_ms_median"], 5),
+        "launch_ms_min": round(head["launch_ms_min"], 5),
         "measured_ceiling": None if ceilings is None else dict(
             ceilings, frac_of_read=round(head["alg_GBps"] / ceilings["read_GBps"], 4),
             frac_of_read_at_size=(None if not ceilings.get("read_at_size_GBps") else

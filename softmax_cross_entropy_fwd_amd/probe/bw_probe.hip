@@ -96,6 +96,38 @@ __global__ void __launch_bounds__(256) read_tiles_kernel(const V4 *__restrict__ 
     out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = __uint_as_float(acc & 0x7fffffu);
 }
 
+// The read with the streamed forward's pattern: a W-wavefront workgroup
+// takes whole rows of row_vecs vectors (rows grid-strided) and reads each in
+// chunks of W*64*K vectors with non-temporal loads, every chunk's loads
+// issued together and folded before the next chunk's.
+template <int W, int K>
+__global__ void __launch_bounds__(W * 64) read_rows_kernel(const V4 *__restrict__ src,
+                                                          int64_t nrows, int64_t row_vecs,
+                                                          float *__restrict__ out)
+{
+    constexpr int64_t CH = (int64_t)W * 64 * K;
+    uint32_t acc = 0;
+    for (int64_t row = blockIdx.x; row < nrows; row += gridDim.x) {
+        const V4 *q = src + row * row_vecs;
+        for (int64_t c = 0; c < row_vecs; c += CH) {
+            V4 r[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                int64_t i = c + threadIdx.x + (int64_t)k * W * 64;
+                i = i < row_vecs ? i : row_vecs - 1;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    r[k].w[j] = __builtin_nontemporal_load(&q[i].w[j]);
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                acc ^= r[k].w[0] ^ r[k].w[1] ^ r[k].w[2] ^ r[k].w[3];
+        }
+    }
+    // one value per lane so the loads cannot be dropped
+    out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = __uint_as_float(acc & 0x7fffffu);
+}
+
 template <int U>
 __global__ void __launch_bounds__(256) copy_kernel(V4 *__restrict__ dst, const V4 *__restrict__ src,
                                                    int64_t nvec)
@@ -214,6 +246,27 @@ int probe_read_tiles(const void *src, int64_t bytes, int grid, int k, int nt, fl
         return hipGetLastError() == hipSuccess ? 0 : -6; }
     PROBE_TILES(8, false) PROBE_TILES(16, false) PROBE_TILES(8, true) PROBE_TILES(16, true)
 #undef PROBE_TILES
+    return -1;
+}
+
+// The streamed-forward pattern read (read_rows_kernel): rows of row_bytes (a
+// multiple of 16 dividing bytes), workgroups of W = 4, 8 or 16 wavefronts,
+// chunks of W*64*K vectors (K = 4 or 8); out needs W * 64 * grid floats.
+int probe_read_rows(const void *src, int64_t bytes, int64_t row_bytes, int W, int K, int grid,
+                    float *out, void *stream)
+{
+    if (!src || !out || grid < 1 || row_bytes < 16 || row_bytes % 16 || bytes % row_bytes)
+        return -1;
+    const int64_t nrows = bytes / row_bytes, row_vecs = row_bytes / 16;
+    hipStream_t s = (hipStream_t)stream;
+    const V4 *p = (const V4 *)src;
+#define PROBE_ROWS(WW, KK) \
+    if (W == WW && K == KK) { \
+        hipLaunchKernelGGL((read_rows_kernel<WW, KK>), dim3(grid), dim3(WW * 64), 0, s, p, nrows, \
+                           row_vecs, out); \
+        return hipGetLastError() == hipSuccess ? 0 : -6; }
+    PROBE_ROWS(16, 4) PROBE_ROWS(8, 4) PROBE_ROWS(4, 4) PROBE_ROWS(16, 8) PROBE_ROWS(8, 8)
+#undef PROBE_ROWS
     return -1;
 }
 
