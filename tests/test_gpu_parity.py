@@ -227,6 +227,23 @@ def test_row_maps(ce, tuning, row_map):
                           offset=0 if red == "mean" else 1)
 
 
+# Rows kernels whose grid holds 8 or 16 wavefronts per CU (the bytes each
+# keeps in flight set the count), at batches that take several grid-stride
+# passes, forward and fused backward, every element against the oracle.
+@pytest.mark.parametrize("dtype,M,V", [("bf16", 20000, 2000), ("f32", 12000, 2000),
+                                      ("f16", 6000, 4000)])
+def test_rows_kernels_full_grid(ce, dtype, M, V):
+    code = {"f32": 0, "f16": 1, "bf16": 2}[dtype]
+    for op, cop in (("fwd", ce.CE_OP_FWD), ("fwd_bwd", ce.CE_OP_FWD_BWD)):
+        plan = ce.ce_plan_describe(M, V, code, "mean", op=cop)
+        say("plan", op, plan)
+        grid = int(plan.split("grid=")[1].split()[0])
+        assert plan.startswith("rows:") and grid >= 512, plan
+        for red in ("mean", "none"):
+            run_and_check(ce, dtype, M, V, 3.0, seed=M + V + len(red), reduction=red, op=op,
+                          offset=0 if red == "mean" else 1)
+
+
 def test_default_row_map(ce):
     # one row per wavefront in the forward at 4 wavefronts per CU: bands;
     # everything else interleaved
