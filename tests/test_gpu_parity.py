@@ -244,6 +244,31 @@ def test_rows_kernels_full_grid(ce, dtype, M, V):
                           offset=0 if red == "mean" else 1)
 
 
+def test_rows_grid_rule(ce):
+    # wavefronts per CU of the rows kernels: ~64 KiB in flight per CU (K KiB
+    # each), ~128 KiB for 16-bit rows and for softmax / the fused backward,
+    # 4 to 16; two-buffer narrow rows 4 (the grids below are for 256 CUs and
+    # batches large enough to fill them)
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    cases = [  # (M, V, dtype code, op, wavefronts per CU)
+        (32768, 4096, 0, ce.CE_OP_FWD, 4),         # fp32, K = 16
+        (32768, 4096, 0, ce.CE_OP_SOFTMAX, 8),     # folded epilogue
+        (32768, 4096, 0, ce.CE_OP_FWD_BWD, 8),
+        (32768, 4096, 0, ce.CE_OP_BWD, 4),         # epilogue without a fold
+        (65536, 2000, 0, ce.CE_OP_FWD, 8),         # fp32, K = 8
+        (131072, 2000, 2, ce.CE_OP_FWD, 16),       # bf16, K = 4
+        (32768, 8000, 2, ce.CE_OP_FWD, 8),         # bf16, K = 16
+        (1048576, 128, 0, ce.CE_OP_FWD, 4),        # two buffers
+    ]
+    for M, V, code, op, waves in cases:
+        plan = ce.ce_plan_describe(M, V, code, "mean", op=op)
+        grid = int(plan.split("grid=")[1].split()[0])
+        block = int(plan.split("block=")[1].split()[0])
+        assert plan.startswith("rows:"), plan
+        assert grid * block // 64 == waves * cus, (M, V, code, op, plan)
+
+
 def test_default_row_map(ce):
     # one row per wavefront in the forward at 4 wavefronts per CU: bands;
     # everything else interleaved
