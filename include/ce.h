@@ -227,9 +227,11 @@ const char *ce_status_string(int status);
 /*
  * The library reads its tuning environment variables once, at its first
  * call: CE_FORCE_PLAN, CE_FORCE_SPLIT, CE_FORCE_NBUF, CE_WAVES_PER_CU,
- * CE_FORCE_GRID, CE_ROW_MAP (kernel mapping and launch overrides) and
- * CE_LINEAR_GEMM (ce_linear.h).  ce_tuning_reload reads them again; for
- * tuning and tests, and not while other threads call the library.
+ * CE_FORCE_GRID, CE_ROW_MAP=interleaved|blocked (kernel mapping and launch
+ * overrides), CE_FUSE_MAX_BYTES=N (the in-launch final sum of a mean or sum
+ * only for inputs of at most N bytes; 0: never) and CE_LINEAR_GEMM
+ * (ce_linear.h).  ce_tuning_reload reads them again; for tuning and tests,
+ * and not while other threads call the library.
  */
 void ce_tuning_reload(void);
 
