@@ -83,9 +83,18 @@ int pow2ceil(int64_t n)
 
 // Mapping and tile for a row of nvec 16-byte vectors (worst case over rows),
 // from measurements on MI355X:
-//  - rows up to 16 KB sit in the registers of 1..64 lanes (rows kernel);
-//  - longer rows are streamed for the forward: by one wavefront per row just
-//    past 16 KB, then by 4-, 8- or 16-wave workgroups as the rows grow;
+//  - the forward of rows of 257-1536 vectors (4-24 KB) streams each row
+//    through one wavefront in chunks of 64 K vectors (K = 8 up to 512
+//    vectors, then 4), 8 wavefronts per CU for fp32 rows and 12 for 16-bit
+//    ones.  Against the rows kernel's register tiles (region times, ~530 MB
+//    of logits): fp32 1500 wide 91 / 113 us, 2000 wide 80 / 85, 3000 wide
+//    118 / 176, 4000 wide 98 / 113, 4096 wide 82.4 / 83.2; bf16 4000 wide
+//    88 / 91, 6000 wide 98 / 131, 8000 wide 84 / 95, 8192 wide 86 / 89: a
+//    tile the row does not fill still takes a full tile's time;
+//  - shorter rows sit in the registers of 1..64 lanes (rows kernel), and so
+//    do the rows of the epilogues up to 16 KB;
+//  - longer rows are streamed for the forward by 4-, 8- or 16-wave
+//    workgroups as the rows grow;
 //  - the epilogues (fused backward, softmax, ...) past 16 KB: rows whose
 //    re-read stays in L2 while the CU's other rows stream are streamed
 //    twice (up to 48 KB by 8-wave workgroups, 32 waves per CU; up to 128 KB
@@ -105,7 +114,12 @@ void choose_shape(int64_t nvec, bool bwd, bool aligned, bool wide, int *kind, in
     *nbuf = 1;
     *waves = 0;
     *kind = cek::KIND_ROWS;
-    if (nvec <= 4) {
+    if (!bwd && nvec > 256 && nvec <= 1536) {
+        *kind = cek::KIND_WSTREAM;
+        *a = 1;
+        *b = nvec > 512 ? 4 : 8;
+        *waves = wide ? 12 : 8;
+    } else if (nvec <= 4) {
         *a = 1;
         *b = nvec <= 1 ? 1 : nvec <= 2 ? 2 : 4;
     } else if (nvec <= 8) {
@@ -165,11 +179,6 @@ void choose_shape(int64_t nvec, bool bwd, bool aligned, bool wide, int *kind, in
         *kind = cek::KIND_WG;
         *a = 16;
         *b = nvec <= 12288 ? 12 : 16;
-    } else if (!bwd && nvec <= 1536) {
-        // just past the register rows: one row per wavefront wastes least
-        *kind = cek::KIND_WSTREAM;
-        *a = 1;
-        *b = 4;
     } else {
         // chunks of W*64*4 vectors; more, smaller workgroups per CU until the
         // rows are long enough to keep a wide one busy (measured: 6283
@@ -463,14 +472,13 @@ int make_plan(int64_t M, int64_t V, int dtype, int op, bool aligned, Plan *plan)
     plan->grid = needed < cap ? needed : cap;
     if (plan->grid < 1)
         plan->grid = 1;
-    // Row order: the whole grid strides over the rows, or each workgroup
-    // walks its own contiguous band.  Bands measured faster for the forward
-    // with one row per wavefront at 4 wavefronts per CU (32768 x 4096 fp32:
-    // 84.7-85.3 against 85.6-86.2 us, alternating pairs on five boxes) and
-    // slower elsewhere (the same forward with 8 or 16 wavefronts per CU
-    // +1 %, 1048576 x 128 fp32 forward +3 %, LM head fused backward +1.4 %).
-    plan->blocked = kind == cek::KIND_ROWS && a == 64 && op == cek::EPI_NONE &&
-                    wg_per_cu * waves_per_wg == 4;
+    // Row order: the whole grid strides over the rows, or (CE_ROW_MAP=blocked,
+    // for tuning) each workgroup walks its own contiguous band.  Bands
+    // measured faster only for the 4096-wide fp32 forward in register rows
+    // (84.7-85.3 against 85.6-86.2 us), which now streams its rows instead;
+    // slower elsewhere (1048576 x 128 fp32 forward +3 %, LM head fused
+    // backward +1.4 %, 8 or 16 wavefronts per CU +1 %).
+    plan->blocked = false;
     if (tuning().row_map && (kind == cek::KIND_ROWS || kind == cek::KIND_WG || kind == cek::KIND_WG2))
         plan->blocked = tuning().row_map == 2;   // the kernels with a choice of row order
     return CE_OK;

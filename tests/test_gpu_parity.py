@@ -207,16 +207,16 @@ def test_epilogue_plan_table(ce, dtype):
 
 
 # Both row orders of the rows and workgroup kernels (the grid striding over
-# the rows, or a contiguous band of rows per workgroup), for the forward with
-# one row per wavefront (blocked by default), a narrower-row forward, the
+# the rows, or a contiguous band of rows per workgroup, CE_ROW_MAP), for
+# forwards in register rows (one row per wavefront, and narrower rows), the
 # fused backward and a workgroup tile.  Batches that leave some workgroups'
 # bands empty (M below the grid's rows per pass) and ragged last bands.
 @pytest.mark.parametrize("row_map", ["interleaved", "blocked"])
 def test_row_maps(ce, tuning, row_map):
     tuning.setenv("CE_ROW_MAP", row_map)
-    cases = [("f32", 1000, 4096, "fwd"), ("f32", 3, 4096, "fwd"), ("bf16", 777, 3000, "fwd"),
+    cases = [("f32", 1000, 1000, "fwd"), ("f32", 3, 1000, "fwd"), ("bf16", 777, 2000, "fwd"),
              ("f16", 5000, 128, "fwd"), ("f32", 2049, 1000, "fwd_bwd"),
-             ("bf16", 300, 32768, "fwd_bwd")]
+             ("f32", 1000, 4096, "fwd_bwd"), ("bf16", 300, 32768, "fwd_bwd")]
     for dtype, M, V, op in cases:
         code = {"f32": 0, "f16": 1, "bf16": 2}[dtype]
         plan = ce.ce_plan_describe(M, V, code, "mean",
@@ -227,18 +227,20 @@ def test_row_maps(ce, tuning, row_map):
                           offset=0 if red == "mean" else 1)
 
 
-# Rows kernels whose grid holds 8 or 16 wavefronts per CU (the bytes each
-# keeps in flight set the count), at batches that take several grid-stride
-# passes, forward and fused backward, every element against the oracle.
+# Grids of 8 to 16 wavefronts per CU (the bytes each keeps in flight set the
+# count), at batches that take several grid-stride passes: the forward (a
+# rows kernel, or for rows of 257-1536 vectors one wavefront per row in
+# chunks) and the fused backward, every element against the oracle.
 @pytest.mark.parametrize("dtype,M,V", [("bf16", 20000, 2000), ("f32", 12000, 2000),
-                                      ("f16", 6000, 4000)])
+                                      ("f16", 6000, 4000), ("f32", 9000, 3000)])
 def test_rows_kernels_full_grid(ce, dtype, M, V):
     code = {"f32": 0, "f16": 1, "bf16": 2}[dtype]
     for op, cop in (("fwd", ce.CE_OP_FWD), ("fwd_bwd", ce.CE_OP_FWD_BWD)):
         plan = ce.ce_plan_describe(M, V, code, "mean", op=cop)
         say("plan", op, plan)
         grid = int(plan.split("grid=")[1].split()[0])
-        assert plan.startswith("rows:") and grid >= 512, plan
+        kinds = ("rows:", "wstream:") if op == "fwd" else ("rows:",)
+        assert plan.startswith(kinds) and grid >= 512, plan
         for red in ("mean", "none"):
             run_and_check(ce, dtype, M, V, 3.0, seed=M + V + len(red), reduction=red, op=op,
                           offset=0 if red == "mean" else 1)
@@ -247,38 +249,41 @@ def test_rows_kernels_full_grid(ce, dtype, M, V):
 def test_rows_grid_rule(ce):
     # wavefronts per CU of the rows kernels: ~64 KiB in flight per CU (K KiB
     # each), ~128 KiB for 16-bit rows and for softmax / the fused backward,
-    # 4 to 16; two-buffer narrow rows 4 (the grids below are for 256 CUs and
-    # batches large enough to fill them)
+    # 4 to 16; two-buffer narrow rows 4.  The forward of rows of 257-1536
+    # vectors: one wavefront per row in chunks, 8 (fp32) or 12 (16-bit) per
+    # CU.  (Batches large enough to fill the grids.)
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    cases = [  # (M, V, dtype code, op, wavefronts per CU)
-        (32768, 4096, 0, ce.CE_OP_FWD, 4),         # fp32, K = 16
-        (32768, 4096, 0, ce.CE_OP_SOFTMAX, 8),     # folded epilogue
-        (32768, 4096, 0, ce.CE_OP_FWD_BWD, 8),
-        (32768, 4096, 0, ce.CE_OP_BWD, 4),         # epilogue without a fold
-        (65536, 2000, 0, ce.CE_OP_FWD, 8),         # fp32, K = 8
-        (131072, 2000, 2, ce.CE_OP_FWD, 16),       # bf16, K = 4
-        (32768, 8000, 2, ce.CE_OP_FWD, 8),         # bf16, K = 16
-        (1048576, 128, 0, ce.CE_OP_FWD, 4),        # two buffers
+    cases = [  # (M, V, dtype code, op, mapping, wavefronts per CU)
+        (131072, 1000, 0, ce.CE_OP_FWD, "rows:64:4", 16),     # fp32, K = 4
+        (131072, 512, 0, ce.CE_OP_FWD, "rows:32:4", 16),
+        (131072, 2000, 2, ce.CE_OP_FWD, "rows:64:4", 16),     # bf16, K = 4
+        (1048576, 128, 0, ce.CE_OP_FWD, "rows:4:8", 4),       # two buffers
+        (32768, 4096, 0, ce.CE_OP_SOFTMAX, "rows:64:16", 8),  # folded epilogue
+        (32768, 4096, 0, ce.CE_OP_FWD_BWD, "rows:64:16", 8),
+        (32768, 4096, 0, ce.CE_OP_BWD, "rows:64:16", 4),      # epilogue without a fold
+        (65536, 2000, 0, ce.CE_OP_SOFTMAX, "rows:64:8", 16),
+        (32768, 8000, 2, ce.CE_OP_SOFTMAX, "rows:64:16", 8),  # bf16, K = 16
+        (32768, 4096, 0, ce.CE_OP_FWD, "wstream:1:4", 8),
+        (65536, 2000, 0, ce.CE_OP_FWD, "wstream:1:8", 8),
+        (32768, 8000, 2, ce.CE_OP_FWD, "wstream:1:4", 12),
+        (65536, 1500, 2, ce.CE_OP_FWD, "rows:64:4", 16),      # 188 vectors
     ]
-    for M, V, code, op, waves in cases:
+    for M, V, code, op, mapping, waves in cases:
         plan = ce.ce_plan_describe(M, V, code, "mean", op=op)
         grid = int(plan.split("grid=")[1].split()[0])
         block = int(plan.split("block=")[1].split()[0])
-        assert plan.startswith("rows:"), plan
+        assert plan.startswith(mapping + " "), (M, V, code, op, plan)
         assert grid * block // 64 == waves * cus, (M, V, code, op, plan)
 
 
 def test_default_row_map(ce):
-    # one row per wavefront in the forward at 4 wavefronts per CU: bands;
-    # everything else interleaved
-    assert " blocked " in ce.ce_plan_describe(32768, 4096, 0, "mean")
-    assert " blocked " in ce.ce_plan_describe(100, 4096, 0, "none")
-    assert " blocked " not in ce.ce_plan_describe(65536, 2000, 0, "mean")
-    assert " blocked " not in ce.ce_plan_describe(100, 2000, 2, "none")
-    assert " blocked " not in ce.ce_plan_describe(1048576, 128, 0, "mean")
-    assert " blocked " not in ce.ce_plan_describe(32768, 4096, 0, "mean", op=ce.CE_OP_FWD_BWD)
-    assert " blocked " not in ce.ce_plan_describe(16384, 131072, 2, "mean")
+    # by default every grid strides over the rows (bands only on request)
+    for M, V, code, op in ((32768, 4096, 0, ce.CE_OP_FWD), (100, 1000, 0, ce.CE_OP_FWD),
+                           (65536, 2000, 0, ce.CE_OP_FWD), (100, 2000, 2, ce.CE_OP_FWD),
+                           (1048576, 128, 0, ce.CE_OP_FWD), (32768, 4096, 0, ce.CE_OP_FWD_BWD),
+                           (16384, 131072, 2, ce.CE_OP_FWD)):
+        assert " blocked " not in ce.ce_plan_describe(M, V, code, "mean", op=op)
 
 
 # ------------------------------------------------------------------ edge cases
