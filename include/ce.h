@@ -93,8 +93,7 @@ enum {
  * Bytes of device workspace a call with these arguments can use:
  *  - the mean or sum of ce_fwd / ce_fwd_lse / ce_fwd_bwd_inplace needs
  *    128 KiB (up to 16384 fp64 partial sums, one per workgroup of the
- *    launch, or per wavefront in the one-row-per-wavefront kernel; they are
- *    added in a fixed order, by the launch's last workgroup or a
+ *    launch, added in a fixed order by the launch's last workgroup or a
  *    one-wavefront kernel);
  *  - few long rows (M <= 128 and rows of at least 256 KiB) are split over
  *    several workgroups when the call gets a workspace of the size returned

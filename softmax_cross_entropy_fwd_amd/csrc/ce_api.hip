@@ -463,9 +463,8 @@ int make_plan(int64_t M, int64_t V, int dtype, int op, bool aligned, Plan *plan)
     int64_t cap = (int64_t)plan->cus * wg_per_cu;
     if (tuning().force_grid > 0)
         cap = tuning().force_grid;
-    // one published partial per wavefront (one-row-per-wavefront streamed
-    // kernel) or workgroup (the others)
-    const int64_t units_per_wg = kind == cek::KIND_WSTREAM ? plan->k.block / 64 : 1;
+    // one published partial per workgroup
+    const int64_t units_per_wg = 1;
     plan->units_per_wg = (int)units_per_wg;
     if (cap * units_per_wg > cek::kMaxPartials)
         cap = cek::kMaxPartials / units_per_wg;

@@ -1030,8 +1030,8 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
 }
 
 // --------------------------------------------- end of kernel: mean / sum
-// Every unit (a wavefront of the one-row-per-wavefront streamed kernel, a
-// workgroup of the others) stores its fp64 loss sum in its own slot, and the slots
+// Every workgroup stores its fp64 loss sum (its wavefronts' sums added in
+// wavefront order) in its own slot, and the slots
 // are added in index order by one wavefront: the last workgroup of the same
 // launch (finish_in_kernel, below), or, where the launch has no counter (a
 // graph capture, split rows), a second one-wavefront kernel on the same
@@ -1372,11 +1372,20 @@ __global__ void __launch_bounds__(256) wstream_kernel(Params p)
     }
     if (p.reduction == RED_NONE)
         return;
-    // lane 0 holds the wavefront's sum
+    // lane 0 holds the wavefront's sum; the workgroup's are added in
+    // wavefront order into one partial per workgroup (as the rows kernels do)
+    __shared__ double s_wave_sums[4];   // 256 threads
     if (lane == 0)
-        publish_partial(p, blockIdx.x * nwaves + wave, acc);
+        s_wave_sums[wave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double wg_total = s_wave_sums[0];
+        for (int w = 1; w < nwaves; ++w)
+            wg_total += s_wave_sums[w];
+        publish_partial(p, blockIdx.x, wg_total);
+    }
     if (p.ticket)
-        finish_in_kernel(p, (unsigned)(gridDim.x * nwaves), lane, wave);
+        finish_in_kernel(p, gridDim.x, lane, wave);
 }
 
 // ---- one row per workgroup, streamed in chunks ---------------------------------
