@@ -83,7 +83,8 @@ int pow2ceil(int64_t n)
 
 // Mapping and tile for a row of nvec 16-byte vectors (worst case over rows),
 // from measurements on MI355X:
-//  - the forward of rows of 257-1536 vectors (4-24 KB) streams each row
+//  - the forward of rows of 257-1536 vectors (4-24 KB; fp32 rows from 129
+//    vectors) streams each row
 //    through one wavefront in chunks of 64 K vectors (K = 8 up to 512
 //    vectors, then 4), 8 wavefronts per CU for fp32 rows and 12 for 16-bit
 //    ones.  Against the rows kernel's register tiles (region times, ~530 MB
@@ -119,6 +120,16 @@ void choose_shape(int64_t nvec, bool bwd, bool aligned, bool wide, int *kind, in
         *a = 1;
         *b = nvec > 512 ? 4 : 8;
         *waves = wide ? 12 : 8;
+    } else if (!bwd && !wide && nvec > 128 && nvec <= 256) {
+        // fp32 rows of 129-256 vectors: one chunk per row, more wavefronts
+        // the shorter it is (region times against the rows kernel, ~530 MB:
+        // 700 wide 94 / 107 us at 16, 800 wide 98 / 110 at 16, 900 wide 73 /
+        // 81 at 12, 1000 wide 82 / 86 at 12); 16-bit rows this short stay
+        // in register rows (1800 wide 99 / 92)
+        *kind = cek::KIND_WSTREAM;
+        *a = 1;
+        *b = 4;
+        *waves = nvec > 208 ? 12 : 16;
     } else if (nvec <= 4) {
         *a = 1;
         *b = nvec <= 1 ? 1 : nvec <= 2 ? 2 : 4;

@@ -214,7 +214,7 @@ def test_epilogue_plan_table(ce, dtype):
 @pytest.mark.parametrize("row_map", ["interleaved", "blocked"])
 def test_row_maps(ce, tuning, row_map):
     tuning.setenv("CE_ROW_MAP", row_map)
-    cases = [("f32", 1000, 1000, "fwd"), ("f32", 3, 1000, "fwd"), ("bf16", 777, 2000, "fwd"),
+    cases = [("f32", 1000, 500, "fwd"), ("f32", 3, 500, "fwd"), ("bf16", 777, 2000, "fwd"),
              ("f16", 5000, 128, "fwd"), ("f32", 2049, 1000, "fwd_bwd"),
              ("f32", 1000, 4096, "fwd_bwd"), ("bf16", 300, 32768, "fwd_bwd")]
     for dtype, M, V, op in cases:
@@ -251,11 +251,13 @@ def test_rows_grid_rule(ce):
     # each), ~128 KiB for 16-bit rows and for softmax / the fused backward,
     # 4 to 16; two-buffer narrow rows 4.  The forward of rows of 257-1536
     # vectors: one wavefront per row in chunks, 8 (fp32) or 12 (16-bit) per
-    # CU.  (Batches large enough to fill the grids.)
+    # CU; fp32 rows of 129-256 vectors: one chunk per row, 12 or 16 per CU.
+    # (Batches large enough to fill the grids.)
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     cases = [  # (M, V, dtype code, op, mapping, wavefronts per CU)
-        (131072, 1000, 0, ce.CE_OP_FWD, "rows:64:4", 16),     # fp32, K = 4
+        (131072, 1000, 0, ce.CE_OP_FWD, "wstream:1:4", 12),   # fp32, one chunk per row
+        (196608, 800, 0, ce.CE_OP_FWD, "wstream:1:4", 16),
         (131072, 512, 0, ce.CE_OP_FWD, "rows:32:4", 16),
         (131072, 2000, 2, ce.CE_OP_FWD, "rows:64:4", 16),     # bf16, K = 4
         (1048576, 128, 0, ce.CE_OP_FWD, "rows:4:8", 4),       # two buffers
