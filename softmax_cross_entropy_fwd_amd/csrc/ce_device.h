@@ -867,13 +867,25 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
     // epilogue starts as the row's vectors arrive, and taking the logit from
     // the registers first made it wait for the whole row, 17 % slower on the
     // classifier rows) and narrower rows read it from memory.
+    //
+    // Forwards of short rows read with non-temporal loads (XT_FOLD) instead
+    // pick the target's vector as it is folded: a line loaded
+    // non-temporally may be gone from the cache by the time the logit's own
+    // load arrives, which then fetches it from memory a second time.
+    // Measured per launch (~540 MB): fp32 rows of 512 bytes over 8 lanes
+    // 91.4 -> 87.0 us, bf16 rows of 512 bytes over 8 lanes 96.2 -> 92.4,
+    // fp32 rows of 32-128 vectors over 16-32 lanes 1.6-3 % faster; slower
+    // for 16-bit rows over 16 lanes x 2 vectors (6 %) and misaligned f16
+    // rows of 125 vectors over 32 lanes (5 %), which keep the load.
     constexpr bool XT_REGS = BWD && OP != EPI_LSE_GRAD && STRIDE >= 64;
+    constexpr bool XT_FOLD =
+        nt_fwd_loads<OP, STRIDE>() && (DT == DT_F32 ? STRIDE <= 32 : STRIDE == 8);
     const int kt_own = tp.valid ? tp.vt / STRIDE : -1;
     const bool xt_owner = tp.valid && lidx == tp.vt % STRIDE;
     const int owner_lane = tp.valid ? tp.vt % STRIDE : 0;
     float xt_own = 0.0f;
     float xt = __builtin_nanf("");
-    if constexpr (!XT_REGS)
+    if constexpr (!XT_REGS && !XT_FOLD)
         xt = tp.valid ? load_logit<DT>(p, cur.row, cur.t) : __builtin_nanf("");
     auto take_xt = [&]() {
         if constexpr (XT_REGS) {
@@ -948,6 +960,8 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
         // once with the next row's vector.
         float m_run = -__builtin_inff();
         float s_run = 0.0f;
+        const int kt_sel = xt_owner ? kt_own : -1;   // XT_FOLD: the owner's target vector
+        Vec tv = {};
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int v = lidx + STRIDE * k;
@@ -961,6 +975,11 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
             if constexpr (BWD) {
                 if (masked)
                     raw[k] = x;
+            }
+            if constexpr (XT_FOLD) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    tv.w[i] = k == kt_sel ? x.w[i] : tv.w[i];
             }
             const bool valid = vec_valid<STRIDE, EXACT>(k, kfull, lidx, w.nvec);
             const float mn = vec_max<DT>(x, m_run);
@@ -981,6 +1000,15 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
         else
             red.combine(m_run, s_run, m, s);
         shared_xt();
+        if constexpr (XT_FOLD) {
+            const float own = vec_elem_dyn<DT>(tv, tp.jt);
+            float sh;
+            if constexpr (STRIDE == 64)
+                sh = red.share_xt(own, owner_lane);
+            else
+                sh = group_bcast<STRIDE>(own, owner_lane);
+            xt = tp.valid ? sh : __builtin_nanf("");
+        }
     }
     const float mL = m * kLog2e;
 

@@ -249,7 +249,8 @@ def test_rows_kernels_full_grid(ce, dtype, M, V):
 def test_rows_grid_rule(ce):
     # wavefronts per CU of the rows kernels: ~64 KiB in flight per CU (K KiB
     # each), ~128 KiB for 16-bit rows and for softmax / the fused backward,
-    # 4 to 16; two-buffer narrow rows 4.  The forward of rows of 257-1536
+    # 4 to 16; two-buffer narrow rows (epilogues of rows of 17-32 vectors) 4.
+    # The forward of rows of 17-32 vectors: 8 lanes x 4 vectors.  Of 257-1536
     # vectors: one wavefront per row in chunks, 8 (fp32) or 12 (16-bit) per
     # CU; fp32 rows of 129-256 vectors: one chunk per row, 12 or 16 per CU.
     # (Batches large enough to fill the grids.)
@@ -260,7 +261,9 @@ def test_rows_grid_rule(ce):
         (196608, 800, 0, ce.CE_OP_FWD, "wstream:1:4", 16),
         (131072, 512, 0, ce.CE_OP_FWD, "rows:32:4", 16),
         (131072, 2000, 2, ce.CE_OP_FWD, "rows:64:4", 16),     # bf16, K = 4
-        (1048576, 128, 0, ce.CE_OP_FWD, "rows:4:8", 4),       # two buffers
+        (1048576, 128, 0, ce.CE_OP_FWD, "rows:8:4", 16),      # whole lines per load
+        (1048576, 256, 2, ce.CE_OP_FWD, "rows:8:4", 16),
+        (1048576, 128, 0, ce.CE_OP_FWD_BWD, "rows:4:8", 4),   # two buffers
         (32768, 4096, 0, ce.CE_OP_SOFTMAX, "rows:64:16", 8),  # folded epilogue
         (32768, 4096, 0, ce.CE_OP_FWD_BWD, "rows:64:16", 8),
         (32768, 4096, 0, ce.CE_OP_BWD, "rows:64:16", 4),      # epilogue without a fold
