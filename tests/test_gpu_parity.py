@@ -159,6 +159,31 @@ def test_every_kernel_shape(ce, shape, tuning):
         _check_shape(ce, shape, kind, cap)
 
 
+# the forward mappings that pick the target's logit from their registers as
+# the row is folded (fp32 rows over 8-32 lanes, 16-bit rows over 8 lanes)
+@pytest.mark.parametrize("dtype,V,shape", [("f32", 128, "rows:8:4"), ("f32", 100, "rows:8:4"),
+                                           ("f32", 37, "rows:8:4"), ("f32", 256, "rows:16:4"),
+                                           ("f32", 61, "rows:16:2"), ("f32", 500, "rows:32:4"),
+                                           ("bf16", 256, "rows:8:4"), ("f16", 203, "rows:8:4")])
+def test_forward_target_at_every_position(ce, tuning, dtype, V, shape):
+    """Row i's target is i mod V, so every element of the row -- every lane,
+    register and element slot of the tile -- is the target of some row;
+    per-row losses against the oracle, aligned and shifted bases, one and two
+    register sets, and a spread wide enough that many targets dominate."""
+    tuning.setenv("CE_FORCE_PLAN", shape)
+    M = 2 * V + 37
+    targets = [i % V for i in range(M)]
+    for nbuf in ("1", "2"):
+        tuning.setenv("CE_FORCE_NBUF", nbuf)
+        for offset, sigma in ((0, 3.0), (1, 3.0), (0, 12.0)):
+            plan = ce.ce_plan_describe(M, V, {"f32": 0, "f16": 1, "bf16": 2}[dtype], "none")
+            assert plan.startswith(shape), plan
+            run_and_check(ce, dtype, M, V, sigma, seed=V + M + offset, reduction="none",
+                          offset=offset, targets=targets)
+            run_and_check(ce, dtype, M, V, sigma, seed=V + 7, reduction="mean", offset=offset,
+                          targets=targets)
+
+
 def _check_shape(ce, shape, kind, cap):
     for dtype in DTYPES:
         if kind == "wg2" and dtype == "f32":
