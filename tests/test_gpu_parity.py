@@ -142,7 +142,9 @@ SHAPES = ["rows:1:1", "rows:1:2", "rows:1:4", "rows:2:4", "rows:4:4", "rows:8:4"
           "wg2:8:9", "wg2:8:11", "wg2:8:13", "stream:4:8", "stream:8:4", "stream:8:8", "stream:16:4",
           "stream:4:16", "stream:1:4", "stream:2:4", "stream:4:4", "stream:1:8", "stream:2:8",
           "stream:1:16", "stream:16:2", "stream:16:1", "stream:8:2",
-          "wstream:1:2", "wstream:1:4", "wstream:1:8"]
+          "wstream:1:2", "wstream:1:4", "wstream:1:8",
+          # forward only: 5 or 6 vectors per lane
+          "rows:8:5", "rows:8:6", "rows:16:5", "rows:16:6", "rows:32:5", "rows:32:6"]
 # row buffers of the rows kernel: 1 or 2 with 4-wave workgroups, 17 or 18 with
 # 16-wave workgroups (64:16 and 4:8 only)
 NBUFS = {"rows:64:16": ("1", "2", "17", "18"), "rows:4:8": ("1", "2", "17", "18")}
@@ -164,7 +166,10 @@ def test_every_kernel_shape(ce, shape, tuning):
 @pytest.mark.parametrize("dtype,V,shape", [("f32", 128, "rows:8:4"), ("f32", 100, "rows:8:4"),
                                            ("f32", 37, "rows:8:4"), ("f32", 256, "rows:16:4"),
                                            ("f32", 61, "rows:16:2"), ("f32", 500, "rows:32:4"),
-                                           ("bf16", 256, "rows:8:4"), ("f16", 203, "rows:8:4")])
+                                           ("bf16", 256, "rows:8:4"), ("f16", 203, "rows:8:4"),
+                                           ("f32", 160, "rows:8:5"), ("f32", 188, "rows:8:6"),
+                                           ("f16", 250, "rows:8:5"), ("bf16", 384, "rows:8:6"),
+                                           ("f32", 320, "rows:16:5"), ("f32", 380, "rows:16:6")])
 def test_forward_target_at_every_position(ce, tuning, dtype, V, shape):
     """Row i's target is i mod V, so every element of the row -- every lane,
     register and element slot of the tile -- is the target of some row;
@@ -297,7 +302,10 @@ def test_rows_grid_rule(ce):
         (32768, 4096, 0, ce.CE_OP_FWD, "wstream:1:4", 8),
         (65536, 2000, 0, ce.CE_OP_FWD, "wstream:1:8", 8),
         (32768, 8000, 2, ce.CE_OP_FWD, "wstream:1:4", 12),
-        (65536, 1500, 2, ce.CE_OP_FWD, "rows:64:4", 16),      # 188 vectors
+        (65536, 1500, 2, ce.CE_OP_FWD, "rows:32:6", 16),      # 188 vectors: 32 x 6
+        (1048576, 160, 0, ce.CE_OP_FWD, "rows:8:5", 12),      # 40 vectors: 8 x 5
+        (524288, 320, 0, ce.CE_OP_FWD, "rows:16:5", 12),      # 80 vectors: 16 x 5
+        (65536, 1500, 2, ce.CE_OP_FWD_BWD, "rows:64:4", 16),  # epilogues keep 4 per lane
     ]
     for M, V, code, op, mapping, waves in cases:
         plan = ce.ce_plan_describe(M, V, code, "mean", op=op)
