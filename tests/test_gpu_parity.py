@@ -279,8 +279,10 @@ def test_rows_kernels_full_grid(ce, dtype, M, V):
 def test_rows_grid_rule(ce):
     # wavefronts per CU of the rows kernels: ~64 KiB in flight per CU (K KiB
     # each), ~128 KiB for 16-bit rows and for softmax / the fused backward,
-    # 4 to 16; two-buffer narrow rows (epilogues of rows of 17-32 vectors) 4.
-    # The forward of rows of 17-32 vectors: 8 lanes x 4 vectors.  Of 257-1536
+    # to the nearest whole 4-wave workgroup, 4 to 16; two-buffer narrow rows
+    # (epilogues of rows of 17-32 vectors) 4.  The forward of rows of 17-32
+    # vectors: 8 lanes x 4 vectors; of 33-128 (16-bit: 33-256): 4-6 vectors
+    # per lane over a power-of-two number of lanes.  Of 257-1536
     # vectors: one wavefront per row in chunks, 8 (fp32) or 12 (16-bit) per
     # CU; fp32 rows of 129-256 vectors: one chunk per row, 12 or 16 per CU.
     # (Batches large enough to fill the grids.)
@@ -305,6 +307,8 @@ def test_rows_grid_rule(ce):
         (65536, 1500, 2, ce.CE_OP_FWD, "rows:32:6", 16),      # 188 vectors: 32 x 6
         (1048576, 160, 0, ce.CE_OP_FWD, "rows:8:5", 12),      # 40 vectors: 8 x 5
         (524288, 320, 0, ce.CE_OP_FWD, "rows:16:5", 12),      # 80 vectors: 16 x 5
+        (524288, 380, 0, ce.CE_OP_FWD, "rows:16:6", 12),      # 95 vectors: 16 x 6
+        (262144, 1500, 1, ce.CE_OP_FWD, "rows:32:6", 16),
         (65536, 1500, 2, ce.CE_OP_FWD_BWD, "rows:64:4", 16),  # epilogues keep 4 per lane
     ]
     for M, V, code, op, mapping, waves in cases:
