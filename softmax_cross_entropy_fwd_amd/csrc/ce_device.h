@@ -334,15 +334,22 @@ __device__ __forceinline__ void opt_barrier(Vec (&raw)[K])
 // lane's vector lies inside every row's window.  Elements of the window
 // outside the row become -inf; only the first and the last window vector (and
 // copies of the last) can hold such elements.
-template <int DT, int K, int STRIDE, bool NTL = false>
+// PART: vector slots that lie wholly past the window for this lane's
+// wavefront (its first lane index is wfirst, wave-uniform) are not loaded and
+// hold -inf.
+template <int DT, int K, int STRIDE, bool NTL = false, bool PART = false>
 __device__ __forceinline__ void load_window(Vec (&raw)[K], const Vec *xrow, int lidx, int nvec,
-                                            int kfull, int head, int64_t V, bool aligned)
+                                            int kfull, int head, int64_t V, bool aligned,
+                                            int wfirst = 0)
 {
     constexpr int E = Traits<DT>::E;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int v = lidx + STRIDE * k;
-        raw[k] = ldv<NTL>(&xrow[v < nvec ? v : nvec - 1]);
+        if (!PART || wfirst + STRIDE * k < nvec)
+            raw[k] = ldv<NTL>(&xrow[v < nvec ? v : nvec - 1]);
+        else
+            raw[k] = neg_inf_vec<DT>();
     }
     if (!aligned) {
         if (lidx == 0 && head > 0)
@@ -1545,17 +1552,22 @@ __global__ void __launch_bounds__(W * 64) stream_kernel(Params p)
             // max takes every element, the sum every element but the target
             float m_run = -__builtin_inff();
             float s_run = 0.0f;
-            for (int cb = 0; cb < w.nvec; cb += CH) {
+            // 16-bit forwards: in a row's last, partly empty chunk, the vector
+            // slots wholly past the row for a wavefront (a uniform test) are
+            // neither loaded nor folded -- the folds are VALU-bound; full
+            // chunks, fp32 rows and the epilogues take the loop below as it
+            // was
+            constexpr bool SKIP = DT != DT_F32 && OP == EPI_NONE;
+            const int wfirst = __builtin_amdgcn_readfirstlane(64 * wave);
+            auto chunk = [&](auto part, int cb) {
+                constexpr bool PART = decltype(part)::value;
                 Vec raw[K];
-                const int kfull = (w.nvec - cb) >= CH ? K : (w.nvec - cb) / NT;
-                // the chunk is a window of its own: the row's head lies in chunk 0,
-                // and its end is at element head + V - cb*E of the chunk
-                load_window<DT, K, NT, !BWD>(raw, w.xrow + cb, tid, w.nvec - cb, kfull,
-                                             cb == 0 ? w.head : 0,
-                                             cb == 0 ? p.V : p.V + w.head - (int64_t)cb * E,
-                                             p.aligned != 0);
-                // the lane holding the target keeps its logit aside and drops it
-                // from the vector: it enters the max below, not the sum
+                const int n = w.nvec - cb;
+                const int kfull = n >= CH ? K : n / NT;
+                load_window<DT, K, NT, !BWD, PART>(raw, w.xrow + cb, tid, n, kfull,
+                                                   cb == 0 ? w.head : 0,
+                                                   cb == 0 ? p.V : p.V + w.head - (int64_t)cb * E,
+                                                   p.aligned != 0, wfirst);
                 float tval = -__builtin_inff();
                 if (tp.valid && tp.vt >= cb && tp.vt < cb + CH) {
                     const int off = tp.vt - cb;
@@ -1569,19 +1581,71 @@ __global__ void __launch_bounds__(W * 64) stream_kernel(Params p)
                 }
                 float cm = fmaxf(m_run, tval);
 #pragma unroll
-                for (int k = 0; k < K; ++k)
+                for (int k = 0; k < K; ++k) {
+                    if (PART && wfirst + NT * k >= n)
+                        break;
                     cm = vec_max<DT>(raw[k], cm);
+                }
                 if (cm != -__builtin_inff()) {
                     const float cmL = cm * kLog2e;
                     float add = 0.0f;
 #pragma unroll
                     for (int k = 0; k < K; ++k) {
+                        if (PART && wfirst + NT * k >= n)
+                            break;
                         const float e = vec_sumexp<DT>(raw[k], cmL);
-                        add += vec_valid<NT>(k, kfull, tid, w.nvec - cb) ? e : 0.0f;
+                        add += vec_valid<NT>(k, kfull, tid, n) ? e : 0.0f;
                     }
-                    // the old sum is scaled by 2^(m_old - m_new); m_old = -inf gives 0
                     s_run = s_run * fast_exp2((m_run - cm) * kLog2e) + add;
                     m_run = cm;
+                }
+            };
+            if constexpr (SKIP) {
+                for (int cb = 0; cb < w.nvec; cb += CH) {
+                    if (w.nvec - cb < CH)
+                        chunk(BoolTag<true>{}, cb);
+                    else
+                        chunk(BoolTag<false>{}, cb);
+                }
+            } else {
+                for (int cb = 0; cb < w.nvec; cb += CH) {
+                    Vec raw[K];
+                    const int kfull = (w.nvec - cb) >= CH ? K : (w.nvec - cb) / NT;
+                    // the chunk is a window of its own: the row's head lies in chunk 0,
+                    // and its end is at element head + V - cb*E of the chunk
+                    load_window<DT, K, NT, !BWD>(raw, w.xrow + cb, tid, w.nvec - cb, kfull,
+                                                 cb == 0 ? w.head : 0,
+                                                 cb == 0 ? p.V : p.V + w.head - (int64_t)cb * E,
+                                                 p.aligned != 0);
+                    // the lane holding the target keeps its logit aside and drops it
+                    // from the vector: it enters the max below, not the sum
+                    float tval = -__builtin_inff();
+                    if (tp.valid && tp.vt >= cb && tp.vt < cb + CH) {
+                        const int off = tp.vt - cb;
+#pragma unroll
+                        for (int k = 0; k < K; ++k)
+                            if (off == tid + NT * k) {
+                                tval = vec_elem_dyn<DT>(raw[k], tp.jt);
+                                s_xt = tval;
+                                set_elem<DT>(raw[k], tp.jt, -__builtin_inff());
+                            }
+                    }
+                    float cm = fmaxf(m_run, tval);
+#pragma unroll
+                    for (int k = 0; k < K; ++k)
+                        cm = vec_max<DT>(raw[k], cm);
+                    if (cm != -__builtin_inff()) {
+                        const float cmL = cm * kLog2e;
+                        float add = 0.0f;
+#pragma unroll
+                        for (int k = 0; k < K; ++k) {
+                            const float e = vec_sumexp<DT>(raw[k], cmL);
+                            add += vec_valid<NT>(k, kfull, tid, w.nvec - cb) ? e : 0.0f;
+                        }
+                        // the old sum is scaled by 2^(m_old - m_new); m_old = -inf gives 0
+                        s_run = s_run * fast_exp2((m_run - cm) * kLog2e) + add;
+                        m_run = cm;
+                    }
                 }
             }
             float wm = group_reduce<64>(m_run, OpMax());
