@@ -887,6 +887,7 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
     constexpr bool XT_REGS = BWD && OP != EPI_LSE_GRAD && STRIDE >= 64;
     constexpr bool XT_FOLD =
         nt_fwd_loads<OP, STRIDE>() && (DT == DT_F32 ? STRIDE <= 32 : STRIDE == 8);
+    constexpr bool FOLD2 = !BWD && DT == DT_F32;
     const int kt_own = tp.valid ? tp.vt / STRIDE : -1;
     const bool xt_owner = tp.valid && lidx == tp.vt % STRIDE;
     const int owner_lane = tp.valid ? tp.vt % STRIDE : 0;
@@ -926,6 +927,55 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
         // with m = lse and s = 1
         m = cur.lse;
         s = 1.0f;
+    } else if constexpr (FOLD2) {
+        // Forwards of fp32 rows: the lane's max over its vectors first, then
+        // the sum against it, each register refilled with the next row's
+        // vector once it is summed -- no rescale of the running sum per
+        // vector (one exp2 in five, for 4-element vectors).
+        float ml = -__builtin_inff();
+        const int kt_sel = xt_owner ? kt_own : -1;   // XT_FOLD: the owner's target vector
+        Vec tv = {};
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int v = lidx + STRIDE * k;
+            if (masked) {
+                if (k == 0 && lidx == 0 && w.head > 0)
+                    mask_outside<DT>(raw[k], w.head, E);
+                if (k + 1 >= kfull && v >= w.nvec - 1)
+                    mask_outside<DT>(raw[k], 0, (int)(w.head + p.V - (int64_t)(w.nvec - 1) * E));
+            }
+            if constexpr (XT_FOLD) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    tv.w[i] = k == kt_sel ? raw[k].w[i] : tv.w[i];
+            }
+            const bool valid = vec_valid<STRIDE, EXACT>(k, kfull, lidx, w.nvec);
+            ml = valid ? vec_max<DT>(raw[k], ml) : ml;
+        }
+        const float mlL = ml == -__builtin_inff() ? 0.0f : ml * kLog2e;
+        float sl = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int v = lidx + STRIDE * k;
+            const float e = vec_sumexp<DT>(raw[k], mlL);
+            sl += vec_valid<STRIDE, EXACT>(k, kfull, lidx, w.nvec) ? e : 0.0f;
+            raw[k] = ldv<nt_fwd_loads<OP, STRIDE>()>(&next.w.xrow[next_vec<EXACT>(next, v)]);
+            // keep each load after the use of the register it refills
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (STRIDE > 64)
+            red.combine(ml, sl, m, s, xt_own, xt_owner);
+        else
+            red.combine(ml, sl, m, s);
+        if constexpr (XT_FOLD) {
+            const float own = vec_elem_dyn<DT>(tv, tp.jt);
+            float sh;
+            if constexpr (STRIDE == 64)
+                sh = red.share_xt(own, owner_lane);
+            else
+                sh = group_bcast<STRIDE>(own, owner_lane);
+            xt = tp.valid ? sh : __builtin_nanf("");
+        }
     } else if constexpr (BWD && DT == DT_F16) {
         // The epilogues issue the next row's loads only as they store, so the
         // fold may take two passes over the registers: the lane's max (two
