@@ -482,6 +482,12 @@ int make_plan(int64_t M, int64_t V, int dtype, int op, bool aligned, Plan *plan)
         // per lane: 12 wavefronts, 126 us for 512K x 380 against 137 at 8)
         rows_waves = 4 * ((target_kib + 2 * b) / (4 * b));
         rows_waves = rows_waves < 4 ? 4 : rows_waves > 16 ? 16 : rows_waves;
+        // fp32 forwards over 8+ lanes per row (non-temporal loads): 12
+        // (per launch at 12 / 16: 1M x 128 84.6 / 85.8 us, 512K x 256 84.6 /
+        // 85.9, 256K x 512 83.7 / 86.0; narrower rows and 16-bit ones keep
+        // 16: fp32 4M x 20 114 / 97, f16 256K x 1000 99 / 93)
+        if (dtype == CE_F32 && op == cek::EPI_NONE && a >= 8 && rows_waves > 12)
+            rows_waves = 12;
     }
     const int target_waves = tw > 0                   ? tw
                              : kind == cek::KIND_ROWS ? rows_waves

@@ -279,7 +279,8 @@ def test_rows_kernels_full_grid(ce, dtype, M, V):
 def test_rows_grid_rule(ce):
     # wavefronts per CU of the rows kernels: ~64 KiB in flight per CU (K KiB
     # each), ~128 KiB for 16-bit rows and for softmax / the fused backward,
-    # to the nearest whole 4-wave workgroup, 4 to 16; two-buffer narrow rows
+    # to the nearest whole 4-wave workgroup, 4 to 16 (fp32 forwards over 8+
+    # lanes per row: at most 12); two-buffer narrow rows
     # (epilogues of rows of 17-32 vectors) 4.  The forward of rows of 17-32
     # vectors: 8 lanes x 4 vectors; of 33-128 (16-bit: 33-256): 4-6 vectors
     # per lane over a power-of-two number of lanes.  Of 257-1536
@@ -291,9 +292,9 @@ def test_rows_grid_rule(ce):
     cases = [  # (M, V, dtype code, op, mapping, wavefronts per CU)
         (131072, 1000, 0, ce.CE_OP_FWD, "wstream:1:4", 12),   # fp32, one chunk per row
         (196608, 800, 0, ce.CE_OP_FWD, "wstream:1:4", 16),
-        (131072, 512, 0, ce.CE_OP_FWD, "rows:32:4", 16),
+        (131072, 512, 0, ce.CE_OP_FWD, "rows:32:4", 12),
         (131072, 2000, 2, ce.CE_OP_FWD, "rows:64:4", 16),     # bf16, K = 4
-        (1048576, 128, 0, ce.CE_OP_FWD, "rows:8:4", 16),      # whole lines per load
+        (1048576, 128, 0, ce.CE_OP_FWD, "rows:8:4", 12),      # whole lines per load
         (1048576, 256, 2, ce.CE_OP_FWD, "rows:8:4", 16),
         (1048576, 128, 0, ce.CE_OP_FWD_BWD, "rows:4:8", 4),   # two buffers
         (32768, 4096, 0, ce.CE_OP_SOFTMAX, "rows:64:16", 8),  # folded epilogue
