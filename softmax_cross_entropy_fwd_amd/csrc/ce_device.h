@@ -888,6 +888,12 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
     constexpr bool XT_FOLD =
         nt_fwd_loads<OP, STRIDE>() && (DT == DT_F32 ? STRIDE <= 32 : STRIDE == 8);
     constexpr bool FOLD2 = !BWD;
+    // The epilogues of exact workgroup tiles refill with non-temporal loads
+    // (per launch: LM head fused backward 1.640 -> 1.613 ms, its softmax
+    // 1.616 -> 1.597, fp32 16384 x 32768 fused backward 811 -> 791 us);
+    // register rows of one wavefront measured 6 % slower with them (32768 x
+    // 4096 fp32 fused backward), misaligned tiles too (the stress rows).
+    constexpr bool NT_EPI = BWD && EXACT && STRIDE > 64;
     const int kt_own = tp.valid ? tp.vt / STRIDE : -1;
     const bool xt_owner = tp.valid && lidx == tp.vt % STRIDE;
     const int owner_lane = tp.valid ? tp.vt % STRIDE : 0;
@@ -1108,7 +1114,7 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
             }
             if (cur.active && vec_valid<STRIDE, EXACT>(k, kfull, lidx, w.nvec))
                 store_grad<DT>(w.yrow, v, g, w.head, p.V, EXACT || p.aligned);
-            raw[k] = ldv(&next.w.xrow[next_vec<EXACT>(next, v)]);
+            raw[k] = ldv<NT_EPI>(&next.w.xrow[next_vec<EXACT>(next, v)]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
