@@ -890,10 +890,15 @@ __device__ __forceinline__ float pipeline_step(const Params &p, Red &red, Vec (&
     constexpr bool FOLD2 = !BWD;
     // The epilogues of exact workgroup tiles refill with non-temporal loads
     // (per launch: LM head fused backward 1.640 -> 1.613 ms, its softmax
-    // 1.616 -> 1.597, fp32 16384 x 32768 fused backward 811 -> 791 us);
-    // register rows of one wavefront measured 6 % slower with them (32768 x
-    // 4096 fp32 fused backward), misaligned tiles too (the stress rows).
-    constexpr bool NT_EPI = BWD && EXACT && STRIDE > 64;
+    // 1.616 -> 1.597, fp32 16384 x 32768 fused backward 811 -> 791 us), and
+    // so does the softmax of exact register rows, whose output goes to
+    // another buffer (32768 x 4096 fp32: 200 -> 190 us).  The fused backward
+    // of register rows of one wavefront measured 6 % slower with them (32768
+    // x 4096 fp32), misaligned rows 2-7 % (the stress rows' fused backward
+    // and softmax, fp32 2001 and f16 999 wide softmax), the backward from a
+    // given lse no faster.
+    constexpr bool NT_EPI =
+        BWD && EXACT && (STRIDE > 64 || OP == EPI_SOFTMAX || OP == EPI_LOGSOFTMAX);
     const int kt_own = tp.valid ? tp.vt / STRIDE : -1;
     const bool xt_owner = tp.valid && lidx == tp.vt % STRIDE;
     const int owner_lane = tp.valid ? tp.vt % STRIDE : 0;
