@@ -774,7 +774,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
