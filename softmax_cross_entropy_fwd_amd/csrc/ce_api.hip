@@ -151,26 +151,23 @@ void choose_shape(int64_t nvec, bool bwd, bool aligned, bool wide, int *kind, in
         *a = 4;
         *b = 8;
         *nbuf = 2;
-    } else if (!bwd && nvec <= (wide ? 256 : 128)) {
-        // forward rows of 33-128 vectors (16-bit: 33-256): the power-of-two
-        // lanes per row that leave 4-6 vectors per lane, so the tile fits the
-        // row (the fold runs over every slot of a tile).  Measured per launch
-        // (1M rows unless noted): fp32 160 wide 138 us in 16 x 4 against 109
-        // in 8 x 5; misaligned f16 250 wide 224 / 137 (8 x 5); fp32 320 wide
-        // (512K rows) 143 in 32 x 4 against 105 in 16 x 5; bf16 384 wide 180
-        // in 16 x 4 against 136 in 8 x 6
-        const int g = nvec <= 48 ? 8 : nvec <= 96 ? 16 : nvec <= 192 ? 32 : 64;
-        *a = g;
-        *b = (int)((nvec + g - 1) / g);
-    } else if (nvec <= 64) {
-        *a = 16;
-        *b = 4;
-    } else if (nvec <= 128) {
-        *a = 32;
-        *b = 4;
     } else if (nvec <= 256) {
-        *a = 64;
-        *b = 4;
+        // rows of 33-256 vectors (the fp32 forwards of 129-256 stream, above):
+        // the power-of-two lanes per row that leave 4-6 vectors per lane, so
+        // the tile fits the row (the fold and the epilogue run over every
+        // slot of a tile).  Measured per launch (1M rows unless noted), 4
+        // vectors per lane against the fitted tile: forwards fp32 160 wide
+        // 138 / 109 us (8 x 5), misaligned f16 250 wide 224 / 137, fp32 320
+        // wide (512K rows) 143 / 105 (16 x 5), bf16 384 wide 180 / 136 (8 x
+        // 6); fused backward f16 250 wide 367 / 322, bf16 384 wide 331 / 305,
+        // bf16 1200 wide (256K rows) 322 / 246 (32 x 5), fp32 320 wide 257 /
+        // 248; bf16 384 wide softmax 314 / 291.  fp32 epilogues of 129-256
+        // vectors keep 64 x 4 (600 wide: softmax 254 / 260, fused backward
+        // 241 / 240 in 32 x 5).
+        const int g = nvec <= 48 ? 8 : nvec <= 96 ? 16 : nvec <= 128 ? 32
+                      : (wide && nvec <= 192) ? 32 : 64;
+        *a = g;
+        *b = g == 64 ? 4 : (int)((nvec + g - 1) / g);
     } else if (nvec <= 512) {
         *a = 64;
         *b = 8;

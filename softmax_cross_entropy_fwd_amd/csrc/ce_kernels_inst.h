@@ -38,11 +38,9 @@ KernelRef pick_all(int kind, int a, int b, int nbuf)
         CE_ROWS(16, 4) CE_ROWS(32, 4) CE_ROWS(64, 4) CE_ROWS(64, 8) CE_ROWS(64, 16)
         CE_ROWS(4, 8) CE_ROWS(8, 2) CE_ROWS(16, 2) CE_ROWS(32, 1) CE_ROWS(32, 8) CE_ROWS(32, 16)
         CE_ROWS(32, 32) CE_ROWS(2, 16)
-        // 5 or 6 vectors per lane: forward rows just over a tile size
-        if constexpr (OP == EPI_NONE) {
-            CE_ROWS1(8, 5) CE_ROWS1(8, 6) CE_ROWS1(16, 5) CE_ROWS1(16, 6) CE_ROWS1(32, 5)
-            CE_ROWS1(32, 6)
-        }
+        // 5 or 6 vectors per lane: rows just over a tile size
+        CE_ROWS1(8, 5) CE_ROWS1(8, 6) CE_ROWS1(16, 5) CE_ROWS1(16, 6) CE_ROWS1(32, 5)
+        CE_ROWS1(32, 6)
     } else if (kind == KIND_WG) {
         CE_WG(4, 8) CE_WG(8, 8) CE_WG(8, 12) CE_WG(8, 16) CE_WG(16, 8) CE_WG(16, 12) CE_WG(16, 16)
         CE_WG(4, 16) CE_WG(16, 4) CE_WG(16, 2) CE_WG(16, 3) CE_WG(16, 5) CE_WG(16, 6) CE_WG(16, 7)
@@ -71,6 +69,8 @@ KernelRef pick_table(int kind, int a, int b, int nbuf)
                              : KernelRef{(const void *)&rows_kernel<DT, 4, 8, OP, EXACT, 1>, 256};
         CE_ROWS1(1, 1) CE_ROWS1(1, 2) CE_ROWS1(1, 4) CE_ROWS1(2, 4) CE_ROWS1(4, 4)
         CE_ROWS1(16, 4) CE_ROWS1(32, 4) CE_ROWS1(64, 4) CE_ROWS1(64, 8) CE_ROWS1(64, 16)
+        CE_ROWS1(8, 5) CE_ROWS1(8, 6) CE_ROWS1(16, 5) CE_ROWS1(16, 6) CE_ROWS1(32, 5)
+        CE_ROWS1(32, 6)
     } else if (kind == KIND_WG) {
         CE_WG(16, 2) CE_WG(16, 3) CE_WG(16, 4) CE_WG(16, 5) CE_WG(16, 6) CE_WG(16, 7)
         CE_WG(16, 8) CE_WG(16, 12) CE_WG(16, 16)

@@ -287,7 +287,9 @@ def test_every_softmax_and_grad_shape(ce, tuning):
                        ("wg:16:7", 7168), ("wg:16:8", 8192), ("wg2:8:9", 4608),
                        ("wg2:8:13", 6656),
                        ("wg:16:12", 12288), ("wg:16:16", 16384), ("stream:8:4", 1 << 30),
-                       ("stream:16:4", 1 << 30)):
+                       ("stream:16:4", 1 << 30), ("rows:8:5", 40), ("rows:8:6", 48),
+                       ("rows:16:5", 80), ("rows:16:6", 96), ("rows:32:5", 160),
+                       ("rows:32:6", 192)):
         tuning.setenv("CE_FORCE_PLAN", shape)
         for dtype in DTYPES:
             if shape.startswith("wg2") and dtype == "f32":
@@ -340,7 +342,10 @@ def test_fused_and_split_backward_agree(ce):
 # (16-bit rows of 4097-6656 vectors: 8-wave tiles, two per CU), register
 # tiles beyond; the backward from a given lse streams 16-bit rows of 4096
 # vectors or more.
-EPI_DEFAULTS = [(1500, "stream:8:4", "stream:8:4"), (4096, "wg:16:4", "wg:16:4"),
+EPI_DEFAULTS = [(40, "rows:8:5", "rows:8:5"), (48, "rows:8:6", "rows:8:6"),
+                (80, "rows:16:5", "rows:16:5"), (150, "rows:64:4", "rows:32:5"),
+                (190, "rows:64:4", "rows:32:6"),
+                (1500, "stream:8:4", "stream:8:4"), (4096, "wg:16:4", "wg:16:4"),
                 (6000, "stream:16:4", "wg2:8:12"), (7168, "wg:16:7", "wg:16:7"),
                 (7800, "stream:16:4", "stream:16:4"), (10240, "wg:16:12", "wg:16:12")]
 

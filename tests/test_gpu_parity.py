@@ -283,7 +283,7 @@ def test_rows_grid_rule(ce):
     # lanes per row: at most 12); two-buffer narrow rows
     # (epilogues of rows of 17-32 vectors) 4.  The forward of rows of 17-32
     # vectors: 8 lanes x 4 vectors; of 33-128 (16-bit: 33-256): 4-6 vectors
-    # per lane over a power-of-two number of lanes.  Of 257-1536
+    # per lane over a power-of-two number of lanes (every operation).  Of 257-1536
     # vectors: one wavefront per row in chunks, 8 (fp32) or 12 (16-bit) per
     # CU; fp32 rows of 129-256 vectors: one chunk per row, 12 or 16 per CU.
     # (Batches large enough to fill the grids.)
@@ -310,7 +310,9 @@ def test_rows_grid_rule(ce):
         (524288, 320, 0, ce.CE_OP_FWD, "rows:16:5", 12),      # 80 vectors: 16 x 5
         (524288, 380, 0, ce.CE_OP_FWD, "rows:16:6", 12),      # 95 vectors: 16 x 6
         (262144, 1500, 1, ce.CE_OP_FWD, "rows:32:6", 16),
-        (65536, 1500, 2, ce.CE_OP_FWD_BWD, "rows:64:4", 16),  # epilogues keep 4 per lane
+        (65536, 1500, 2, ce.CE_OP_FWD_BWD, "rows:32:6", 16),  # the epilogues' tiles fit too
+        (1048576, 384, 2, ce.CE_OP_SOFTMAX, "rows:8:6", 16),
+        (524288, 320, 0, ce.CE_OP_BWD, "rows:16:5", 12),
     ]
     for M, V, code, op, mapping, waves in cases:
         plan = ce.ce_plan_describe(M, V, code, "mean", op=op)
